@@ -35,8 +35,12 @@ specification, not by code):
   2*(k&3)+1 .. 2*(k&3)); d3 / d4 pack eight 1-bit fields (bit k & 7).
 * DELTA2: d = salient_val if k is salient else step[n] * (c - 2), c in [0, 3],
   packed like q2.
-* SwiGLU expert: h = silu(x Wg^T) * (x Wu^T), y = h Wd^T, with gate rows
-  0..I-1 and up rows I..2I-1 of the gate_up matrix.
+* SwiGLU expert: h = silu(x Wg^T) * (x Wu^T), y = bf16(h) Wd^T, with gate
+  rows 0..I-1 and up rows I..2I-1 of the gate_up matrix.  The rounding of h
+  to bf16 is the "A16" of W4A16 (ExactMoE) and the 16-bit GEMM of the D2MoE
+  pipeline equation: the activation entering each expert GEMM is a 16-bit
+  value.  Everything else stays float64 (gate/up products, SiLU, the expert
+  output y and the combine).
 * MWQ segment order inside an expert: b = 4, 3, 2 (sub-key 4 - b).
 """
 from __future__ import annotations
@@ -185,20 +189,30 @@ def permute(ids, E: int, pair_bits=None):
 
 
 # ----------------------------------------------------------------------- experts
+def round_bf16(a) -> np.ndarray:
+    """Nearest bf16 value (8 significant bits, ties to even) of float64 values,
+    rounded once from the float64 value; returned as float64."""
+    a = np.asarray(a, dtype=F64)
+    m, e = np.frexp(a)                    # a = m * 2**e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
 def silu(g):
     return g / (1.0 + np.exp(-g))
 
 
 def swiglu_expert(xrows, w_gate_up, w_down):
-    """SwiGLU FFN of one expert on rows of activations (float64).
+    """SwiGLU FFN of one expert on rows of 16-bit activations.
 
     w_gate_up [2I][H]: rows 0..I-1 gate, I..2I-1 up; w_down [H][I].
+    The intermediate activation h is a bf16 value (W4A16: 16-bit activations
+    into every expert GEMM); products and sums are float64.
     Returns (h [m][I], y [m][H]).
     """
     I = w_gate_up.shape[0] // 2
     g = xrows @ w_gate_up[:I].T
     u = xrows @ w_gate_up[I:].T
-    h = silu(g) * u
+    h = round_bf16(silu(g) * u)
     return h, h @ w_down.T
 
 

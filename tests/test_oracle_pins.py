@@ -55,12 +55,21 @@ def py_silu(g):
     return g / (1.0 + math.exp(-g))
 
 
+def py_bf16(v):
+    """Nearest number with 8 significant bits (ties to even), pure Python."""
+    if v == 0.0:
+        return 0.0
+    m, e = math.frexp(v)
+    return math.ldexp(round(m * 256.0), e - 8)   # round(): half to even
+
+
 def py_ffn(x, wgu, wd, I):
-    """Textbook SwiGLU on Python lists: wgu[n][k] (2I x H), wd[m][n] (H x I)."""
+    """Textbook SwiGLU on Python lists: wgu[n][k] (2I x H), wd[m][n] (H x I);
+    the activation h entering the down projection is a 16-bit (bf16) value."""
     H = len(x)
     g = [sum(x[kk] * wgu[n][kk] for kk in range(H)) for n in range(I)]
     u = [sum(x[kk] * wgu[I + n][kk] for kk in range(H)) for n in range(I)]
-    h = [py_silu(g[n]) * u[n] for n in range(I)]
+    h = [py_bf16(py_silu(g[n]) * u[n]) for n in range(I)]
     return [sum(h[n] * wd[m][n] for n in range(I)) for m in range(H)]
 
 
@@ -415,3 +424,19 @@ def test_compare_metric():
     m = oracle.compare(r + np.array([0.03, 0.0]), r)
     assert abs(m["rel_l2"] - 0.03 / 5.0) < 1e-15
     assert abs(m["max_abs_over_rms"] - 0.03 / math.sqrt(12.5)) < 1e-15
+
+
+def test_round_bf16_pins():
+    """bf16 keeps 8 significant bits; ties go to the even neighbour."""
+    one = 1.0
+    assert oracle.round_bf16(one + 2.0 ** -8) == one                   # tie -> even (1.0)
+    assert oracle.round_bf16(one + 3 * 2.0 ** -8) == one + 2.0 ** -6   # tie -> even (1 + 2^-6)
+    assert oracle.round_bf16(one + 2.0 ** -8 + 2.0 ** -30) == one + 2.0 ** -7
+    assert oracle.round_bf16(-3.0) == -3.0 and oracle.round_bf16(0.0) == 0.0
+    assert oracle.round_bf16(255.0) == 255.0 and oracle.round_bf16(257.0) == 256.0
+    # float32 inputs: agrees with the bit-level float32 -> bf16 conversion of the generator
+    v = np.random.default_rng(4).standard_normal(20000).astype(np.float32) * 7
+    bits = gen.f32_to_bf16_bits(v)
+    assert np.array_equal(oracle.round_bf16(v.astype(np.float64)), gen.bf16_bits_to_f32(bits).astype(np.float64))
+    for x in v[:200]:
+        assert oracle.round_bf16(float(x)) == py_bf16(float(x))
