@@ -1,0 +1,307 @@
+"""Python binding of libmoe_qexpert.so (the routed-expert quantized MoE library).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.  The functions carry
+the C ABI's names; outputs are allocated here unless passed in.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_qexpert.so")
+
+MOE_ABI_VERSION = 1
+MOE_W_INT4_GROUP, MOE_W_MWQ_2_3_4, MOE_W_DELTA2_SALIENT = 1, 2, 3
+MOE_LAYOUT_CANONICAL, MOE_LAYOUT_TILED = 0, 1
+MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_NONE_F32 = 0, 1, 2
+MOE_DTYPE_BF16, MOE_DTYPE_F32 = 0, 1
+(MOE_FIELD_CODES, MOE_FIELD_PLANE3, MOE_FIELD_PLANE4, MOE_FIELD_SCALES,
+ MOE_FIELD_SALIENT_IDX, MOE_FIELD_SALIENT_VAL, MOE_FIELD_BASE) = range(7)
+
+EXPORTED = [
+    "moe_status_string", "moe_last_error_detail", "moe_abi_version", "moe_route_topk",
+    "moe_permute_workspace_size", "moe_permute", "moe_weight_field_bytes", "moe_repack_weights",
+    "moe_grouped_qgemm_workspace_size", "moe_grouped_qgemm", "moe_unpermute_combine",
+]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status}: {detail}")
+        self.status = status
+
+
+class WDesc(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", ctypes.c_int32), ("format", ctypes.c_int32), ("layout", ctypes.c_int32),
+        ("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+        ("group_size", ctypes.c_int32), ("zero_point", ctypes.c_int32), ("n_salient", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("codes", ctypes.c_void_p), ("plane3", ctypes.c_void_p), ("plane4", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p), ("salient_idx", ctypes.c_void_p), ("salient_val", ctypes.c_void_p),
+        ("base", ctypes.c_void_p),
+    ]
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run quantized_moe_expert_top_amd/build.py "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "moe_status_string": (ctypes.c_char_p, [i32]),
+        "moe_last_error_detail": (ctypes.c_char_p, []),
+        "moe_abi_version": (i32, []),
+        "moe_route_topk": (i32, [vp, i32, i32, i32, vp, vp, vp]),
+        "moe_permute_workspace_size": (sz, [i32, i32, i32, i32]),
+        "moe_permute": (i32, [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]),
+        "moe_weight_field_bytes": (sz, [ctypes.POINTER(WDesc), i32]),
+        "moe_repack_weights": (i32, [ctypes.POINTER(WDesc), ctypes.POINTER(WDesc), vp]),
+        "moe_grouped_qgemm_workspace_size": (sz, [ctypes.POINTER(WDesc), i32, i32]),
+        "moe_grouped_qgemm": (i32, [ctypes.POINTER(WDesc), vp, i32, vp, i32, vp, i32, i32, vp, vp, sz, vp]),
+        "moe_unpermute_combine": (i32, [vp, i32, vp, vp, i32, i32, i32, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        _lib = load_library()
+        if _lib.moe_abi_version() != MOE_ABI_VERSION:
+            raise ImportError("libmoe_qexpert.so ABI version mismatch")
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise MoeError(status, where, lib().moe_last_error_detail().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _bf16(t: torch.Tensor) -> torch.Tensor:
+    if t.element_size() != 2:
+        raise ValueError("expected 16-bit (bf16 bit pattern) tensor")
+    return t
+
+
+# ------------------------------------------------------------------ entry points
+def moe_route_topk(logits: torch.Tensor, k: int, ids: torch.Tensor = None, w: torch.Tensor = None, stream=None):
+    assert logits.dtype == torch.float32 and logits.dim() == 2
+    T, E = logits.shape
+    ids = torch.empty((T, k), dtype=torch.int32, device=logits.device) if ids is None else ids
+    w = torch.empty((T, k), dtype=torch.float32, device=logits.device) if w is None else w
+    _check(lib().moe_route_topk(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream(stream)), "moe_route_topk")
+    return ids, w
+
+
+@dataclass
+class Permutation:
+    counts: torch.Tensor
+    seg_offsets: torch.Tensor
+    sorted_pair: torch.Tensor
+    pair_pos: torch.Tensor
+    workspace: torch.Tensor
+    x_perm: Optional[torch.Tensor] = None
+
+
+def moe_permute(ids: torch.Tensor, E: int, pair_bits: torch.Tensor = None, x: torch.Tensor = None,
+                want_x_perm: bool = False, out: Permutation = None, stream=None) -> Permutation:
+    T, k = ids.shape
+    S = 3 if pair_bits is not None else 1
+    dev = ids.device
+    if out is None:
+        ws_bytes = lib().moe_permute_workspace_size(T, k, E, S)
+        out = Permutation(
+            counts=torch.empty(E, dtype=torch.int32, device=dev),
+            seg_offsets=torch.empty(E * S + 1, dtype=torch.int32, device=dev),
+            sorted_pair=torch.empty(T * k, dtype=torch.int32, device=dev),
+            pair_pos=torch.empty(T * k, dtype=torch.int32, device=dev),
+            workspace=torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev),
+            x_perm=(torch.empty((T * k, x.shape[1]), dtype=x.dtype, device=dev) if want_x_perm else None),
+        )
+    H = x.shape[1] if x is not None else 0
+    _check(lib().moe_permute(_ptr(ids), _ptr(pair_bits), T, k, E, _ptr(out.counts), _ptr(out.seg_offsets),
+                             _ptr(out.sorted_pair), _ptr(out.pair_pos), _ptr(x), H, _ptr(out.x_perm),
+                             _ptr(out.workspace), out.workspace.numel(), _stream(stream)), "moe_permute")
+    return out
+
+
+@dataclass
+class QuantizedExperts:
+    """A weight set in one layout; keeps its tensors alive with the descriptor."""
+    desc: WDesc
+    tensors: dict = field(default_factory=dict)
+
+    @property
+    def N(self):
+        return self.desc.N
+
+    @property
+    def K(self):
+        return self.desc.K
+
+
+def make_desc(fmt: int, layout: int, E: int, N: int, K: int, group_size: int, zero_point: int,
+              n_salient: int = 0, **tensors) -> QuantizedExperts:
+    d = WDesc()
+    d.abi_version, d.format, d.layout = MOE_ABI_VERSION, fmt, layout
+    d.E, d.N, d.K, d.group_size, d.zero_point, d.n_salient = E, N, K, group_size, zero_point, n_salient
+    for name in ("codes", "plane3", "plane4", "scales", "salient_idx", "salient_val", "base"):
+        t = tensors.get(name)
+        setattr(d, name, _ptr(t) if t is not None else None)
+    return QuantizedExperts(d, {k: v for k, v in tensors.items() if v is not None})
+
+
+def moe_weight_field_bytes(q: QuantizedExperts, fld: int) -> int:
+    return lib().moe_weight_field_bytes(ctypes.byref(q.desc), fld)
+
+
+def moe_repack_weights(src: QuantizedExperts, stream=None) -> QuantizedExperts:
+    """Canonical -> tiled copy of a weight set (offline; allocates the tiled buffers)."""
+    s = src.desc
+    dev = next(iter(src.tensors.values())).device
+    probe = make_desc(s.format, MOE_LAYOUT_TILED, s.E, s.N, s.K, s.group_size, s.zero_point, s.n_salient)
+    t = {}
+    for name, fld in (("codes", MOE_FIELD_CODES), ("plane3", MOE_FIELD_PLANE3), ("plane4", MOE_FIELD_PLANE4),
+                      ("salient_val", MOE_FIELD_SALIENT_VAL)):
+        nb = moe_weight_field_bytes(probe, fld)
+        if nb and name in src.tensors:
+            t[name] = torch.empty(nb, dtype=torch.uint8, device=dev)
+    if "base" in src.tensors:
+        t["base"] = torch.empty_like(src.tensors["base"])
+    for name in ("scales", "salient_idx"):
+        if name in src.tensors:
+            t[name] = src.tensors[name]
+    dst = make_desc(s.format, MOE_LAYOUT_TILED, s.E, s.N, s.K, s.group_size, s.zero_point, s.n_salient, **t)
+    _check(lib().moe_repack_weights(ctypes.byref(s), ctypes.byref(dst.desc), _stream(stream)), "moe_repack_weights")
+    return dst
+
+
+def moe_grouped_qgemm(w: QuantizedExperts, A: torch.Tensor, seg_offsets: torch.Tensor, M_total: int,
+                      epilogue: int = MOE_EPI_NONE, gather_pair: torch.Tensor = None, k: int = 1,
+                      out: torch.Tensor = None, workspace: torch.Tensor = None, stream=None) -> torch.Tensor:
+    _bf16(A)
+    A_rows = A.shape[0]
+    n_out = w.N // 2 if epilogue == MOE_EPI_SWIGLU else w.N
+    if out is None:
+        dt = torch.float32 if epilogue == MOE_EPI_NONE_F32 else torch.bfloat16
+        out = torch.empty((M_total, n_out), dtype=dt, device=A.device)
+    ws_need = lib().moe_grouped_qgemm_workspace_size(ctypes.byref(w.desc), A_rows, M_total)
+    if workspace is None and ws_need:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=A.device)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(lib().moe_grouped_qgemm(ctypes.byref(w.desc), _ptr(A), A_rows, _ptr(gather_pair), k, _ptr(seg_offsets),
+                                   M_total, epilogue, _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
+           "moe_grouped_qgemm")
+    return out
+
+
+def moe_unpermute_combine(y_perm: torch.Tensor, pair_pos: torch.Tensor, topk_w: Optional[torch.Tensor],
+                          T: int, k: int, out: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """y_perm: fp32 or 16-bit (bf16 bit pattern) rows in grouped order."""
+    y_dtype = MOE_DTYPE_F32 if y_perm.dtype == torch.float32 else MOE_DTYPE_BF16
+    if y_dtype == MOE_DTYPE_BF16:
+        _bf16(y_perm)
+    H = y_perm.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y_perm.device)
+    _check(lib().moe_unpermute_combine(_ptr(y_perm), y_dtype, _ptr(pair_pos), _ptr(topk_w), T, k, H, _ptr(out),
+                                       _stream(stream)), "moe_unpermute_combine")
+    return out
+
+
+# --------------------------------------------------------------- conveniences
+def int4_experts(codes: torch.Tensor, scales: torch.Tensor, group_size: int, zero_point: int = 8) -> QuantizedExperts:
+    """Canonical INT4 weights: codes u8 [E][N][K/2], scales fp16 [E][N][K/G]."""
+    E, N, Kh = codes.shape
+    return make_desc(MOE_W_INT4_GROUP, MOE_LAYOUT_CANONICAL, E, N, 2 * Kh, group_size, zero_point,
+                     codes=codes, scales=scales)
+
+
+def mwq_experts(q2, d3, d4, scales, group_size: int, zero_point: int = 8) -> QuantizedExperts:
+    E, N, Kq = q2.shape
+    return make_desc(MOE_W_MWQ_2_3_4, MOE_LAYOUT_CANONICAL, E, N, 4 * Kq, group_size, zero_point,
+                     codes=q2, plane3=d3, plane4=d4, scales=scales)
+
+
+def delta2_experts(codes, step, salient_idx, salient_val, base=None, zero_point: int = 2) -> QuantizedExperts:
+    E, N, Kq = codes.shape
+    return make_desc(MOE_W_DELTA2_SALIENT, MOE_LAYOUT_CANONICAL, E, N, 4 * Kq, 4 * Kq, zero_point,
+                     n_salient=salient_idx.shape[1], codes=codes, scales=step, salient_idx=salient_idx,
+                     salient_val=salient_val, base=base)
+
+
+@dataclass
+class LayerBuffers:
+    """Preallocated intermediates of one MoE layer forward."""
+    ids: torch.Tensor
+    w: torch.Tensor
+    perm: Permutation
+    h: torch.Tensor
+    y_perm: torch.Tensor
+    out: torch.Tensor
+
+
+def alloc_layer(T: int, E: int, k: int, H: int, I: int, mwq: bool, device) -> LayerBuffers:
+    S = 3 if mwq else 1
+    ws = lib().moe_permute_workspace_size(T, k, E, S)
+    perm = Permutation(
+        counts=torch.empty(E, dtype=torch.int32, device=device),
+        seg_offsets=torch.empty(E * S + 1, dtype=torch.int32, device=device),
+        sorted_pair=torch.empty(T * k, dtype=torch.int32, device=device),
+        pair_pos=torch.empty(T * k, dtype=torch.int32, device=device),
+        workspace=torch.empty(max(ws, 16), dtype=torch.uint8, device=device))
+    return LayerBuffers(
+        ids=torch.empty((T, k), dtype=torch.int32, device=device),
+        w=torch.empty((T, k), dtype=torch.float32, device=device),
+        perm=perm,
+        h=torch.empty((T * k, I), dtype=torch.bfloat16, device=device),
+        y_perm=torch.empty((T * k, H), dtype=torch.float32, device=device),
+        out=torch.empty((T, H), dtype=torch.bfloat16, device=device))
+
+
+def moe_layer_forward(x: torch.Tensor, logits: torch.Tensor, k: int, gate_up: QuantizedExperts,
+                      down: QuantizedExperts, pair_bits: torch.Tensor = None,
+                      buf: LayerBuffers = None, stream=None) -> LayerBuffers:
+    """Route -> group -> gate_up (+SwiGLU, bf16 h) -> down (fp32 expert outputs) -> combine, one stream."""
+    T, H = x.shape
+    E = logits.shape[1]
+    I = gate_up.N // 2
+    if buf is None:
+        buf = alloc_layer(T, E, k, H, I, pair_bits is not None, x.device)
+    moe_route_topk(logits, k, ids=buf.ids, w=buf.w, stream=stream)
+    moe_permute(buf.ids, E, pair_bits=pair_bits, out=buf.perm, stream=stream)
+    moe_grouped_qgemm(gate_up, x, buf.perm.seg_offsets, T * k, MOE_EPI_SWIGLU, gather_pair=buf.perm.sorted_pair,
+                      k=k, out=buf.h, stream=stream)
+    moe_grouped_qgemm(down, buf.h, buf.perm.seg_offsets, T * k, MOE_EPI_NONE_F32, out=buf.y_perm, stream=stream)
+    moe_unpermute_combine(buf.y_perm, buf.perm.pair_pos, buf.w, T, k, out=buf.out, stream=stream)
+    return buf

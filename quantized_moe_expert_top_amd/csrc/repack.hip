@@ -1,0 +1,206 @@
+// Offline conversion of canonical weight storage to the tiled layout that the
+// grouped GEMM streams.  Codes are moved, never changed (except the salient
+// input channels of a 2-bit delta, whose codes become the zero code because
+// their value travels separately in bf16).
+//
+// Tiled layout, one "tile block" per (expert e, 32 output channels ct, 128
+// input channels kb), tile blocks ordered (e, ct, kb) so that a wavefront
+// streams one channel tile along K contiguously.  Inside a tile block, lane l
+// of a wavefront owns channel ct*32 + (l % 32) and, for every 16-wide K step
+// s = 0..7, the 8 inputs k = kb*128 + 16*s + 8*(l/32) + i, i = 0..7 (the MFMA
+// 32x32x16 operand layout).  The bits of one lane and step are placed so that
+// pairs (i = 2p, 2p+1) land in the low / high halfword of a dword after one
+// shift and mask:
+//   4-bit  (2 KB / tile block): byte (s/4)*1024 + 16*l + 4*(s%4) is a dword with
+//          element i at bit 16*(i&1) + 4*(i>>1).
+//   2-bit  (1 KB): dword at 16*l + 4*(s/2); with P = 4*(s%2) + (i>>1), element i
+//          at bit 16*(i&1) + 2*P.
+//   1-bit  (512 B): dword at 8*l + 4*(s/4); with P = 4*(s%4) + (i>>1), element i
+//          at bit 16*(i&1) + P.
+//   bf16 base (8 KB): 16 bytes at 1024*s + 16*l hold the 8 inputs in order.
+//   salient values: per (e, ct) ceil(S/16) blocks of 1 KB; lane l holds slots
+//          16*step + 8*(l/32) + i of channel ct*32 + l%32 (zero past S).
+#include "common.h"
+
+namespace moe {
+
+namespace {
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void repack_u4_kernel(const uint8_t* __restrict__ src, int N, int K,
+                                                             uint32_t* __restrict__ dst, size_t ndw) {
+  const size_t d = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (d >= ndw) return;
+  const int KB = K / 128, NT = N / 32;
+  const size_t blk = d / 512;
+  const int within = (int)(d % 512);
+  const int h = within / 256, l = (within % 256) / 4, w = within % 4;
+  const int kb = (int)(blk % KB);
+  const size_t ect = blk / KB;
+  const int ct = (int)(ect % NT);
+  const size_t e = ect / NT;
+  const int ch = ct * 32 + (l & 31);
+  const int s = 4 * h + w;
+  const int k0 = kb * 128 + 16 * s + 8 * (l >> 5);
+  const uint32_t v = *reinterpret_cast<const uint32_t*>(src + (e * N + ch) * (size_t)(K / 2) + k0 / 2);
+  uint32_t o = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o |= ((v >> (4 * i)) & 0xFu) << (16 * (i & 1) + 4 * (i >> 1));
+  dst[d] = o;
+}
+
+// 2-bit plane; zero_code >= 0 replaces the codes of salient channels (DELTA2).
+__global__ __launch_bounds__(kThreads) void repack_u2_kernel(const uint8_t* __restrict__ src, int N, int K,
+                                                             uint32_t* __restrict__ dst, const int32_t* sal_idx,
+                                                             int n_sal, int zero_code) {
+  // one workgroup = one 1 KB tile block (256 dwords)
+  __shared__ uint32_t salmask[4];
+  const int KB = K / 128, NT = N / 32;
+  const size_t blk = blockIdx.x;
+  const int kb = (int)(blk % KB);
+  const size_t ect = blk / KB;
+  const int ct = (int)(ect % NT);
+  const size_t e = ect / NT;
+  if (threadIdx.x < 4) salmask[threadIdx.x] = 0;
+  __syncthreads();
+  if (sal_idx && (int)threadIdx.x < n_sal) {
+    const int kk = sal_idx[e * n_sal + threadIdx.x] - kb * 128;
+    if (kk >= 0 && kk < 128) atomicOr(&salmask[kk >> 5], 1u << (kk & 31));
+  }
+  __syncthreads();
+  const int within = threadIdx.x;
+  const int l = within / 4, w = within % 4;
+  const int ch = ct * 32 + (l & 31);
+  uint32_t o = 0;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int s = 2 * w + t;
+    const int koff = 16 * s + 8 * (l >> 5);
+    const int k0 = kb * 128 + koff;
+    const uint32_t v = *reinterpret_cast<const uint16_t*>(src + (e * N + ch) * (size_t)(K / 4) + k0 / 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t f = (v >> (2 * i)) & 3u;
+      const int kk = koff + i;
+      if (zero_code >= 0 && ((salmask[kk >> 5] >> (kk & 31)) & 1u)) f = (uint32_t)zero_code;
+      const int P = 4 * t + (i >> 1);
+      o |= f << (16 * (i & 1) + 2 * P);
+    }
+  }
+  dst[blk * 256 + within] = o;
+}
+
+__global__ __launch_bounds__(kThreads) void repack_u1_kernel(const uint8_t* __restrict__ src, int N, int K,
+                                                             uint32_t* __restrict__ dst, size_t ndw) {
+  const size_t d = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (d >= ndw) return;
+  const int KB = K / 128, NT = N / 32;
+  const size_t blk = d / 128;
+  const int within = (int)(d % 128);
+  const int l = within / 2, w = within % 2;
+  const int kb = (int)(blk % KB);
+  const size_t ect = blk / KB;
+  const int ct = (int)(ect % NT);
+  const size_t e = ect / NT;
+  const int ch = ct * 32 + (l & 31);
+  uint32_t o = 0;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int s = 4 * w + t;
+    const int k0 = kb * 128 + 16 * s + 8 * (l >> 5);
+    const uint32_t v = src[(e * N + ch) * (size_t)(K / 8) + k0 / 8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int P = 4 * t + (i >> 1);
+      o |= ((v >> i) & 1u) << (16 * (i & 1) + P);
+    }
+  }
+  dst[d] = o;
+}
+
+__global__ __launch_bounds__(kThreads) void repack_base_kernel(const uint16_t* __restrict__ src, int N, int K,
+                                                               u32x4* __restrict__ dst, size_t nvec) {
+  const size_t d = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (d >= nvec) return;
+  const int KB = K / 128;
+  const size_t blk = d / 512;
+  const int within = (int)(d % 512);
+  const int s = within / 64, l = within % 64;
+  const int kb = (int)(blk % KB);
+  const int ct = (int)(blk / KB);
+  const int ch = ct * 32 + (l & 31);
+  const int k0 = kb * 128 + 16 * s + 8 * (l >> 5);
+  dst[d] = *reinterpret_cast<const u32x4*>(src + (size_t)ch * K + k0);
+}
+
+__global__ __launch_bounds__(kThreads) void repack_salient_kernel(const uint16_t* __restrict__ src, int E, int N,
+                                                                  int n_sal, int nsteps,
+                                                                  uint32_t* __restrict__ dst, size_t ndw) {
+  const size_t d = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (d >= ndw) return;
+  const int NT = N / 32;
+  const size_t blk = d / 256;  // (e, ct, step)
+  const int within = (int)(d % 256);
+  const int l = within / 4, w = within % 4;
+  const int step = (int)(blk % nsteps);
+  const size_t ect = blk / nsteps;
+  const int ct = (int)(ect % NT);
+  const size_t e = ect / NT;
+  const int ch = ct * 32 + (l & 31);
+  uint32_t o = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = 16 * step + 8 * (l >> 5) + 2 * w + h;
+    const uint32_t v = j < n_sal ? src[(e * n_sal + j) * (size_t)N + ch] : 0u;
+    o |= v << (16 * h);
+  }
+  dst[d] = o;
+}
+
+inline unsigned grid_for(size_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
+}  // namespace
+
+size_t tiled_salient_bytes(int E, int N, int n_sal) {
+  const size_t nsteps = (size_t)(n_sal + 15) / 16;
+  return (size_t)E * (N / 32) * nsteps * 1024;
+}
+
+hipError_t launch_repack(const QWeights& src, const QWeights& dst, hipStream_t s) {
+  const size_t ENK = (size_t)src.E * src.N * src.K;
+  if (ENK == 0) return hipSuccess;
+  uint32_t* codes = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(dst.codes));
+  if (src.fmt == 1) {
+    const size_t ndw = ENK / 8;
+    hipLaunchKernelGGL(repack_u4_kernel, dim3(grid_for(ndw)), dim3(kThreads), 0, s, src.codes, src.N, src.K, codes,
+                       ndw);
+  } else {
+    const size_t nblk = ENK / (32 * 128);
+    const bool delta = src.fmt == 3;
+    hipLaunchKernelGGL(repack_u2_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, s, src.codes, src.N, src.K, codes,
+                       delta ? src.sal_idx : nullptr, delta ? src.n_sal : 0, delta ? src.z : -1);
+    if (src.fmt == 2) {
+      const size_t ndw = ENK / 32;
+      hipLaunchKernelGGL(repack_u1_kernel, dim3(grid_for(ndw)), dim3(kThreads), 0, s, src.p3, src.N, src.K,
+                         reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(dst.p3)), ndw);
+      hipLaunchKernelGGL(repack_u1_kernel, dim3(grid_for(ndw)), dim3(kThreads), 0, s, src.p4, src.N, src.K,
+                         reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(dst.p4)), ndw);
+    }
+    if (delta) {
+      if (src.n_sal > 0) {
+        const int nsteps = (src.n_sal + 15) / 16;
+        const size_t ndw = tiled_salient_bytes(src.E, src.N, src.n_sal) / 4;
+        hipLaunchKernelGGL(repack_salient_kernel, dim3(grid_for(ndw)), dim3(kThreads), 0, s, src.sal_val, src.E,
+                           src.N, src.n_sal, nsteps, reinterpret_cast<uint32_t*>(const_cast<uint16_t*>(dst.sal_val)),
+                           ndw);
+      }
+      if (src.base) {
+        const size_t nvec = (size_t)src.N * src.K / 8;
+        hipLaunchKernelGGL(repack_base_kernel, dim3(grid_for(nvec)), dim3(kThreads), 0, s, src.base, src.N, src.K,
+                           reinterpret_cast<u32x4*>(const_cast<uint16_t*>(dst.base)), nvec);
+      }
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,83 @@
+"""Shared helpers of the GPU tests: move generated workloads to the device and
+run the library's C ABI calls on them (through the Python binding)."""
+import numpy as np
+import torch
+
+import gen
+import quantized_moe_expert_top_amd as q
+
+DEV = "cuda:0"
+
+# parity bar for bf16 outputs
+REL_L2 = 5e-3
+MAX_ABS_OVER_RMS = 2e-2
+GATE_RTOL = 1e-6
+
+
+def t(a, dtype=None):
+    """numpy -> device tensor; uint16 bit patterns travel as int16."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    x = torch.from_numpy(a).to(DEV)
+    return x if dtype is None else x.view(dtype)
+
+
+def bf16_to_np(x: torch.Tensor) -> np.ndarray:
+    """bf16 (or already fp32) device tensor -> float64 numpy."""
+    if x.dtype == torch.float32:
+        return x.cpu().numpy().astype(np.float64)
+    return x.view(torch.bfloat16).float().cpu().numpy().astype(np.float64)
+
+
+def experts_int4(d, prefix, G):
+    return q.int4_experts(t(d[prefix + "codes"]), t(d[prefix + "scales"]), G)
+
+
+def experts_mwq(d, prefix, G):
+    return q.mwq_experts(t(d[prefix + "q2"]), t(d[prefix + "d3"]), t(d[prefix + "d4"]), t(d[prefix + "scales"]), G)
+
+
+def tiled_layer(d, cfg):
+    """Repacked (tiled) gate_up and down weight sets of a generated MoE layer."""
+    mk = experts_int4 if cfg.fmt == "int4" else experts_mwq
+    gu = q.moe_repack_weights(mk(d, "gu_", cfg.G))
+    dn = q.moe_repack_weights(mk(d, "dn_", cfg.G))
+    return gu, dn
+
+
+def run_layer(d, cfg, gu=None, dn=None):
+    """Full layer on the GPU; returns the LayerBuffers (synchronised)."""
+    if gu is None:
+        gu, dn = tiled_layer(d, cfg)
+    x = t(d["x"])
+    logits = t(d["logits"])
+    bits = t(d["pair_bits"]) if cfg.fmt == "mwq" else None
+    buf = q.moe_layer_forward(x, logits, cfg.k, gu, dn, pair_bits=bits)
+    torch.cuda.synchronize()
+    return buf
+
+
+def delta_layer(d, cfg):
+    """Tiled DELTA2 weight set (with the shared base) of a generated delta layer."""
+    src = q.delta2_experts(t(d["codes"]), t(d["step"]), t(d["salient_idx"]), t(d["salient_val"]), base=t(d["base"]))
+    return q.moe_repack_weights(src)
+
+
+def run_delta(d, cfg, w=None):
+    if w is None:
+        w = delta_layer(d, cfg)
+    x = t(d["x"])
+    ids = t(d["ids"]).view(cfg.T, 1)
+    perm = q.moe_permute(ids, cfg.E)
+    y_perm = q.moe_grouped_qgemm(w, x, perm.seg_offsets, cfg.T, q.MOE_EPI_NONE, gather_pair=perm.sorted_pair, k=1)
+    out = q.moe_unpermute_combine(y_perm, perm.pair_pos, None, cfg.T, 1)
+    torch.cuda.synchronize()
+    return perm, y_perm, out
+
+
+def check_close(gpu, ref, what=""):
+    from oracle import compare
+    m = compare(gpu, ref)
+    assert m["rel_l2"] <= REL_L2 and m["max_abs_over_rms"] <= MAX_ABS_OVER_RMS, f"{what}: {m}"
+    return m

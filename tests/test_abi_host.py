@@ -1,0 +1,163 @@
+"""Host-side checks of the C ABI library (no GPU needed): the built library
+loads, exports every function the header declares, and rejects bad arguments
+with the documented status codes before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_moe_expert_top_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_qexpert.h")
+
+OK, NULL_ARG, BAD_SHAPE, BAD_FORMAT, MISALIGNED, WS_SMALL, UNSUPPORTED, HIP = range(8)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(q.LIB_PATH):
+        pytest.fail("library not built: run __graft_entry__.build()")
+    return q.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(moe_[a-z_]+)\(", text, re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for n in ("moe_route_topk", "moe_permute", "moe_grouped_qgemm", "moe_unpermute_combine",
+              "moe_repack_weights", "moe_permute_workspace_size"):
+        assert n in names
+    assert set(names) == set(q.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(q.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+    assert lib.moe_abi_version() == q.MOE_ABI_VERSION
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert lib.moe_status_string(s)
+    assert lib.moe_status_string(99) == b"unknown status"
+
+
+def fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_route_validation(lib):
+    A = fake(0x1000)
+    assert lib.moe_route_topk(A, 4, 0, 1, A, A, None) == BAD_SHAPE
+    assert lib.moe_route_topk(A, 4, 8, 9, A, A, None) == BAD_SHAPE
+    assert lib.moe_route_topk(A, 4, 2000, 2, A, A, None) == BAD_SHAPE
+    assert lib.moe_route_topk(A, -1, 8, 2, A, A, None) == BAD_SHAPE
+    assert lib.moe_route_topk(None, 4, 8, 2, A, A, None) == NULL_ARG
+    assert b"required" in lib.moe_last_error_detail()
+    assert lib.moe_route_topk(fake(0x1002), 4, 8, 2, A, A, None) == MISALIGNED
+    assert lib.moe_route_topk(None, 0, 8, 2, None, None, None) == OK  # nothing to do
+    assert lib.moe_last_error_detail() == b""
+    assert lib.moe_route_topk(A, 1 << 28, 1024, 16, A, A, None) == BAD_SHAPE  # T*k >= 2^31
+
+
+def test_permute_validation(lib):
+    A = fake(0x1000)
+    need = lib.moe_permute_workspace_size(8192, 8, 64, 1)
+    assert need > 256
+    assert lib.moe_permute_workspace_size(32, 8, 64, 1) == 256 + 0 + 0 or lib.moe_permute_workspace_size(32, 8, 64, 1) >= 256
+    assert lib.moe_permute_workspace_size(4, 1, 8, 2) == 0  # S must be 1 or 3
+    args = lambda ws_bytes, ws=A: (A, None, 8192, 8, 64, A, A, A, A, None, 0, None, ws, ws_bytes, None)  # noqa: E731
+    assert lib.moe_permute(*args(need - 1)) == WS_SMALL
+    assert lib.moe_permute(*args(need, None)) == NULL_ARG
+    assert lib.moe_permute(*args(need, fake(0x1004))) == MISALIGNED
+    assert lib.moe_permute(A, None, 16, 9, 8, A, A, A, A, None, 0, None, A, 1 << 20, None) == BAD_SHAPE
+    # x_perm requested without x / with bad H
+    assert lib.moe_permute(A, None, 16, 2, 8, A, A, A, A, None, 64, A, A, 1 << 20, None) == NULL_ARG
+    assert lib.moe_permute(A, None, 16, 2, 8, A, A, A, A, A, 12, A, A, 1 << 20, None) == BAD_SHAPE
+
+
+def desc(fmt=q.MOE_W_INT4_GROUP, layout=q.MOE_LAYOUT_TILED, E=8, N=256, K=512, G=128, z=8, ns=0, **ptrs):
+    d = q.WDesc()
+    d.abi_version, d.format, d.layout = q.MOE_ABI_VERSION, fmt, layout
+    d.E, d.N, d.K, d.group_size, d.zero_point, d.n_salient = E, N, K, G, z, ns
+    d.codes = ptrs.get("codes", 0x10000)
+    d.scales = ptrs.get("scales", 0x20000)
+    d.plane3 = ptrs.get("plane3", 0x30000)
+    d.plane4 = ptrs.get("plane4", 0x40000)
+    d.salient_idx = ptrs.get("salient_idx", 0x50000)
+    d.salient_val = ptrs.get("salient_val", 0x60000)
+    d.base = ptrs.get("base", None)
+    return d
+
+
+def gemm(lib, d, A=0x1000, rows=64, gather=0x2000, k=2, seg=0x3000, M=128, epi=q.MOE_EPI_SWIGLU, out=0x4000):
+    return lib.moe_grouped_qgemm(ctypes.byref(d), fake(A) if A else None, rows, fake(gather) if gather else None, k,
+                                 fake(seg) if seg else None, M, epi, fake(out) if out else None, None, 0, None)
+
+
+def test_grouped_qgemm_validation(lib):
+    assert gemm(lib, desc(layout=q.MOE_LAYOUT_CANONICAL)) == BAD_FORMAT
+    d = desc()
+    d.abi_version = 7
+    assert gemm(lib, d) == BAD_FORMAT
+    assert gemm(lib, desc(fmt=9)) == BAD_FORMAT
+    assert gemm(lib, desc(G=48)) == UNSUPPORTED
+    assert gemm(lib, desc(N=48)) == UNSUPPORTED
+    assert gemm(lib, desc(K=200)) == UNSUPPORTED
+    assert gemm(lib, desc(z=16)) == BAD_SHAPE
+    assert gemm(lib, desc(codes=0)) == NULL_ARG
+    assert gemm(lib, desc(codes=0x10008)) == MISALIGNED
+    assert gemm(lib, desc(fmt=q.MOE_W_MWQ_2_3_4, plane3=0)) == NULL_ARG
+    assert gemm(lib, desc(fmt=q.MOE_W_DELTA2_SALIENT, z=2, ns=65)) == UNSUPPORTED
+    assert gemm(lib, desc(), epi=5) == BAD_FORMAT
+    assert gemm(lib, desc(N=32), epi=q.MOE_EPI_SWIGLU) == UNSUPPORTED
+    assert gemm(lib, desc(), rows=10, k=2, M=128) == BAD_SHAPE        # A_rows * k < M_total
+    assert gemm(lib, desc(), gather=0, rows=10, M=128) == BAD_SHAPE   # A_rows < M_total
+    assert gemm(lib, desc(), A=0) == NULL_ARG
+    assert gemm(lib, desc(), out=0x4004) == MISALIGNED
+    assert gemm(lib, desc(), M=0, A=0, seg=0, out=0) == OK           # empty problem
+
+
+def test_weight_field_bytes_and_nested_storage(lib):
+    H, I, E, G = 4096, 14336, 8, 128
+    mwq = desc(fmt=q.MOE_W_MWQ_2_3_4, layout=q.MOE_LAYOUT_CANONICAL, E=E, N=2 * I, K=H, G=G)
+    int4 = desc(fmt=q.MOE_W_INT4_GROUP, layout=q.MOE_LAYOUT_CANONICAL, E=E, N=2 * I, K=H, G=G)
+    fb = lambda d, f: lib.moe_weight_field_bytes(ctypes.byref(d), f)  # noqa: E731
+    planes = fb(mwq, q.MOE_FIELD_CODES) + fb(mwq, q.MOE_FIELD_PLANE3) + fb(mwq, q.MOE_FIELD_PLANE4)
+    assert planes == fb(int4, q.MOE_FIELD_CODES) == E * 2 * I * H // 2
+    assert fb(int4, q.MOE_FIELD_PLANE3) == 0
+    assert fb(int4, q.MOE_FIELD_SCALES) == E * 2 * I * (H // G) * 2
+    tiled = desc(fmt=q.MOE_W_DELTA2_SALIENT, E=16, N=14336, K=4096, z=2, ns=41)
+    assert fb(tiled, q.MOE_FIELD_SALIENT_VAL) == 16 * (14336 // 32) * 3 * 1024
+    assert fb(tiled, q.MOE_FIELD_BASE) == 14336 * 4096 * 2
+    assert fb(desc(G=48), q.MOE_FIELD_CODES) == 0   # invalid descriptor
+
+
+def test_repack_validation(lib):
+    src = desc(layout=q.MOE_LAYOUT_CANONICAL)
+    dst = desc(layout=q.MOE_LAYOUT_TILED, codes=0x70000)
+    assert lib.moe_repack_weights(ctypes.byref(dst), ctypes.byref(dst), None) == BAD_FORMAT
+    bad = desc(layout=q.MOE_LAYOUT_TILED, codes=0x70000, N=512)
+    assert lib.moe_repack_weights(ctypes.byref(src), ctypes.byref(bad), None) == BAD_SHAPE
+    same = desc(layout=q.MOE_LAYOUT_TILED)
+    assert lib.moe_repack_weights(ctypes.byref(src), ctypes.byref(same), None) == BAD_SHAPE
+
+
+def test_combine_validation(lib):
+    A = fake(0x1000)
+    assert lib.moe_unpermute_combine(A, 0, A, A, 4, 2, 12, A, None) == BAD_SHAPE
+    assert lib.moe_unpermute_combine(A, 3, A, A, 4, 2, 16, A, None) == BAD_FORMAT
+    assert lib.moe_unpermute_combine(None, 1, A, A, 4, 2, 16, A, None) == NULL_ARG
+    assert lib.moe_unpermute_combine(fake(0x1008), 0, A, A, 4, 2, 16, A, None) == MISALIGNED
+    assert lib.moe_unpermute_combine(None, 0, None, None, 0, 2, 16, None, None) == OK
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    with pytest.raises(ImportError):
+        q.load_library(str(tmp_path / "missing.so"))

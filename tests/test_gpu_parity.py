@@ -1,0 +1,209 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Bars: expert ids, counts, offsets and permutation indices bit-exact; gate
+weights within 1e-6 relative; bf16 outputs within relative L2 5e-3 and
+max-abs 2e-2 x RMS of the oracle output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def G():
+    from tests import gpu_helpers  # imports torch and the binding
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return gpu_helpers
+
+
+# ------------------------------------------------------------------ routing
+@pytest.mark.parametrize("name,k", [("tiny", 2), ("olmoe_decode", 8), ("olmoe_prefill", 8),
+                                    ("olmoe_prefill_zipf", 8), ("mixtral_mwq", 2)])
+def test_route_topk_parity(G, name, k):
+    cfg = gen.config(name)
+    logits = gen._logits(cfg)
+    ids, w = G.q.moe_route_topk(G.t(logits), k)
+    ref_ids, ref_w = oracle.route_topk(logits, k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    np.testing.assert_allclose(w.cpu().numpy().astype(np.float64), ref_w, rtol=G.GATE_RTOL, atol=0)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 1), (37, 8, 8), (100, 1024, 16), (5, 130, 7), (64, 64, 64)])
+def test_route_topk_edges_and_ties(G, T, E, k):
+    rng = np.random.default_rng(T * 1000 + E)
+    logits = rng.integers(-2, 3, size=(T, E)).astype(np.float32)  # heavy ties
+    logits[0, :] = 0.0
+    ids, w = G.q.moe_route_topk(G.t(logits), k)
+    ref_ids, ref_w = oracle.route_topk(logits, k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    np.testing.assert_allclose(w.cpu().numpy().astype(np.float64), ref_w, rtol=G.GATE_RTOL, atol=0)
+
+
+# ----------------------------------------------------------------- grouping
+def _perm_check(G, ids_np, E, bits_np=None):
+    ids = G.t(ids_np.astype(np.int32))
+    bits = G.t(bits_np.astype(np.uint8)) if bits_np is not None else None
+    p = G.q.moe_permute(ids, E, pair_bits=bits)
+    torch.cuda.synchronize()
+    c, s, sp, pp = oracle.permute(ids_np, E, bits_np)
+    assert np.array_equal(p.counts.cpu().numpy(), c)
+    assert np.array_equal(p.seg_offsets.cpu().numpy(), s)
+    assert np.array_equal(p.sorted_pair.cpu().numpy(), sp)
+    assert np.array_equal(p.pair_pos.cpu().numpy(), pp)
+    assert int(p.workspace[:4].view(torch.int32).item()) == 0
+
+
+@pytest.mark.parametrize("T,E,k", [(64, 8, 2), (32, 64, 8), (8192, 64, 8), (1, 4, 1), (300, 5, 5), (5000, 1024, 3)])
+def test_permute_parity(G, T, E, k):
+    rng = np.random.default_rng(T + E + k)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]) if T else np.zeros((0, k))
+    _perm_check(G, ids, E)
+
+
+def test_permute_skew_and_bits(G):
+    rng = np.random.default_rng(9)
+    ids = np.zeros((3000, 1), np.int64)                       # every pair on expert 0
+    _perm_check(G, ids, 16)
+    ids = np.stack([rng.permutation(8)[:2] for _ in range(9000)])
+    bits = rng.integers(2, 5, size=18000)
+    _perm_check(G, ids, 8, bits)                              # MWQ sub-keys, multi-block path
+    _perm_check(G, ids[:512], 8, bits[:1024])                 # MWQ sub-keys, single workgroup
+
+
+def test_permute_flags_invalid_ids(G):
+    ids = np.array([[0, 1], [2, 7], [1, 3]], np.int32)
+    p = G.q.moe_permute(G.t(ids), 4)
+    torch.cuda.synchronize()
+    assert int(p.workspace[:4].view(torch.int32).item()) != 0
+    assert p.seg_offsets.cpu().numpy()[-1] == 5
+    assert p.counts.cpu().numpy().sum() == 5
+
+
+# --------------------------------------------------------------- full layers
+def _layer_parity(G, cfg, tokens=None):
+    d = gen.generate(cfg)
+    buf = G.run_layer(d, cfg)
+    ref = oracle.moe_forward(d, cfg, tokens=tokens)
+    assert np.array_equal(buf.ids.cpu().numpy(), ref["ids"])
+    np.testing.assert_allclose(buf.w.cpu().numpy().astype(np.float64), ref["w"], rtol=G.GATE_RTOL, atol=0)
+    assert np.array_equal(buf.perm.counts.cpu().numpy(), ref["counts"])
+    assert np.array_equal(buf.perm.seg_offsets.cpu().numpy(), ref["seg_offsets"])
+    assert np.array_equal(buf.perm.sorted_pair.cpu().numpy(), ref["sorted_pair"])
+    assert np.array_equal(buf.perm.pair_pos.cpu().numpy(), ref["pair_pos"])
+    sel = ref["tokens"]
+    rows = ref["pair_pos"].reshape(cfg.T, cfg.k)[sel].ravel()
+    # intermediates: diagnostics with a looser bar (h is rounded to bf16 before the down GEMM)
+    hm = oracle.compare(G.bf16_to_np(buf.h)[rows], ref["h_perm"][rows])
+    ym = oracle.compare(G.bf16_to_np(buf.y_perm)[rows], ref["y_perm"][rows])
+    assert hm["rel_l2"] < 1e-2 and ym["rel_l2"] < 1e-2, (hm, ym)
+    m = G.check_close(G.bf16_to_np(buf.out)[sel], ref["out"][sel], cfg.name)
+    print(cfg.name, "h", hm, "y", ym, "out", m)
+    return buf
+
+
+def test_layer_tiny_full(G):
+    _layer_parity(G, gen.config("tiny"))
+
+
+def test_layer_decode_full(G):
+    _layer_parity(G, gen.config("olmoe_decode"))
+
+
+@pytest.mark.parametrize("T", [1, 33, 97])
+def test_layer_ragged_small(G, T):
+    _layer_parity(G, gen.config("tiny", T=T, seed=7 + T))
+
+
+def test_layer_g128_one_hot_expert(G):
+    # every token routed to expert 3 (all other experts empty), G = 128
+    cfg = gen.config("tiny", T=70, H=256, I=256, E=6, k=1, G=128, seed=77)
+    d = gen.generate(cfg)
+    d["logits"][:, 3] = 50.0
+    buf = G.run_layer(d, cfg)
+    ref = oracle.moe_forward(d, cfg)
+    G.check_close(G.bf16_to_np(buf.out), ref["out"], "one expert")
+
+
+def test_layer_k_equals_E(G):
+    _layer_parity(G, gen.config("tiny", T=40, E=4, k=4, seed=5))
+
+
+def test_layer_prefill_sampled(G):
+    cfg = gen.config("olmoe_prefill")
+    tokens = np.random.default_rng(1).choice(cfg.T, size=48, replace=False)
+    _layer_parity(G, cfg, tokens=np.sort(tokens))
+
+
+def test_layer_prefill_zipf_sampled(G):
+    cfg = gen.config("olmoe_prefill_zipf")
+    tokens = np.random.default_rng(2).choice(cfg.T, size=48, replace=False)
+    _layer_parity(G, cfg, tokens=np.sort(tokens))
+
+
+def test_layer_mwq_small_full(G):
+    _layer_parity(G, gen.config("mixtral_mwq", T=96, H=512, I=1024, E=4, k=2, seed=41))
+
+
+def test_layer_mwq_all_b4_equals_int4(G):
+    """Nested planes at b = 4 everywhere give the INT4 path on the same codes."""
+    cfg = gen.config("mixtral_mwq", T=64, H=256, I=512, E=4, k=2, seed=43)
+    d = gen.generate(cfg)
+    d["pair_bits"][:] = 4
+    buf = G.run_layer(d, cfg)
+    ref = oracle.moe_forward(d, cfg)
+    G.check_close(G.bf16_to_np(buf.out), ref["out"], "mwq b=4")
+
+
+def test_layer_mwq_full_size_sampled(G):
+    cfg = gen.config("mixtral_mwq")
+    _layer_parity(G, cfg, tokens=np.array([0, 211, 377, 510]))
+
+
+# ------------------------------------------------------------------- delta
+def _delta_parity(G, cfg, tokens=None):
+    d = gen.generate(cfg)
+    perm, y_perm, out = G.run_delta(d, cfg)
+    ref = oracle.delta_linear(d, cfg, tokens=tokens)
+    assert np.array_equal(perm.counts.cpu().numpy(), ref["counts"])
+    assert np.array_equal(perm.sorted_pair.cpu().numpy(), ref["sorted_pair"])
+    sel = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
+    m = G.check_close(G.bf16_to_np(out)[sel], ref["out"][sel], cfg.name)
+    print(cfg.name, m)
+
+
+def test_delta_small_full(G):
+    _delta_parity(G, gen.config("meswitch_delta", requests=12, tokens_per_request=5, K=512, N=256, E=4,
+                                n_salient=7, seed=9))
+
+
+def test_delta_full_size_sampled(G):
+    cfg = gen.config("meswitch_delta")
+    _delta_parity(G, cfg, tokens=np.array([0, 17, 1000, 2047, 3333, 4095]))
+
+
+# ---------------------------------------------------------- combine, determinism
+def test_combine_round_trip(G):
+    cfg = gen.config("tiny")
+    d = gen.generate(cfg)
+    x = G.t(d["x"])
+    ids, w = G.q.moe_route_topk(G.t(d["logits"]), cfg.k)
+    p = G.q.moe_permute(ids, cfg.E)
+    x_perm = G.q.moe_permute(ids, cfg.E, x=x, want_x_perm=True).x_perm
+    back = G.q.moe_unpermute_combine(x_perm, p.pair_pos, w, cfg.T, cfg.k)
+    torch.cuda.synchronize()
+    G.check_close(G.bf16_to_np(back), oracle.bf16_to_f64(d["x"]), "round trip")
+
+
+def test_bitwise_deterministic(G):
+    cfg = gen.config("olmoe_decode")
+    d = gen.generate(cfg)
+    gu, dn = G.tiled_layer(d, cfg)
+    a = G.run_layer(d, cfg, gu, dn).out.clone()
+    b = G.run_layer(d, cfg, gu, dn).out.clone()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
