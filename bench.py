@@ -44,7 +44,31 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="weight copies rotated (0: enough to exceed 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU oracle sample")
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="only time a plain 512 MiB device copy (achievable HBM rate; counter calibration)")
     return ap.parse_args()
+
+
+def hbm_probe():
+    """Achievable HBM rate of a plain device-to-device copy of known size."""
+    import torch
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    reps = 20
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    gbs = 2 * n / (ms * 1e-3) / 1e9
+    print(json.dumps({"probe": "device copy", "bytes_read": n, "bytes_written": n, "ms": round(ms, 4),
+                      "gbs_read_plus_write": round(gbs, 1)}), flush=True)
 
 
 def to_dev(a):
@@ -64,6 +88,9 @@ def weight_bytes_per_expert(cfg, matrix):
 
 def main():
     args = parse()
+    if args.hbm_probe:
+        hbm_probe()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)

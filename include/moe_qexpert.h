@@ -146,9 +146,10 @@ moe_status moe_permute(const int32_t* topk_ids, const uint8_t* pair_bits,
  *
  * Layouts: MOE_LAYOUT_CANONICAL is the storage layout above.  The GEMM reads
  * MOE_LAYOUT_TILED, produced once, offline, by moe_repack_weights: codes,
- * planes, salient_val and base are re-ordered into 64-lane MFMA tiles (same
- * byte counts for codes / planes / base); scales, step and salient_idx keep
- * their canonical layout and may be shared between the two descriptors.
+ * planes, salient_val and base are re-ordered into tiles of 16 output
+ * channels x 128 inputs laid out as 64-lane MFMA operand fragments (same byte
+ * counts for codes / planes / base); scales, step and salient_idx keep their
+ * canonical layout and may be shared between the two descriptors.
  */
 #define MOE_W_INT4_GROUP 1
 #define MOE_W_MWQ_2_3_4 2
@@ -229,8 +230,7 @@ moe_status moe_repack_weights(const moe_wdesc* src, const moe_wdesc* dst, void* 
  *               device counts back
  *   out         bf16 or fp32 (see epilogue) [M_total][N or N/2], 16-byte aligned
  *   workspace   moe_grouped_qgemm_workspace_size(...) bytes (may be 0 / NULL)
- * Supported: N % 32 == 0 (SWIGLU: (N/2) % 32 == 0), K % 128 == 0, G in
- * {16, 32, 64, 128} for INT4 and MWQ.
+ * Supported: N % 32 == 0, K % 128 == 0, G in {32, 64, 128} for INT4 and MWQ.
  */
 size_t moe_grouped_qgemm_workspace_size(const moe_wdesc* w, int32_t A_rows, int32_t M_total);
 moe_status moe_grouped_qgemm(const moe_wdesc* w, const uint16_t* A, int32_t A_rows,

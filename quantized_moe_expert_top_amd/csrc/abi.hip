@@ -5,7 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "../../include/moe_qexpert.h"
+#include "moe_qexpert.h"
 #include "common.h"
 
 namespace {
@@ -50,8 +50,8 @@ moe_status check_desc(const moe_wdesc* w, int layout, bool need_buffers) {
       return fail(MOE_ERR_UNSUPPORTED, "n_salient=%d (0..64 supported)", w->n_salient);
   } else {
     const int G = w->group_size;
-    if (!(G == 16 || G == 32 || G == 64 || G == 128))
-      return fail(MOE_ERR_UNSUPPORTED, "group_size %d (16, 32, 64 or 128 supported)", G);
+    if (!(G == 32 || G == 64 || G == 128))
+      return fail(MOE_ERR_UNSUPPORTED, "group_size %d (32, 64 or 128 supported)", G);
     if (w->zero_point < 0 || w->zero_point > 15) return fail(MOE_ERR_BAD_SHAPE, "zero_point %d", w->zero_point);
   }
   if (!need_buffers) return MOE_OK;
@@ -232,8 +232,6 @@ moe_status moe_grouped_qgemm(const moe_wdesc* w, const uint16_t* A, int32_t A_ro
   if (M_total < 0 || A_rows < 0) return fail(MOE_ERR_BAD_SHAPE, "M_total=%d A_rows=%d", M_total, A_rows);
   if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SWIGLU && epilogue != MOE_EPI_NONE_F32)
     return fail(MOE_ERR_BAD_FORMAT, "unknown epilogue %d", epilogue);
-  if (epilogue == MOE_EPI_SWIGLU && (w->N / 2) % 32 != 0)
-    return fail(MOE_ERR_UNSUPPORTED, "SwiGLU needs N/2 a multiple of 32 (N=%d)", w->N);
   if (gather_pair) {
     if (k < 1) return fail(MOE_ERR_BAD_SHAPE, "k=%d with gather_pair", k);
     if ((int64_t)A_rows * k < M_total) return fail(MOE_ERR_BAD_SHAPE, "A_rows*k < M_total");
@@ -250,7 +248,9 @@ moe_status moe_grouped_qgemm(const moe_wdesc* w, const uint16_t* A, int32_t A_ro
   if (need && !workspace) return fail(MOE_ERR_NULL_ARG, "workspace is NULL");
   st = check_device();
   if (st != MOE_OK) return st;
-  moe::QGemmArgs a{q, A, gather_pair, k, seg_offsets, w->E * (w->format == MOE_W_MWQ_2_3_4 ? 3 : 1), M_total,
+  if ((int64_t)A_rows * w->K * 2 >= ((int64_t)1 << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "activation matrix of %lld bytes (4 GiB or more)", (long long)A_rows * w->K * 2);
+  moe::QGemmArgs a{q, A, A_rows, gather_pair, k, seg_offsets, w->E * (w->format == MOE_W_MWQ_2_3_4 ? 3 : 1), M_total,
                    epilogue, out, workspace};
   return hip_status(moe::launch_qgemm(a, (hipStream_t)stream), "grouped_qgemm launch");
 }

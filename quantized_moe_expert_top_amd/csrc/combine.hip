@@ -11,32 +11,47 @@ namespace {
 constexpr int kThreads = 256;
 
 // Y_F32: expert outputs in fp32 (not rounded before the combine) or bf16.
+// Slots are taken in batches of 8: all row loads of a batch are issued before
+// the first multiply-add, in slot order.
 template <bool Y_F32>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restrict__ yv,
                                                            const int32_t* __restrict__ pos,
                                                            const float* __restrict__ w, int k, int H,
                                                            uint16_t* __restrict__ out) {
+  constexpr int B = 8;
   const int t = blockIdx.x;
   const int nvec = H >> 3;
   for (int c = threadIdx.x; c < nvec; c += kThreads) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int p = pos[(size_t)t * k + j];
-      const float g = w ? w[(size_t)t * k + j] : 1.0f;
-      if (Y_F32) {
-        const f32x4* row = reinterpret_cast<const f32x4*>(static_cast<const float*>(yv) + (size_t)p * H);
-        const f32x4 v0 = row[2 * c], v1 = row[2 * c + 1];
+    for (int j0 = 0; j0 < k; j0 += B) {
+      f32x4 v[B][2];
+      float g[B];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[q] = __builtin_fmaf(g, v0[q], acc[q]);
-          acc[4 + q] = __builtin_fmaf(g, v1[q], acc[4 + q]);
+      for (int i = 0; i < B; ++i) {
+        const int j = j0 + i;
+        if (j < k) {
+          const int p = pos[(size_t)t * k + j];
+          g[i] = w ? w[(size_t)t * k + j] : 1.0f;
+          if (Y_F32) {
+            const f32x4* row = reinterpret_cast<const f32x4*>(static_cast<const float*>(yv) + (size_t)p * H);
+            v[i][0] = row[2 * c];
+            v[i][1] = row[2 * c + 1];
+          } else {
+            const u32x4 b = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(yv) + (size_t)p * H)[c];
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+              v[i][q] = f32x4{bf16_lo(b[2 * q]), bf16_hi(b[2 * q]), bf16_lo(b[2 * q + 1]), bf16_hi(b[2 * q + 1])};
+          }
         }
-      } else {
-        const u32x4 v = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(yv) + (size_t)p * H)[c];
+      }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] = __builtin_fmaf(g, bf16_lo(v[q]), acc[2 * q]);
-          acc[2 * q + 1] = __builtin_fmaf(g, bf16_hi(v[q]), acc[2 * q + 1]);
+      for (int i = 0; i < B; ++i) {
+        if (j0 + i < k) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[q] = __builtin_fmaf(g[i], v[i][0][q], acc[q]);
+            acc[4 + q] = __builtin_fmaf(g[i], v[i][1][q], acc[4 + q]);
+          }
         }
       }
     }

@@ -30,6 +30,33 @@ __device__ __forceinline__ float f16_to_f32(uint16_t v) { return (float)__builti
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// (x & m) | o in one v_and_or_b32 (the compiler otherwise splits it when both
+// constants are literals).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(o));
+  return r;
+}
+
+// Raw buffer loads: wave-uniform resource + per-lane byte offset + uniform
+// byte offset.  Reads at or past `bytes` return zero instead of faulting.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_x4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ u32x2 buf_x2(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_x1(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint16_t buf_u16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
 // D = A * B + C for a 32x32 tile with K = 16 (v_mfma_f32_32x32x16_bf16).
 // Operand lane layout: lane l holds row (l % 32), k = 8*(l / 32) .. +7 of A
 // (and column (l % 32), same k range, of B).  Accumulator: lane l, register r
@@ -39,6 +66,46 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// Top-k of one token by one wavefront, E <= 64 (expert gate of the Dual
+// Routing equations, D2MoE page): lane e holds logit e and counts the experts
+// that beat it (larger logit, or equal logit and lower index); a count below k
+// is the lane's slot.  Gates = softmax over the k selected logits in float64,
+// rounded once to float32.  sel_val / sel_exp: 64-entry LDS scratch of this
+// wavefront; slot_ids (optional) receives the k ids as well.
+// v: this lane's logit (lane < E), -inf for lanes >= E.
+__device__ __forceinline__ void route_token_rank(float v, int E, int k, int32_t* __restrict__ ids,
+                                                 float* __restrict__ w, float* sel_val, double* sel_exp,
+                                                 int* slot_ids) {
+  const int lane = threadIdx.x & 63;
+  int rank = 0;
+#pragma unroll
+  for (int j = 0; j < 64; ++j) {
+    const float vj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
+    rank += (vj > v || (vj == v && j < lane)) ? 1 : 0;
+  }
+  if (lane < E && rank < k) {
+    ids[rank] = lane;
+    sel_val[rank] = v;
+    if (slot_ids) slot_ids[rank] = lane;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const double l0 = (double)sel_val[0];
+  if (lane < k) sel_exp[lane] = exp((double)sel_val[lane] - l0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < k) {
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j) sum += sel_exp[j];
+    w[lane] = (float)(sel_exp[lane] / sum);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // Kernel-side launch helpers return hipGetLastError() after the launch.
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
@@ -60,6 +127,7 @@ struct PermuteArgs {
 size_t permute_workspace_bytes(int P, int E, int S);
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 
+
 hipError_t launch_combine(const void* y, bool y_f32, const int32_t* pos, const float* w, int T, int k, int H,
                           uint16_t* out, hipStream_t s);
 
@@ -78,6 +146,7 @@ struct QWeights {
 struct QGemmArgs {
   QWeights w;
   const uint16_t* A;
+  int A_rows;
   const int32_t* gather;
   int k;
   const int32_t* seg_offsets;

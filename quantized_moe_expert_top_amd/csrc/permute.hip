@@ -48,9 +48,11 @@ __device__ __forceinline__ int nbits_for(int n) {  // bits to tell keys 0..n apa
   return b;
 }
 
-// Exclusive scan in place over data[0..n) (LDS), all threads of the block.
+// Exclusive scan in place over data[0..n) (LDS), all NT threads of the block.
 // Returns the total.
-__device__ int block_exclusive_scan(int* data, int n, int* scratch /* >= kThreads/64 + 1 ints */) {
+template <int NT>
+__device__ int block_exclusive_scan(int* data, int n, int* scratch /* >= NT/64 + 1 ints */) {
+  constexpr int kThreads = NT;
   const int tid = threadIdx.x;
   const int per = (n + kThreads - 1) / kThreads;
   const int lo = min(n, tid * per), hi = min(n, lo + per);
@@ -88,9 +90,12 @@ __device__ int block_exclusive_scan(int* data, int n, int* scratch /* >= kThread
 }
 
 // Stable scatter of pairs [p0, p1) whose key bases are in base[] (LDS; base[key]
-// = output position of the next pair with that key).  tagbuf: 4 * (NK+1) ints.
+// = output position of the next pair with that key).  tagbuf: NT/64 * (NK+1)
+// ints.  NT threads take NT pairs per step.
+template <int NT>
 __device__ void scatter_chunk(const Keyer& kr, int p0, int p1, int* base, int* tagbuf, int32_t* sorted_pair,
                               int32_t* pair_pos) {
+  constexpr int kThreads = NT;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nk1 = kr.NK + 1;
   const int nbits = nbits_for(kr.NK);
@@ -151,11 +156,11 @@ __global__ __launch_bounds__(kThreads) void permute_small_kernel(Keyer kr, int P
     counts[e] = c;
   }
   __syncthreads();
-  block_exclusive_scan(hist, nk1, scratch);
+  block_exclusive_scan<kThreads>(hist, nk1, scratch);
   for (int i = tid; i < nk1; i += kThreads) seg_offsets[i] = hist[i];
   if (tid == 0) flag[0] = sbad;
   __syncthreads();
-  scatter_chunk(kr, 0, P, hist, tagbuf, sorted_pair, pair_pos);
+  scatter_chunk<kThreads>(kr, 0, P, hist, tagbuf, sorted_pair, pair_pos);
 }
 
 // ---- multi-block path -------------------------------------------------------
@@ -209,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void permute_scan_kernel(Keyer kr, int nb
     counts[e] = c;
   }
   __syncthreads();
-  block_exclusive_scan(total, nk1, scratch);
+  block_exclusive_scan<kThreads>(total, nk1, scratch);
   for (int i = tid; i < nk1; i += kThreads) seg_offsets[i] = total[i];
   for (int key = tid; key < nk1; key += kThreads) {
     const int base = total[key];
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void permute_scatter_kernel(Keyer kr, int
   for (int i = tid; i < 4 * nk1; i += kThreads) tagbuf[i] = -1;
   __syncthreads();
   const int p0 = blockIdx.x * kChunk, p1 = min(P, p0 + kChunk);
-  scatter_chunk(kr, p0, p1, base, tagbuf, sorted_pair, pair_pos);
+  scatter_chunk<kThreads>(kr, p0, p1, base, tagbuf, sorted_pair, pair_pos);
 }
 
 __global__ __launch_bounds__(kThreads) void gather_rows_kernel(const uint16_t* __restrict__ x, int H, int k,

@@ -3,23 +3,24 @@
 // input channels of a 2-bit delta, whose codes become the zero code because
 // their value travels separately in bf16).
 //
-// Tiled layout, one "tile block" per (expert e, 32 output channels ct, 128
+// Tiled layout, one "tile block" per (expert e, 16 output channels ct, 128
 // input channels kb), tile blocks ordered (e, ct, kb) so that a wavefront
 // streams one channel tile along K contiguously.  Inside a tile block, lane l
-// of a wavefront owns channel ct*32 + (l % 32) and, for every 16-wide K step
-// s = 0..7, the 8 inputs k = kb*128 + 16*s + 8*(l/32) + i, i = 0..7 (the MFMA
-// 32x32x16 operand layout).  The bits of one lane and step are placed so that
-// pairs (i = 2p, 2p+1) land in the low / high halfword of a dword after one
-// shift and mask:
-//   4-bit  (2 KB / tile block): byte (s/4)*1024 + 16*l + 4*(s%4) is a dword with
-//          element i at bit 16*(i&1) + 4*(i>>1).
-//   2-bit  (1 KB): dword at 16*l + 4*(s/2); with P = 4*(s%2) + (i>>1), element i
-//          at bit 16*(i&1) + 2*P.
-//   1-bit  (512 B): dword at 8*l + 4*(s/4); with P = 4*(s%4) + (i>>1), element i
-//          at bit 16*(i&1) + P.
-//   bf16 base (8 KB): 16 bytes at 1024*s + 16*l hold the 8 inputs in order.
-//   salient values: per (e, ct) ceil(S/16) blocks of 1 KB; lane l holds slots
-//          16*step + 8*(l/32) + i of channel ct*32 + l%32 (zero past S).
+// of a wavefront owns channel ct*16 + (l % 16) and, for each 32-wide K step
+// t = 0..3, the 8 inputs k = kb*128 + 32*t + 8*(l/16) + i, i = 0..7 (the
+// operand layout of v_mfma_f32_16x16x32_bf16).  The bits of one lane and step
+// are placed so that pairs (i = 2p, 2p+1) land in the low / high halfword of a
+// dword after one shift and mask:
+//   4-bit  (1 KB / tile block): dword at 16*l + 4*t; element i at bit
+//          16*(i&1) + 4*(i>>1).
+//   2-bit  (512 B): dword at 8*l + 4*(t/2); with P = 4*(t%2) + (i>>1), element
+//          i at bit 16*(i&1) + 2*P.
+//   1-bit  (256 B): dword at 4*l; with P = 4*t + (i>>1), element i at bit
+//          16*(i&1) + P.
+//   bf16 base (4 KB, no expert index): 16 bytes at 1024*t + 16*l hold the 8
+//          inputs in order.
+//   salient values: per (e, ct) ceil(S/32) blocks of 1 KB; lane l holds slots
+//          32*step + 8*(l/16) + i of channel ct*16 + l%16 (zero past S).
 #include "common.h"
 
 namespace moe {
@@ -27,88 +28,83 @@ namespace moe {
 namespace {
 constexpr int kThreads = 256;
 
+struct TileIdx {
+  size_t e;
+  int ct, kb;
+};
+__device__ __forceinline__ TileIdx tile_of(size_t blk, int N, int K) {
+  const int KB = K / 128, NT = N / 16;
+  TileIdx r;
+  r.kb = (int)(blk % KB);
+  const size_t ect = blk / KB;
+  r.ct = (int)(ect % NT);
+  r.e = ect / NT;
+  return r;
+}
+
 __global__ __launch_bounds__(kThreads) void repack_u4_kernel(const uint8_t* __restrict__ src, int N, int K,
                                                              uint32_t* __restrict__ dst, size_t ndw) {
   const size_t d = (size_t)blockIdx.x * kThreads + threadIdx.x;
   if (d >= ndw) return;
-  const int KB = K / 128, NT = N / 32;
-  const size_t blk = d / 512;
-  const int within = (int)(d % 512);
-  const int h = within / 256, l = (within % 256) / 4, w = within % 4;
-  const int kb = (int)(blk % KB);
-  const size_t ect = blk / KB;
-  const int ct = (int)(ect % NT);
-  const size_t e = ect / NT;
-  const int ch = ct * 32 + (l & 31);
-  const int s = 4 * h + w;
-  const int k0 = kb * 128 + 16 * s + 8 * (l >> 5);
-  const uint32_t v = *reinterpret_cast<const uint32_t*>(src + (e * N + ch) * (size_t)(K / 2) + k0 / 2);
+  const TileIdx ti = tile_of(d / 256, N, K);
+  const int within = (int)(d % 256);
+  const int l = within / 4, t = within % 4;
+  const int ch = ti.ct * 16 + (l & 15);
+  const int k0 = ti.kb * 128 + 32 * t + 8 * (l >> 4);
+  const uint32_t v = *reinterpret_cast<const uint32_t*>(src + (ti.e * N + ch) * (size_t)(K / 2) + k0 / 2);
   uint32_t o = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) o |= ((v >> (4 * i)) & 0xFu) << (16 * (i & 1) + 4 * (i >> 1));
   dst[d] = o;
 }
 
-// 2-bit plane; zero_code >= 0 replaces the codes of salient channels (DELTA2).
-__global__ __launch_bounds__(kThreads) void repack_u2_kernel(const uint8_t* __restrict__ src, int N, int K,
-                                                             uint32_t* __restrict__ dst, const int32_t* sal_idx,
-                                                             int n_sal, int zero_code) {
-  // one workgroup = one 1 KB tile block (256 dwords)
+// 2-bit plane, one 128-thread workgroup per 512-byte tile block; zero_code >= 0
+// replaces the codes of salient channels (2-bit delta).
+__global__ __launch_bounds__(128) void repack_u2_kernel(const uint8_t* __restrict__ src, int N, int K,
+                                                        uint32_t* __restrict__ dst, const int32_t* sal_idx,
+                                                        int n_sal, int zero_code) {
   __shared__ uint32_t salmask[4];
-  const int KB = K / 128, NT = N / 32;
-  const size_t blk = blockIdx.x;
-  const int kb = (int)(blk % KB);
-  const size_t ect = blk / KB;
-  const int ct = (int)(ect % NT);
-  const size_t e = ect / NT;
+  const TileIdx ti = tile_of(blockIdx.x, N, K);
   if (threadIdx.x < 4) salmask[threadIdx.x] = 0;
   __syncthreads();
   if (sal_idx && (int)threadIdx.x < n_sal) {
-    const int kk = sal_idx[e * n_sal + threadIdx.x] - kb * 128;
+    const int kk = sal_idx[ti.e * n_sal + threadIdx.x] - ti.kb * 128;
     if (kk >= 0 && kk < 128) atomicOr(&salmask[kk >> 5], 1u << (kk & 31));
   }
   __syncthreads();
-  const int within = threadIdx.x;
-  const int l = within / 4, w = within % 4;
-  const int ch = ct * 32 + (l & 31);
+  const int l = threadIdx.x / 2, w = threadIdx.x % 2;
+  const int ch = ti.ct * 16 + (l & 15);
   uint32_t o = 0;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int s = 2 * w + t;
-    const int koff = 16 * s + 8 * (l >> 5);
-    const int k0 = kb * 128 + koff;
-    const uint32_t v = *reinterpret_cast<const uint16_t*>(src + (e * N + ch) * (size_t)(K / 4) + k0 / 4);
+  for (int tt = 0; tt < 2; ++tt) {
+    const int t = 2 * w + tt;
+    const int koff = 32 * t + 8 * (l >> 4);
+    const int k0 = ti.kb * 128 + koff;
+    const uint32_t v = *reinterpret_cast<const uint16_t*>(src + (ti.e * N + ch) * (size_t)(K / 4) + k0 / 4);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       uint32_t f = (v >> (2 * i)) & 3u;
       const int kk = koff + i;
       if (zero_code >= 0 && ((salmask[kk >> 5] >> (kk & 31)) & 1u)) f = (uint32_t)zero_code;
-      const int P = 4 * t + (i >> 1);
+      const int P = 4 * tt + (i >> 1);
       o |= f << (16 * (i & 1) + 2 * P);
     }
   }
-  dst[blk * 256 + within] = o;
+  dst[(size_t)blockIdx.x * 128 + threadIdx.x] = o;
 }
 
 __global__ __launch_bounds__(kThreads) void repack_u1_kernel(const uint8_t* __restrict__ src, int N, int K,
                                                              uint32_t* __restrict__ dst, size_t ndw) {
   const size_t d = (size_t)blockIdx.x * kThreads + threadIdx.x;
   if (d >= ndw) return;
-  const int KB = K / 128, NT = N / 32;
-  const size_t blk = d / 128;
-  const int within = (int)(d % 128);
-  const int l = within / 2, w = within % 2;
-  const int kb = (int)(blk % KB);
-  const size_t ect = blk / KB;
-  const int ct = (int)(ect % NT);
-  const size_t e = ect / NT;
-  const int ch = ct * 32 + (l & 31);
+  const TileIdx ti = tile_of(d / 64, N, K);
+  const int l = (int)(d % 64);
+  const int ch = ti.ct * 16 + (l & 15);
   uint32_t o = 0;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int s = 4 * w + t;
-    const int k0 = kb * 128 + 16 * s + 8 * (l >> 5);
-    const uint32_t v = src[(e * N + ch) * (size_t)(K / 8) + k0 / 8];
+    const int k0 = ti.kb * 128 + 32 * t + 8 * (l >> 4);
+    const uint32_t v = src[(ti.e * N + ch) * (size_t)(K / 8) + k0 / 8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int P = 4 * t + (i >> 1);
@@ -123,22 +119,22 @@ __global__ __launch_bounds__(kThreads) void repack_base_kernel(const uint16_t* _
   const size_t d = (size_t)blockIdx.x * kThreads + threadIdx.x;
   if (d >= nvec) return;
   const int KB = K / 128;
-  const size_t blk = d / 512;
-  const int within = (int)(d % 512);
-  const int s = within / 64, l = within % 64;
+  const size_t blk = d / 256;
+  const int within = (int)(d % 256);
+  const int t = within / 64, l = within % 64;
   const int kb = (int)(blk % KB);
   const int ct = (int)(blk / KB);
-  const int ch = ct * 32 + (l & 31);
-  const int k0 = kb * 128 + 16 * s + 8 * (l >> 5);
+  const int ch = ct * 16 + (l & 15);
+  const int k0 = kb * 128 + 32 * t + 8 * (l >> 4);
   dst[d] = *reinterpret_cast<const u32x4*>(src + (size_t)ch * K + k0);
 }
 
-__global__ __launch_bounds__(kThreads) void repack_salient_kernel(const uint16_t* __restrict__ src, int E, int N,
+__global__ __launch_bounds__(kThreads) void repack_salient_kernel(const uint16_t* __restrict__ src, int N,
                                                                   int n_sal, int nsteps,
                                                                   uint32_t* __restrict__ dst, size_t ndw) {
   const size_t d = (size_t)blockIdx.x * kThreads + threadIdx.x;
   if (d >= ndw) return;
-  const int NT = N / 32;
+  const int NT = N / 16;
   const size_t blk = d / 256;  // (e, ct, step)
   const int within = (int)(d % 256);
   const int l = within / 4, w = within % 4;
@@ -146,11 +142,11 @@ __global__ __launch_bounds__(kThreads) void repack_salient_kernel(const uint16_t
   const size_t ect = blk / nsteps;
   const int ct = (int)(ect % NT);
   const size_t e = ect / NT;
-  const int ch = ct * 32 + (l & 31);
+  const int ch = ct * 16 + (l & 15);
   uint32_t o = 0;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int j = 16 * step + 8 * (l >> 5) + 2 * w + h;
+    const int j = 32 * step + 8 * (l >> 4) + 2 * w + h;
     const uint32_t v = j < n_sal ? src[(e * n_sal + j) * (size_t)N + ch] : 0u;
     o |= v << (16 * h);
   }
@@ -161,8 +157,8 @@ inline unsigned grid_for(size_t n) { return (unsigned)((n + kThreads - 1) / kThr
 }  // namespace
 
 size_t tiled_salient_bytes(int E, int N, int n_sal) {
-  const size_t nsteps = (size_t)(n_sal + 15) / 16;
-  return (size_t)E * (N / 32) * nsteps * 1024;
+  const size_t nsteps = (size_t)(n_sal + 31) / 32;
+  return (size_t)E * (N / 16) * nsteps * 1024;
 }
 
 hipError_t launch_repack(const QWeights& src, const QWeights& dst, hipStream_t s) {
@@ -174,9 +170,9 @@ hipError_t launch_repack(const QWeights& src, const QWeights& dst, hipStream_t s
     hipLaunchKernelGGL(repack_u4_kernel, dim3(grid_for(ndw)), dim3(kThreads), 0, s, src.codes, src.N, src.K, codes,
                        ndw);
   } else {
-    const size_t nblk = ENK / (32 * 128);
+    const size_t nblk = ENK / (16 * 128);
     const bool delta = src.fmt == 3;
-    hipLaunchKernelGGL(repack_u2_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, s, src.codes, src.N, src.K, codes,
+    hipLaunchKernelGGL(repack_u2_kernel, dim3((unsigned)nblk), dim3(128), 0, s, src.codes, src.N, src.K, codes,
                        delta ? src.sal_idx : nullptr, delta ? src.n_sal : 0, delta ? src.z : -1);
     if (src.fmt == 2) {
       const size_t ndw = ENK / 32;
@@ -187,11 +183,10 @@ hipError_t launch_repack(const QWeights& src, const QWeights& dst, hipStream_t s
     }
     if (delta) {
       if (src.n_sal > 0) {
-        const int nsteps = (src.n_sal + 15) / 16;
+        const int nsteps = (src.n_sal + 31) / 32;
         const size_t ndw = tiled_salient_bytes(src.E, src.N, src.n_sal) / 4;
-        hipLaunchKernelGGL(repack_salient_kernel, dim3(grid_for(ndw)), dim3(kThreads), 0, s, src.sal_val, src.E,
-                           src.N, src.n_sal, nsteps, reinterpret_cast<uint32_t*>(const_cast<uint16_t*>(dst.sal_val)),
-                           ndw);
+        hipLaunchKernelGGL(repack_salient_kernel, dim3(grid_for(ndw)), dim3(kThreads), 0, s, src.sal_val, src.N,
+                           src.n_sal, nsteps, reinterpret_cast<uint32_t*>(const_cast<uint16_t*>(dst.sal_val)), ndw);
       }
       if (src.base) {
         const size_t nvec = (size_t)src.N * src.K / 8;

@@ -2,8 +2,10 @@
 // Design): per token, the k largest logits in descending order, ties to the
 // lower expert index, and gate weights = softmax over the k selected logits.
 //
-// One 64-lane wavefront per token.  Lane l owns experts l, l+64, ... (up to
-// 16 per lane, E <= 1024).  Each of the k rounds is a wave-wide arg-max over
+// One 64-lane wavefront per token.  For E <= 64 every lane holds one logit and
+// computes its rank against the other 63 (scalar broadcasts, no shuffles).
+// For larger E lane l owns experts l, l+64, ... (up to 16 per lane,
+// E <= 1024) and each of the k rounds is a wave-wide arg-max over
 // (logit, -index) with butterfly shuffles; the winner is marked taken.  The
 // softmax runs in float64 on the selected values (k exp calls per token) and
 // is rounded once to float32, so the gates differ from the exact value by at
@@ -82,12 +84,28 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     w[(size_t)t * k + j] = (float)(e / sum);
   }
 }
+// E <= 64: lane e holds logit e and counts the experts that beat it (larger
+// logit, or equal logit and lower index); that count is its slot if < k.
+__global__ __launch_bounds__(256) void route_rank_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                         int32_t* __restrict__ ids, float* __restrict__ w) {
+  __shared__ float sel_val[kWavesPerBlock][64];
+  __shared__ double sel_exp[kWavesPerBlock][64];
+  const int wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * kWavesPerBlock + wv;
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
+  const float v = lane < E ? logits[(size_t)t * E + lane] : -__builtin_inff();
+  route_token_rank(v, E, k, ids + (size_t)t * k, w + (size_t)t * k, sel_val[wv], sel_exp[wv], nullptr);
+}
 }  // namespace
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL(route_topk_kernel, dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, logits, T, E, k, ids, w);
+  if (E <= 64)
+    hipLaunchKernelGGL(route_rank_kernel, dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, logits, T, E, k, ids, w);
+  else
+    hipLaunchKernelGGL(route_topk_kernel, dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, logits, T, E, k, ids, w);
   return hipGetLastError();
 }
 
