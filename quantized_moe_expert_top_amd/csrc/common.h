@@ -29,6 +29,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __builtin_bit_
 __device__ __forceinline__ float f16_to_f32(uint16_t v) { return (float)__builtin_bit_cast(_Float16, v); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+// acc + lo(v) + hi(v) for a bf16 pair, one v_dot2 with (1, 1).  Takes the
+// dword by value: a bit_cast applied directly to an ext_vector element
+// expression (v[h]) is miscompiled to always read element 0.
+__device__ __forceinline__ float add_bf16_pair(uint32_t v, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v), __builtin_bit_cast(bf16x2_t, 0x3F803F80u),
+                                         acc, false);
+}
 
 // (x & m) | o in one v_and_or_b32 (the compiler otherwise splits it when both
 // constants are literals).

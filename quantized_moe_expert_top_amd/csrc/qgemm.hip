@@ -27,6 +27,9 @@
 //                                repack); salient channels are one more MFMA
 //                                K chunk with bf16 values; the shared base is a
 //                                plain bf16 MFMA on the same A operand
+#include <stdlib.h>
+#include <string.h>
+
 #include "common.h"
 
 namespace moe {
@@ -55,8 +58,11 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Locate the row tile `y` (in segment order) -> segment and first row.
-__device__ __forceinline__ bool find_tile(const int32_t* seg_offsets, int nseg, int y, int& seg, int& m0) {
+// Locate the row tile `y` (in segment order; tiles of `rows_per_tile` rows)
+// -> segment and first row.
+__device__ __forceinline__ bool find_tile(const int32_t* seg_offsets, int nseg, int y, int& seg, int& m0,
+                                          int rows_per_tile = kRows) {
+  const int kRows = rows_per_tile;
   const int lane = threadIdx.x & 63;
   int carry = 0;
   for (int s0 = 0; s0 < nseg; s0 += 64) {
@@ -448,6 +454,233 @@ __global__ __launch_bounds__(kThreads) void qgemm_delta_kernel(KArgs p) {
   store_tiles<EPI>(p, c, acc, ct0, ct1, v1, hch, two);
 }
 
+// ------------------------------------------------------------------ prefill
+// Large row tiles: MT rows (64 or 128) x 64 SwiGLU channels / 128 plain
+// channels per workgroup of 4 wavefronts (2 x 2: row half x channel half).
+// Each wavefront dequantises its 4 weight tiles once per K block and reuses
+// them for MT/2 rows.  The activation rows are gathered once per K block into
+// a double-buffered LDS tile; while staging them the loader threads also sum
+// each row over every scale group (v_dot2 with (1, 1)), and that row sum times
+// -(128 + z) starts each group's MFMA chain, which removes the +128 bias of the
+// dequantised codes without a separate correction chain.  Workgroups are
+// numbered so that all row tiles of one weight tile land on the same XCD (one
+// L2) and read the weights from HBM once.
+template <int MT>
+struct PTile {
+  int row0, rows, e, bits;
+};
+
+template <int FMT, int EPI, int GPB, int MT>
+__global__ __launch_bounds__(256, 2) void qgemm_p_kernel(KArgs p, int n_nblk, int n_mt) {
+  constexpr int RT = MT / 32;          // 16-row MFMA tiles per wavefront (MT/2 rows)
+  constexpr int SPG = 4 / GPB;         // MFMA steps per scale group
+  constexpr int TPR = 256 / MT;        // loader threads per row
+  constexpr int NCH = 16 / TPR;        // 16-byte chunks per loader thread per K block
+  __shared__ u32x4 lds_a[2][MT / 16][4][64];
+  __shared__ __attribute__((aligned(16))) float lds_r[2][GPB][MT];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = uniform(tid >> 6), wm = wv & 1, wn = wv >> 1;
+
+  // XCD-aware numbering: workgroup L runs on XCD L % 8; give each XCD a
+  // contiguous range of (weight tile, row tile) items, weight-tile major.
+  const int total = gridDim.x;
+  const int per_xcd = total / 8;
+  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  const int nb = item / n_mt, mt = item % n_mt;
+  if (nb >= n_nblk) return;
+  int seg, m0;
+  if (!find_tile(p.seg_offsets, p.nseg, mt, seg, m0, MT)) return;
+  const int row0 = uniform(p.seg_offsets[seg] + m0);
+  const int rows = uniform(min(MT, p.seg_offsets[seg + 1] - row0));
+  const int e = uniform(seg / p.S);
+  const int bits = uniform(4 - (seg % p.S));
+  const int KB = p.K / 128, NT = p.N / 16;
+
+  // this wavefront's 4 channel tiles: SwiGLU = 2 gate + the 2 matching up tiles
+  int ct[4];
+  bool cv[4];
+  int hch0 = 0;
+  if (EPI == 1) {
+    hch0 = nb * 64 + 32 * wn;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      ct[u] = hch0 / 16 + u;
+      ct[2 + u] = NT / 2 + hch0 / 16 + u;
+      cv[u] = cv[2 + u] = hch0 + 16 * u < p.N / 2;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ct[u] = nb * 8 + 4 * wn + u;
+      cv[u] = ct[u] < NT;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (!cv[u]) ct[u] = 0;  // never stored; keeps the loads in bounds
+
+  // activation loader: thread -> row r, chunks [part*NCH, part*NCH + NCH) of each K block
+  const int lr = tid / TPR, part = tid % TPR;
+  const rsrc_t ar = make_rsrc(p.A, p.A_bytes);
+  const uint32_t aoff = (uint32_t)((src_row(p, Ctx{row0, rows, e, bits}, lr) * p.K + 8 * part * NCH) * 2);
+
+  constexpr uint32_t CB = FMT == 1 ? 1024 : 512;
+  rsrc_t br[4], r3[4], r4[4], sr[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const size_t tile = (size_t)e * NT + ct[u];
+    br[u] = make_rsrc(p.codes + tile * KB * CB, KB * CB);
+    r3[u] = make_rsrc(FMT == 2 ? p.p3 + tile * KB * 256 : nullptr, FMT == 2 ? KB * 256 : 0);
+    r4[u] = make_rsrc(FMT == 2 ? p.p4 + tile * KB * 256 : nullptr, FMT == 2 ? KB * 256 : 0);
+    sr[u] = make_rsrc(p.scales + (tile * 16) * (size_t)(KB * GPB), 16 * KB * GPB * 2);
+  }
+  const uint32_t soff = (uint32_t)((lane & 15) * KB * GPB * 2);
+  const float negz = -(128.0f + (float)p.z);
+
+  f32x4 acc[RT][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[rt][u] = f32x4{};
+
+  u32x4 ra[NCH];
+  BRegs rb[2][2];       // [ring][tile pair]: tiles 2q, 2q+1 in rb[.][q]
+  uint16_t rs[2][4][GPB];
+
+  auto issue_a = [&](int kb) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) ra[c] = buf_x4(ar, aoff + 16 * c, kb * 256);
+  };
+  auto stage_a = [&](int buf) {
+    float part_sum[GPB];
+#pragma unroll
+    for (int g = 0; g < GPB; ++g) part_sum[g] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = part * NCH + c;        // 16-byte chunk of the 128-wide K block
+      const int t = ch / 4, g4 = ch % 4;
+      lds_a[buf][lr / 16][t][(lr % 16) + 16 * g4] = ra[c];
+      const int grp = (8 * ch) / (128 / GPB);
+      float sacc = part_sum[grp];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) sacc = add_bf16_pair(ra[c][h], sacc);
+      part_sum[grp] = sacc;
+    }
+#pragma unroll
+    for (int g = 0; g < GPB; ++g) {
+      float v = part_sum[g];
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) v += __shfl_xor(v, o, 64);
+      if (part == 0) lds_r[buf][g][lr] = v;
+    }
+  };
+  auto issue_b = [&](int slot, int kb) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int u = 2 * q + h;
+        if (FMT == 1) {
+          rb[slot][q].c[h] = buf_x4(br[u], 16 * lane, kb * CB);
+        } else {
+          rb[slot][q].q[h] = buf_x2(br[u], 8 * lane, kb * CB);
+          rb[slot][q].d3[h] = bits >= 3 ? buf_x1(r3[u], 4 * lane, kb * 256) : 0u;
+          rb[slot][q].d4[h] = bits == 4 ? buf_x1(r4[u], 4 * lane, kb * 256) : 0u;
+        }
+#pragma unroll
+        for (int g = 0; g < GPB; ++g) rs[slot][u][g] = buf_u16(sr[u], soff, (kb * GPB + g) * 2);
+      }
+  };
+  auto compute = [&](int slot, int buf) {
+#pragma unroll
+    for (int g = 0; g < GPB; ++g) {
+      // bias correction of this group for each of this wavefront's row tiles
+      f32x4 cinit[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const f32x4 rv = *reinterpret_cast<const f32x4*>(&lds_r[buf][g][wm * (MT / 2) + 16 * rt + 4 * (lane >> 4)]);
+        cinit[rt] = rv * negz;
+      }
+      f32x4 tmp[RT][4];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) tmp[rt][u] = cinit[rt];
+#pragma unroll
+      for (int t = g * SPG; t < (g + 1) * SPG; ++t) {
+        bf16x8 bv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const BRegs& b = rb[slot][u >> 1];
+          bv[u] = (FMT == 1) ? deq_u4(b.c[u & 1], t) : deq_mwq(b.q[u & 1], b.d3[u & 1], b.d4[u & 1], t, bits);
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const bf16x8 av = as_bf16x8(lds_a[buf][wm * (RT) + rt][t][lane]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) tmp[rt][u] = mfma16(av, bv[u], tmp[rt][u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float sv = f16_to_f32(rs[slot][u][g]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[rt][u][r] = __builtin_fmaf(sv, tmp[rt][u][r], acc[rt][u][r]);
+      }
+    }
+  };
+
+  // prologue: activations of block 0 staged, weights of blocks 0 and 1 in flight
+  issue_a(0);
+  issue_b(0, 0);
+  if (1 < KB) issue_b(1, 1);
+  stage_a(0);
+  __syncthreads();
+  for (int kb = 0; kb < KB; kb += 2) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = kb + j;
+      if (i < KB) {
+        if (i + 1 < KB) issue_a(i + 1);
+        compute(j, j);
+        if (i + 2 < KB) issue_b(j, i + 2);
+        if (i + 1 < KB) stage_a(1 - j);
+        __syncthreads();
+      }
+    }
+  }
+
+  // epilogue
+  const int col = lane & 15;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = wm * (MT / 2) + 16 * rt + 4 * (lane >> 4) + r;
+      if (row >= rows) continue;
+      if (EPI == 1) {
+        uint16_t* orow = static_cast<uint16_t*>(p.out) + (size_t)(row0 + row) * p.n_out;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          if (!cv[u]) continue;
+          const float g = acc[rt][u][r], up = acc[rt][2 + u][r];
+          orow[hch0 + 16 * u + col] = f32_to_bf16(g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * up);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (!cv[u]) continue;
+          const size_t o = (size_t)(row0 + row) * p.n_out + ct[u] * 16 + col;
+          if (EPI == 2) static_cast<float*>(p.out)[o] = acc[rt][u][r];
+          else static_cast<uint16_t*>(p.out)[o] = f32_to_bf16(acc[rt][u][r]);
+        }
+      }
+    }
+  }
+}
+
 template <int FMT, int EPI>
 void launch_q(const KArgs& ka, dim3 grid, hipStream_t s) {
   switch (ka.G) {
@@ -457,11 +690,54 @@ void launch_q(const KArgs& ka, dim3 grid, hipStream_t s) {
   }
 }
 
+template <int FMT, int EPI, int MT>
+void launch_p(const KArgs& ka, int n_nblk, int n_mt, hipStream_t s) {
+  const int items = n_nblk * n_mt;
+  const dim3 grid((unsigned)(((items + 7) / 8) * 8));  // multiple of 8: one equal share per XCD
+  switch (ka.G) {
+    case 128: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 1, MT>), grid, dim3(256), 0, s, ka, n_nblk, n_mt); break;
+    case 64: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 2, MT>), grid, dim3(256), 0, s, ka, n_nblk, n_mt); break;
+    default: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 4, MT>), grid, dim3(256), 0, s, ka, n_nblk, n_mt); break;
+  }
+}
+
+// path: 0 = small-row-tile kernel, 64 / 128 = large-row-tile kernel with that tile height
 template <int EPI>
-void launch_epi(const KArgs& ka, int fmt, dim3 grid, hipStream_t s) {
+void launch_epi(const KArgs& ka, int fmt, int path, int M_total, hipStream_t s) {
+  if (fmt != 3 && path != 0) {
+    const int n_nblk = EPI == 1 ? (ka.N / 2 + 63) / 64 : (ka.N + 127) / 128;
+    const int n_mt = (M_total + path - 1) / path + ka.nseg;
+    if (fmt == 1) {
+      if (path == 64) launch_p<1, EPI, 64>(ka, n_nblk, n_mt, s);
+      else launch_p<1, EPI, 128>(ka, n_nblk, n_mt, s);
+    } else {
+      if (path == 64) launch_p<2, EPI, 64>(ka, n_nblk, n_mt, s);
+      else launch_p<2, EPI, 128>(ka, n_nblk, n_mt, s);
+    }
+    return;
+  }
+  // a workgroup covers 64 SwiGLU channels or 128 plain channels
+  const int gx = EPI == 1 ? (ka.N / 2 + 63) / 64 : (ka.N + 127) / 128;
+  const int gy = (M_total + kRows - 1) / kRows + ka.nseg;
+  const dim3 grid(gx, gy);
   if (fmt == 1) launch_q<1, EPI>(ka, grid, s);
   else if (fmt == 2) launch_q<2, EPI>(ka, grid, s);
   else hipLaunchKernelGGL((qgemm_delta_kernel<EPI>), grid, dim3(kThreads), 0, s, ka);
+}
+
+// Row-tile height from the mean rows per segment (the host never sees the
+// device counts): few rows per segment -> 32-row tiles that skip empty MFMA
+// row tiles; many -> 64 / 128-row tiles that reuse each dequantised weight
+// fragment for more rows.  MOE_QGEMM_PATH=small|64|128 forces a path.
+int pick_path(int M_total, int nseg, int G) {
+  if (const char* f = getenv("MOE_QGEMM_PATH")) {
+    if (!strcmp(f, "small")) return 0;
+    if (!strcmp(f, "64")) return 64;
+    if (!strcmp(f, "128")) return 128;
+  }
+  if (G < 64) return 0;  // four scale groups per K block do not fit the large tile's registers
+  const double avg = (double)M_total / (double)(nseg > 0 ? nseg : 1);
+  return avg < 24.0 ? 0 : 64;
 }
 }  // namespace
 
@@ -493,13 +769,11 @@ hipError_t launch_qgemm(const QGemmArgs& a, hipStream_t s) {
   ka.n_sal = w.n_sal;
   const bool swiglu = a.epilogue == 1;
   ka.n_out = swiglu ? w.N / 2 : w.N;
-  // a workgroup covers 64 SwiGLU channels or 128 plain channels
-  const int gx = swiglu ? (w.N / 2 + 63) / 64 : (w.N + 127) / 128;
-  const int gy = (a.M_total + kRows - 1) / kRows + a.nseg;
-  dim3 grid(gx, gy);
-  if (a.epilogue == 1) launch_epi<1>(ka, w.fmt, grid, s);
-  else if (a.epilogue == 2) launch_epi<2>(ka, w.fmt, grid, s);
-  else launch_epi<0>(ka, w.fmt, grid, s);
+  (void)swiglu;
+  const int path = pick_path(a.M_total, a.nseg, w.G);
+  if (a.epilogue == 1) launch_epi<1>(ka, w.fmt, path, a.M_total, s);
+  else if (a.epilogue == 2) launch_epi<2>(ka, w.fmt, path, a.M_total, s);
+  else launch_epi<0>(ka, w.fmt, path, a.M_total, s);
   return hipGetLastError();
 }
 
