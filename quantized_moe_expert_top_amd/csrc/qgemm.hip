@@ -261,32 +261,51 @@ __global__ __launch_bounds__(kThreads) void qgemm_q_kernel(KArgs p) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) acc[rt][u] = f32x4{};
 
-  // Register rings: weights (and scales) run PFB K blocks ahead in a ring of
-  // RB = PFB + 1 slots, activations PFA = 3 ahead in a ring of RA = 4 slots;
-  // the loop is unrolled by 8 so every ring index is a compile-time constant.
+  // Register rings: weights run PFB K blocks ahead in a ring of RB = PFB + 1
+  // slots, activations PFA = 3 ahead in a ring of RA = 4 slots; the loop is
+  // unrolled by 8 so every ring index is a compile-time constant.  Activation
+  // loads are issued before the weight loads of the same iteration: the memory
+  // counter retires loads in issue order, so waiting for the activations of
+  // block i+1 then never waits for weights beyond block i.
+  // Scales travel in chunks of 4 consecutive groups of a channel (one 8-byte
+  // load per tile per CPK = 4 / GPB K blocks) in a ring of RS chunk slots; when
+  // K / G is not a multiple of 4 the chunk is filled one group at a time.
   constexpr int PFB = 3, RB = PFB + 1, RA = 4;
-  static_assert(8 % RB == 0 && 8 % RA == 0, "ring sizes must divide the unroll factor");
+  constexpr int CPK = 4 / GPB, RS = CPK == 4 ? 2 : 4;
+  static_assert(8 % RB == 0 && 8 % RA == 0 && (8 / CPK) % RS == 0, "ring sizes must divide the unroll factor");
+  const bool sc_wide = ((KB * GPB) & 3) == 0;
   u32x4 ra[RA][2];
   BRegs rb[RB];
-  uint16_t rs[RB][2][GPB];
+  u32x2 rsc[RS][2];
 
 #define QG_ISSUE_A(SLOT, KBI)                                                                        \
   {                                                                                                  \
     ra[SLOT][0] = buf_x4(ar, aoff[0], (KBI) * 256);                                                  \
     if (two) ra[SLOT][1] = buf_x4(ar, aoff[1], (KBI) * 256);                                         \
   }
-#define QG_ISSUE_B(SLOT, KBI)                                                                        \
+  // JJ: K block relative to kb (a multiple of 8), a compile-time constant
+#define QG_ISSUE_B(SLOT, JJ)                                                                         \
   if (wvalid) {                                                                                      \
+    const int kbi = kb + (JJ);                                                                       \
     _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                  \
       if (FMT == 1) {                                                                                \
-        rb[SLOT].c[u] = buf_x4(br[u], 16 * lane, (KBI) * CB);                                        \
+        rb[SLOT].c[u] = buf_x4(br[u], 16 * lane, kbi * CB);                                          \
       } else {                                                                                       \
-        rb[SLOT].q[u] = buf_x2(br[u], 8 * lane, (KBI) * CB);                                         \
-        rb[SLOT].d3[u] = c.bits >= 3 ? buf_x1(r3[u], 4 * lane, (KBI) * 256) : 0u;                    \
-        rb[SLOT].d4[u] = c.bits == 4 ? buf_x1(r4[u], 4 * lane, (KBI) * 256) : 0u;                    \
+        rb[SLOT].q[u] = buf_x2(br[u], 8 * lane, kbi * CB);                                           \
+        rb[SLOT].d3[u] = c.bits >= 3 ? buf_x1(r3[u], 4 * lane, kbi * 256) : 0u;                      \
+        rb[SLOT].d4[u] = c.bits == 4 ? buf_x1(r4[u], 4 * lane, kbi * 256) : 0u;                      \
       }                                                                                              \
-      _Pragma("unroll") for (int g = 0; g < GPB; ++g)                                                \
-        rs[SLOT][u][g] = buf_u16(sr[u], soff, ((KBI) * GPB + g) * 2);                                \
+      if (sc_wide) {                                                                                 \
+        if (((JJ) * GPB) % 4 == 0) rsc[((JJ) * GPB / 4) % RS][u] = buf_x2(sr[u], soff, kbi * GPB * 2); \
+      } else {                                                                                       \
+        _Pragma("unroll") for (int g = 0; g < GPB; ++g) {                                            \
+          const int lg = (JJ) * GPB + g;                                                             \
+          const uint32_t v = buf_u16(sr[u], soff, (kbi * GPB + g) * 2);                              \
+          const uint32_t wd = rsc[(lg / 4) % RS][u][(lg % 4) >> 1];                                  \
+          rsc[(lg / 4) % RS][u][(lg % 4) >> 1] =                                                     \
+              (lg & 1) ? ((wd & 0xFFFFu) | (v << 16)) : ((wd & 0xFFFF0000u) | v);                    \
+        }                                                                                            \
+      }                                                                                              \
     }                                                                                                \
   }
 #define QG_STAGE(SLOT, KBI)                                                                          \
@@ -308,15 +327,16 @@ __global__ __launch_bounds__(kThreads) void qgemm_q_kernel(KArgs p) {
                                      : deq_mwq(rb[(J) % RB].q[u], rb[(J) % RB].d3[u], rb[(J) % RB].d4[u], t, c.bits); \
         tm = mfma16(as_bf16x8(lds_a[SLOT3][RT][t][lane]), bv, tm);                                   \
       }                                                                                              \
-      const float sv = f16_to_f32(rs[(J) % RB][u][T0 / SPG]);                                               \
+      const int lg = (J) * GPB + (T0) / SPG;                                                         \
+      const float sv = f16_to_f32((uint16_t)(rsc[(lg / 4) % RS][u][(lg % 4) >> 1] >> (16 * (lg & 1)))); \
       _Pragma("unroll") for (int r = 0; r < 4; ++r) acc[RT][u][r] = __builtin_fmaf(sv, tm[r], acc[RT][u][r]); \
     }                                                                                                \
   }
 #define QG_STEP(J)                                                                                   \
   if (kb + J < KB) {                                                                                 \
     const int i = kb + J;                                                                            \
-    if (i + PFB < KB) QG_ISSUE_B(((J) + PFB) % RB, i + PFB);                                           \
     if (i + 3 < KB) QG_ISSUE_A((J + 3) % RA, i + 3);                                                 \
+    if (i + PFB < KB) QG_ISSUE_B(((J) + PFB) % RB, (J) + PFB);                                       \
     if (i + 1 < KB) QG_STAGE((J + 1) % RA, i + 1);                                                   \
     __syncthreads();                                                                                 \
     if (wvalid) {                                                                                    \
@@ -328,15 +348,16 @@ __global__ __launch_bounds__(kThreads) void qgemm_q_kernel(KArgs p) {
     }                                                                                                \
   }
 
-  // prologue: weights of K blocks 0..PFB-1 and activations of 0..2 in flight, block 0 staged
-#pragma unroll
-  for (int j = 0; j < PFB; ++j)
-    if (j < KB) QG_ISSUE_B(j % RB, j);
+  // prologue: activations of K blocks 0..2, then weights of 0..PFB-1 in flight; block 0 staged
+  int kb = 0;
 #pragma unroll
   for (int j = 0; j < 3; ++j)
     if (j < KB) QG_ISSUE_A(j, j);
+#pragma unroll
+  for (int j = 0; j < PFB; ++j)
+    if (j < KB) QG_ISSUE_B(j % RB, j);
   QG_STAGE(0, 0);
-  for (int kb = 0; kb < KB; kb += 8) {
+  for (; kb < KB; kb += 8) {
     QG_STEP(0)
     QG_STEP(1)
     QG_STEP(2)
