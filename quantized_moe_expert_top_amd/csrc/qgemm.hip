@@ -28,6 +28,7 @@
 //                                K chunk with bf16 values; the shared base is a
 //                                plain bf16 MFMA on the same A operand
 #include <stdlib.h>
+#include <type_traits>
 #include <string.h>
 
 #include "common.h"
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_q_kernel(KArgs p) {
 #define QG_ISSUE_A(SLOT, KBI)                                                                        \
   {                                                                                                  \
     ra[SLOT][0] = buf_x4(ar, aoff[0], (KBI) * 256);                                                  \
-    if (two) ra[SLOT][1] = buf_x4(ar, aoff[1], (KBI) * 256);                                         \
+    if (TWO) ra[SLOT][1] = buf_x4(ar, aoff[1], (KBI) * 256);                                         \
   }
   // JJ: K block relative to kb (a multiple of 8), a compile-time constant
 #define QG_ISSUE_B(SLOT, JJ)                                                                         \
@@ -311,25 +312,32 @@ __global__ __launch_bounds__(kThreads) void qgemm_q_kernel(KArgs p) {
 #define QG_STAGE(SLOT, KBI)                                                                          \
   {                                                                                                  \
     lds_a[(KBI) % 3][0][wv][lane] = ra[SLOT][0];                                                     \
-    if (two) lds_a[(KBI) % 3][1][wv][lane] = ra[SLOT][1];                                            \
+    if (TWO) lds_a[(KBI) % 3][1][wv][lane] = ra[SLOT][1];                                            \
   }
-  // one scale group (SPG steps starting at T0) for row tile RT: the correction
-  // chain first, then each tile's chain starts from it; acc += scale * chain
-#define QG_GROUP(J, RT, T0, SLOT3)                                                                   \
+  // one scale group (SPG steps starting at T0) for both row tiles: the
+  // correction chains first, then each tile's chain starts from them (each
+  // weight fragment is dequantised once and used for both row tiles);
+  // acc += scale * chain
+#define QG_GROUP(J, T0, SLOT3)                                                                       \
   {                                                                                                  \
-    f32x4 cr = f32x4{};                                                                              \
-    _Pragma("unroll") for (int t = T0; t < T0 + SPG; ++t)                                            \
-      cr = mfma16(as_bf16x8(lds_a[SLOT3][RT][t][lane]), neg, cr);                                    \
+    f32x4 cr0 = f32x4{}, cr1 = f32x4{};                                                              \
+    _Pragma("unroll") for (int t = T0; t < T0 + SPG; ++t) {                                          \
+      cr0 = mfma16(as_bf16x8(lds_a[SLOT3][0][t][lane]), neg, cr0);                                   \
+      if (TWO) cr1 = mfma16(as_bf16x8(lds_a[SLOT3][1][t][lane]), neg, cr1);                          \
+    }                                                                                                \
     _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                  \
-      f32x4 tm = cr;                                                                                 \
+      f32x4 tm0 = cr0, tm1 = cr1;                                                                    \
       _Pragma("unroll") for (int t = T0; t < T0 + SPG; ++t) {                                        \
         const bf16x8 bv = (FMT == 1) ? deq_u4(rb[(J) % RB].c[u], t)                                  \
                                      : deq_mwq(rb[(J) % RB].q[u], rb[(J) % RB].d3[u], rb[(J) % RB].d4[u], t, c.bits); \
-        tm = mfma16(as_bf16x8(lds_a[SLOT3][RT][t][lane]), bv, tm);                                   \
+        tm0 = mfma16(as_bf16x8(lds_a[SLOT3][0][t][lane]), bv, tm0);                                  \
+        if (TWO) tm1 = mfma16(as_bf16x8(lds_a[SLOT3][1][t][lane]), bv, tm1);                         \
       }                                                                                              \
       const int lg = (J) * GPB + (T0) / SPG;                                                         \
       const float sv = f16_to_f32((uint16_t)(rsc[(lg / 4) % RS][u][(lg % 4) >> 1] >> (16 * (lg & 1)))); \
-      _Pragma("unroll") for (int r = 0; r < 4; ++r) acc[RT][u][r] = __builtin_fmaf(sv, tm[r], acc[RT][u][r]); \
+      _Pragma("unroll") for (int r = 0; r < 4; ++r) acc[0][u][r] = __builtin_fmaf(sv, tm0[r], acc[0][u][r]); \
+      if (TWO)                                                                                       \
+        _Pragma("unroll") for (int r = 0; r < 4; ++r) acc[1][u][r] = __builtin_fmaf(sv, tm1[r], acc[1][u][r]); \
     }                                                                                                \
   }
 #define QG_STEP(J)                                                                                   \
@@ -341,13 +349,13 @@ __global__ __launch_bounds__(kThreads) void qgemm_q_kernel(KArgs p) {
     __syncthreads();                                                                                 \
     if (wvalid) {                                                                                    \
       const int sl = i % 3;                                                                          \
-      _Pragma("unroll") for (int t0 = 0; t0 < 4; t0 += SPG) {                                        \
-        QG_GROUP(J, 0, t0, sl);                                                                      \
-        if (two) QG_GROUP(J, 1, t0, sl);                                                             \
-      }                                                                                              \
+      _Pragma("unroll") for (int t0 = 0; t0 < 4; t0 += SPG) QG_GROUP(J, t0, sl);                     \
     }                                                                                                \
   }
 
+  // The K loop, instantiated for one or two 16-row MFMA tiles (uniform branch).
+  auto k_loop = [&](auto two_tag) {
+  constexpr bool TWO = decltype(two_tag)::value;
   // prologue: activations of K blocks 0..2, then weights of 0..PFB-1 in flight; block 0 staged
   int kb = 0;
 #pragma unroll
@@ -367,6 +375,9 @@ __global__ __launch_bounds__(kThreads) void qgemm_q_kernel(KArgs p) {
     QG_STEP(6)
     QG_STEP(7)
   }
+  };
+  if (two) k_loop(std::true_type{});
+  else k_loop(std::false_type{});
 #undef QG_ISSUE_A
 #undef QG_ISSUE_B
 #undef QG_STAGE
