@@ -101,6 +101,7 @@ __device__ __forceinline__ bf16x8 deq_u4(const u32x4& cd, int t) {
   r[1] = and_or(d >> 4, m, o);
   r[2] = and_or(d >> 8, m, o);
   r[3] = and_or(d >> 12, m, o);
+  mfma_operand_fence(r);
   return as_bf16x8(r);
 }
 
@@ -116,6 +117,7 @@ __device__ __forceinline__ bf16x8 deq_mwq(const u32x2& q2, uint32_t d3, uint32_t
     if (b == 4) v = and_or(shr(d4, P3), 0x00010001u, v);
     r[p] = v;
   }
+  mfma_operand_fence(r);
   return as_bf16x8(r);
 }
 
@@ -127,6 +129,7 @@ __device__ __forceinline__ bf16x8 deq_u2(const u32x2& c, int t) {
     const int P = 4 * (t & 1) + p;
     r[p] = and_or(shr(C, 2 * P), 0x00030003u, 0x43004300u);
   }
+  mfma_operand_fence(r);
   return as_bf16x8(r);
 }
 
@@ -152,15 +155,16 @@ __device__ __forceinline__ size_t src_row(const KArgs& p, const Ctx& c, int r) {
 
 // This wavefront's two 16-channel tiles; false if the wavefront has no tile.
 template <bool SWIGLU>
-__device__ __forceinline__ bool wave_tiles(const KArgs& p, int wv, int& ct0, int& ct1, bool& v1, int& hch) {
+__device__ __forceinline__ bool wave_tiles(const KArgs& p, int wv, int& ct0, int& ct1, bool& v1, int& hch,
+                                           int cg = blockIdx.x) {
   if (SWIGLU) {
-    hch = blockIdx.x * 64 + 16 * wv;  // first h channel
+    hch = cg * 64 + 16 * wv;  // first h channel
     ct0 = hch / 16;
     ct1 = p.N / 32 + hch / 16;
     v1 = true;
     return hch < p.N / 2;
   }
-  const int ch = blockIdx.x * 128 + 32 * wv;
+  const int ch = cg * 128 + 32 * wv;
   hch = ch;
   ct0 = ch / 16;
   v1 = ch + 16 < p.N;
@@ -384,6 +388,183 @@ __global__ __launch_bounds__(kThreads) void qgemm_q_kernel(KArgs p) {
 #undef QG_GROUP
 #undef QG_STEP
   if (wvalid) store_tiles<EPI>(p, c, acc, ct0, ct1, v1, hch, two);
+}
+
+// ------------------------------------------------------------ decode, deep
+// One workgroup per (16-row tile of one segment, channel group of 64 SwiGLU /
+// 128 plain channels); each wavefront owns two 16-channel tiles and streams
+// all of K.  Weights and activations both run PF = 7 K blocks ahead in
+// register rings (the memory counter retires loads in issue order, so the
+// activations, issued first, never make a wavefront wait for weights it does
+// not need yet).  Each step's activation fragment is read from LDS once and
+// feeds, per tile, the bias-correction MFMA with -(128 + z) and the MFMA on
+// the dequantised codes, so no fragment stays live across steps.  Workgroups
+// are numbered so that the row tiles of one segment and channel group run on
+// one XCD, back to back: a segment of more than 16 rows reads its weights
+// from HBM once and from that XCD's L2 after.
+template <int FMT, int EPI, int GPB>
+__global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, int n_rt) {
+  constexpr int SPG = 4 / GPB;                 // MFMA steps per scale group
+  constexpr int PF = 7, R = 8;                 // prefetch distance, ring size
+  // Scales: chunks of 4 groups of a channel (one 8-byte load per tile per CPK
+  // K blocks), loaded with the weights, in a ring of RS chunk slots that
+  // covers every chunk alive across the PF + 1 blocks in flight.  The loop
+  // is unrolled by 16 so that every ring index is a compile-time constant.
+  constexpr int U = 16;
+  constexpr int CPK = 4 / GPB, RS = CPK == 4 ? 4 : 8;
+  static_assert(U % R == 0 && (U / CPK) % RS == 0, "rings must divide the unroll factor");
+  static_assert(RS >= (PF + CPK) / CPK + (CPK > 1 ? 1 : 0), "scale ring too short for the prefetch distance");
+  __shared__ u32x4 lds_a[3][4][64];            // [slot][step][lane], 12 KB
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = uniform(tid >> 6);
+
+  const int per_xcd = gridDim.x / 8;
+  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  const int cg = item / n_rt, rtile = item % n_rt;
+  if (cg >= n_cg) return;
+  int seg, m0;
+  if (!find_tile(p.seg_offsets, p.nseg, rtile, seg, m0, 16)) return;
+  Ctx c;
+  c.row0 = uniform(p.seg_offsets[seg] + m0);
+  c.rows = uniform(min(16, p.seg_offsets[seg + 1] - c.row0));
+  c.e = uniform(seg / p.S);
+  c.bits = uniform(4 - (seg % p.S));
+  int ct0, ct1, hch;
+  bool v1;
+  const bool wvalid = wave_tiles<EPI == 1>(p, wv, ct0, ct1, v1, hch, cg);
+  const int KB = p.K / 128, NT = p.N / 16;
+
+  // activations: this thread carries (step wv, lane) of each K block
+  const rsrc_t ar = make_rsrc(p.A, p.A_bytes);
+  const uint32_t aoff = (uint32_t)((src_row(p, c, lane & 15) * p.K + 32 * wv + 8 * (lane >> 4)) * 2);
+  constexpr uint32_t CB = FMT == 1 ? 1024 : 512;
+  rsrc_t br[2], r3[2], r4[2], sr[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const size_t tile = (size_t)c.e * NT + (u ? ct1 : ct0);
+    br[u] = make_rsrc(p.codes + tile * KB * CB, KB * CB);
+    r3[u] = make_rsrc(FMT == 2 ? p.p3 + tile * KB * 256 : nullptr, FMT == 2 ? KB * 256 : 0);
+    r4[u] = make_rsrc(FMT == 2 ? p.p4 + tile * KB * 256 : nullptr, FMT == 2 ? KB * 256 : 0);
+    sr[u] = make_rsrc(p.scales + (tile * 16) * (size_t)(KB * GPB), 16 * KB * GPB * 2);
+  }
+  const uint32_t soff = (uint32_t)((lane & 15) * KB * GPB * 2);
+  const bool sc_wide = ((KB * GPB) & 3) == 0;
+  const uint32_t negc = (0xC300u | (uint32_t)p.z) * 0x00010001u;
+  const bf16x8 neg = as_bf16x8(u32x4{negc, negc, negc, negc});
+
+  f32x4 acc[2] = {f32x4{}, f32x4{}};
+  u32x4 ra[R];
+  BRegs rb[R];
+  u32x2 rsc[RS][2];
+
+#define QD_ISSUE_A(SLOT, KBI) ra[SLOT] = buf_x4(ar, aoff, (KBI) * 256);
+  // JJ: K block relative to kb (a multiple of U), a compile-time constant
+#define QD_ISSUE_B(SLOT, JJ)                                                                         \
+  if (wvalid) {                                                                                      \
+    const int kbi = kb + (JJ);                                                                       \
+    _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                  \
+      if (FMT == 1) {                                                                                \
+        rb[SLOT].c[u] = buf_x4(br[u], 16 * lane, kbi * CB);                                          \
+      } else {                                                                                       \
+        rb[SLOT].q[u] = buf_x2(br[u], 8 * lane, kbi * CB);                                           \
+        rb[SLOT].d3[u] = c.bits >= 3 ? buf_x1(r3[u], 4 * lane, kbi * 256) : 0u;                      \
+        rb[SLOT].d4[u] = c.bits == 4 ? buf_x1(r4[u], 4 * lane, kbi * 256) : 0u;                      \
+      }                                                                                              \
+      if (sc_wide) {                                                                                 \
+        if (((JJ) * GPB) % 4 == 0) rsc[((JJ) * GPB / 4) % RS][u] = buf_x2(sr[u], soff, kbi * GPB * 2); \
+      } else {                                                                                       \
+        _Pragma("unroll") for (int g = 0; g < GPB; ++g) {                                            \
+          const int lg = (JJ) * GPB + g;                                                             \
+          const uint32_t v = buf_u16(sr[u], soff, (kbi * GPB + g) * 2);                              \
+          const uint32_t wd = rsc[(lg / 4) % RS][u][(lg % 4) >> 1];                                  \
+          rsc[(lg / 4) % RS][u][(lg % 4) >> 1] =                                                     \
+              (lg & 1) ? ((wd & 0xFFFFu) | (v << 16)) : ((wd & 0xFFFF0000u) | v);                    \
+        }                                                                                            \
+      }                                                                                              \
+    }                                                                                                \
+  }
+#define QD_STEP(J)                                                                                   \
+  if (kb + J < KB) {                                                                                 \
+    const int i = kb + J;                                                                            \
+    if (i + PF < KB) {                                                                               \
+      QD_ISSUE_A(((J) + PF) % R, i + PF);                                                            \
+      QD_ISSUE_B(((J) + PF) % R, (J) + PF);                                                          \
+    }                                                                                                \
+    if (i + 1 < KB) lds_a[(i + 1) % 3][wv][lane] = ra[((J) + 1) % R];                                 \
+    __syncthreads();                                                                                 \
+    if (wvalid) {                                                                                    \
+      const int sl = i % 3;                                                                          \
+      _Pragma("unroll") for (int t0 = 0; t0 < 4; t0 += SPG) {                                        \
+        f32x4 tm[2] = {f32x4{}, f32x4{}};                                                            \
+        _Pragma("unroll") for (int t = t0; t < t0 + SPG; ++t) {                                      \
+          const bf16x8 av = as_bf16x8(lds_a[sl][t][lane]);                                           \
+          _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                            \
+            const bf16x8 bv = (FMT == 1) ? deq_u4(rb[(J) % R].c[u], t)                               \
+                                         : deq_mwq(rb[(J) % R].q[u], rb[(J) % R].d3[u], rb[(J) % R].d4[u], t, c.bits); \
+            tm[u] = mfma16(av, neg, tm[u]);                                                          \
+            tm[u] = mfma16(av, bv, tm[u]);                                                           \
+          }                                                                                          \
+        }                                                                                            \
+        const int lg = (J) * GPB + t0 / SPG;                                                         \
+        _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                              \
+          const float sv = f16_to_f32((uint16_t)(rsc[(lg / 4) % RS][u][(lg % 4) >> 1] >> (16 * (lg & 1)))); \
+          _Pragma("unroll") for (int r = 0; r < 4; ++r) acc[u][r] = __builtin_fmaf(sv, tm[u][r], acc[u][r]); \
+        }                                                                                            \
+      }                                                                                              \
+    }                                                                                                \
+  }
+
+  // prologue: activations and weights of K blocks 0..PF-1 in flight, block 0 staged
+  int kb = 0;
+#pragma unroll
+  for (int j = 0; j < PF; ++j)
+    if (j < KB) {
+      QD_ISSUE_A(j, j);
+      QD_ISSUE_B(j, j);
+    }
+  lds_a[0][wv][lane] = ra[0];
+  for (; kb < KB; kb += U) {
+    QD_STEP(0)
+    QD_STEP(1)
+    QD_STEP(2)
+    QD_STEP(3)
+    QD_STEP(4)
+    QD_STEP(5)
+    QD_STEP(6)
+    QD_STEP(7)
+    QD_STEP(8)
+    QD_STEP(9)
+    QD_STEP(10)
+    QD_STEP(11)
+    QD_STEP(12)
+    QD_STEP(13)
+    QD_STEP(14)
+    QD_STEP(15)
+  }
+#undef QD_ISSUE_A
+#undef QD_ISSUE_B
+#undef QD_STEP
+  if (!wvalid) return;
+  const int col = lane & 15;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * (lane >> 4) + r;
+    if (row >= c.rows) continue;
+    if (EPI == 2) {
+      float* orow = static_cast<float*>(p.out) + (size_t)(c.row0 + row) * p.n_out;
+      orow[ct0 * 16 + col] = acc[0][r];
+      if (v1) orow[ct1 * 16 + col] = acc[1][r];
+    } else {
+      uint16_t* orow = static_cast<uint16_t*>(p.out) + (size_t)(c.row0 + row) * p.n_out;
+      if (EPI == 1) {
+        const float g = acc[0][r];
+        orow[hch + col] = f32_to_bf16(g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * acc[1][r]);
+      } else {
+        orow[ct0 * 16 + col] = f32_to_bf16(acc[0][r]);
+        if (v1) orow[ct1 * 16 + col] = f32_to_bf16(acc[1][r]);
+      }
+    }
+  }
 }
 
 // -------------------------------------------------------------------- DELTA2
@@ -722,6 +903,17 @@ void launch_q(const KArgs& ka, dim3 grid, hipStream_t s) {
   }
 }
 
+template <int FMT, int EPI>
+void launch_d(const KArgs& ka, int n_cg, int n_rt, hipStream_t s) {
+  const int items = n_cg * n_rt;
+  const dim3 grid((unsigned)(((items + 7) / 8) * 8));  // multiple of 8: one equal share per XCD
+  switch (ka.G) {
+    case 128: hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 1>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt); break;
+    case 64: hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 2>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt); break;
+    default: hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 4>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt); break;
+  }
+}
+
 template <int FMT, int EPI, int MT>
 void launch_p(const KArgs& ka, int n_nblk, int n_mt, hipStream_t s) {
   const int items = n_nblk * n_mt;
@@ -736,7 +928,7 @@ void launch_p(const KArgs& ka, int n_nblk, int n_mt, hipStream_t s) {
 // path: 0 = small-row-tile kernel, 64 / 128 = large-row-tile kernel with that tile height
 template <int EPI>
 void launch_epi(const KArgs& ka, int fmt, int path, int M_total, hipStream_t s) {
-  if (fmt != 3 && path != 0) {
+  if (fmt != 3 && path > 0) {
     const int n_nblk = EPI == 1 ? (ka.N / 2 + 63) / 64 : (ka.N + 127) / 128;
     const int n_mt = (M_total + path - 1) / path + ka.nseg;
     if (fmt == 1) {
@@ -750,11 +942,20 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, hipStream_t s) 
   }
   // a workgroup covers 64 SwiGLU channels or 128 plain channels
   const int gx = EPI == 1 ? (ka.N / 2 + 63) / 64 : (ka.N + 127) / 128;
-  const int gy = (M_total + kRows - 1) / kRows + ka.nseg;
-  const dim3 grid(gx, gy);
-  if (fmt == 1) launch_q<1, EPI>(ka, grid, s);
-  else if (fmt == 2) launch_q<2, EPI>(ka, grid, s);
-  else hipLaunchKernelGGL((qgemm_delta_kernel<EPI>), grid, dim3(kThreads), 0, s, ka);
+  if (fmt == 3) {
+    const int gy = (M_total + kRows - 1) / kRows + ka.nseg;
+    hipLaunchKernelGGL((qgemm_delta_kernel<EPI>), dim3(gx, gy), dim3(kThreads), 0, s, ka);
+    return;
+  }
+  if (path == -32) {
+    const dim3 grid(gx, (M_total + kRows - 1) / kRows + ka.nseg);
+    if (fmt == 1) launch_q<1, EPI>(ka, grid, s);
+    else launch_q<2, EPI>(ka, grid, s);
+    return;
+  }
+  const int n_rt = (M_total + 15) / 16 + ka.nseg;
+  if (fmt == 1) launch_d<1, EPI>(ka, gx, n_rt, s);
+  else launch_d<2, EPI>(ka, gx, n_rt, s);
 }
 
 // Row-tile height from the mean rows per segment (the host never sees the
@@ -764,6 +965,7 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, hipStream_t s) 
 int pick_path(int M_total, int nseg, int G) {
   if (const char* f = getenv("MOE_QGEMM_PATH")) {
     if (!strcmp(f, "small")) return 0;
+    if (!strcmp(f, "small32")) return -32;
     if (!strcmp(f, "64")) return 64;
     if (!strcmp(f, "128")) return 128;
   }
