@@ -38,21 +38,6 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t v, float acc) {
                                          acc, false);
 }
 
-// (x & m) | o in one v_and_or_b32 (the compiler otherwise splits it into an
-// AND and an OR).  The hazard recognizer does not count a VALU write made
-// inside inline asm, so a register produced here must not reach an MFMA
-// operand without mfma_operand_fence().
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(o));
-  return r;
-}
-// Wait states between the last VALU write of `v` (from inline asm) and any
-// later read: an MFMA source operand needs two after a VALU write; three
-// are given.  The "+v" tie keeps the nop after the producers of v and before
-// its consumers.
-__device__ __forceinline__ void mfma_operand_fence(u32x4& v) { asm volatile("s_nop 2" : "+v"(v)); }
-
 // Raw buffer loads: wave-uniform resource + per-lane byte offset + uniform
 // byte offset.  Reads at or past `bytes` return zero instead of faulting.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;

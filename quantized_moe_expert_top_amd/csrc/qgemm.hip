@@ -1,17 +1,18 @@
 // Grouped low-bit GEMM over expert segments (grouped batched expert execution,
 // ExactMoE page; "dequantise -> 16-bit GEMM" pipeline equation, D2MoE page).
 //
-// Work split: one workgroup (4 wavefronts) per (tile of up to 32 rows of one
-// segment, channel group).  Each wavefront owns two 16-channel tiles (a gate
-// tile and the matching up tile for SwiGLU, else two neighbouring tiles) and
-// streams all of K for them with v_mfma_f32_16x16x32_bf16; a 32-row tile is
-// two 16-row MFMA tiles, the second skipped when the tile has <= 16 rows.  Row
-// tiles are assigned on the device from seg_offsets, so the host never reads
-// counts back.  The activation rows of a K block are staged once per
-// workgroup through a 3-slot LDS ring; the weight stream of every wavefront
-// runs 3 K blocks ahead in a 4-slot register ring.
+// Row tiles of a segment are located on the device from seg_offsets (the host
+// never reads counts back), and every kernel streams the tiled weight layout
+// (16 channels x 128 inputs per tile block, see repack.hip) with
+// v_mfma_f32_16x16x32_bf16.  Three kernels:
+//   qgemm_d_kernel  few rows per segment (decode): 16-row tiles, 4 wavefronts
+//                   x 2 channel tiles each, activations shared through LDS,
+//                   weights and activations prefetched in register rings.
+//   qgemm_p_kernel  many rows per segment (prefill): 64-row tiles, each
+//                   dequantised weight fragment reused for 32 rows.
+//   qgemm_delta_kernel  2-bit delta + salient channels + shared bf16 base.
 //
-// Dequantisation is exact and costs one shift + one and-or per pair of
+// Dequantisation is exact and costs under one VALU operation per pair of
 // weights: a code c is dropped into the low mantissa bits of the bf16 number
 // 128 (bits 0x4300), giving exactly 128 + c.  The MFMA accumulates
 // sum_k a_k * (128 + c_k) in fp32, a second MFMA chain with the constant
@@ -28,7 +29,6 @@
 //                                K chunk with bf16 values; the shared base is a
 //                                plain bf16 MFMA on the same A operand
 #include <stdlib.h>
-#include <type_traits>
 #include <string.h>
 
 #include "common.h"
@@ -92,19 +92,27 @@ __device__ __forceinline__ bool find_tile(const int32_t* seg_offsets, int nseg, 
 
 __device__ __forceinline__ uint32_t shr(uint32_t v, int sh) { return sh >= 0 ? (v >> sh) : (v << (-sh)); }
 
-// 8 bf16 values (128 + code) of MFMA step t (0..3) for one lane.
+// 8 bf16 values (128 + code) of MFMA step t (0..3) for one lane.  A code c
+// in the low mantissa bits of the bf16 number 128 (bits 0x4300) is exactly
+// 128 + c.  INT4: the dword of step t holds element i at bit 16*(i&1) +
+// 4*(i>>1); masking the low / high nibble of every byte leaves one code per
+// byte, and a byte permute with the constant 0x43 builds each pair
+// (elements 2p, 2p+1) as two bf16 values: 7 VALU operations per 8 weights.
 __device__ __forceinline__ bf16x8 deq_u4(const u32x4& cd, int t) {
   const uint32_t d = cd[t];
-  const uint32_t m = 0x000F000Fu, o = 0x43004300u;
+  const uint32_t lo = d & 0x0F0F0F0Fu;         // bytes: e0 e4 e1 e5
+  const uint32_t hi = (d >> 4) & 0x0F0F0F0Fu;  // bytes: e2 e6 e3 e7
+  const uint32_t K = 0x43434343u;
   u32x4 r;
-  r[0] = and_or(d, m, o);
-  r[1] = and_or(d >> 4, m, o);
-  r[2] = and_or(d >> 8, m, o);
-  r[3] = and_or(d >> 12, m, o);
-  mfma_operand_fence(r);
+  r[0] = __builtin_amdgcn_perm(K, lo, 0x04020400u);  // (e0, e1)
+  r[1] = __builtin_amdgcn_perm(K, hi, 0x04020400u);  // (e2, e3)
+  r[2] = __builtin_amdgcn_perm(K, lo, 0x04030401u);  // (e4, e5)
+  r[3] = __builtin_amdgcn_perm(K, hi, 0x04030401u);  // (e6, e7)
   return as_bf16x8(r);
 }
 
+// MWQ: c_b = 4*q2 + 2*d3*[b>=3] + d4*[b==4], placed straight into the low
+// mantissa bits (q2 at bits 2-3, d3 at bit 1, d4 at bit 0 of each half).
 __device__ __forceinline__ bf16x8 deq_mwq(const u32x2& q2, uint32_t d3, uint32_t d4, int t, int b) {
   const uint32_t Q = q2[t >> 1];
   u32x4 r;
@@ -112,12 +120,11 @@ __device__ __forceinline__ bf16x8 deq_mwq(const u32x2& q2, uint32_t d3, uint32_t
   for (int p = 0; p < 4; ++p) {
     const int P = 4 * (t & 1) + p;
     const int P3 = 4 * t + p;
-    uint32_t v = and_or(shr(Q, 2 * P - 2), 0x000C000Cu, 0x43004300u);
-    if (b >= 3) v = and_or(shr(d3, P3 - 1), 0x00020002u, v);
-    if (b == 4) v = and_or(shr(d4, P3), 0x00010001u, v);
+    uint32_t v = (shr(Q, 2 * P - 2) & 0x000C000Cu) | 0x43004300u;
+    if (b >= 3) v |= shr(d3, P3 - 1) & 0x00020002u;
+    if (b == 4) v |= shr(d4, P3) & 0x00010001u;
     r[p] = v;
   }
-  mfma_operand_fence(r);
   return as_bf16x8(r);
 }
 
@@ -127,9 +134,8 @@ __device__ __forceinline__ bf16x8 deq_u2(const u32x2& c, int t) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int P = 4 * (t & 1) + p;
-    r[p] = and_or(shr(C, 2 * P), 0x00030003u, 0x43004300u);
+    r[p] = (shr(C, 2 * P) & 0x00030003u) | 0x43004300u;
   }
-  mfma_operand_fence(r);
   return as_bf16x8(r);
 }
 
@@ -206,13 +212,6 @@ __device__ __forceinline__ void store_tiles(const KArgs& p, const Ctx& c, const 
 // ---------------------------------------------------------------- INT4 / MWQ
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Load from a wave-uniform base plus a 32-bit per-lane byte offset (global
-// loads in "scalar base + vector offset" form: no 64-bit address arithmetic).
-template <class T>
-__device__ __forceinline__ T ldg(const void* ubase, uint32_t voff) {
-  return *reinterpret_cast<const T*>(static_cast<const char*>(ubase) + voff);
-}
-
 // Weight registers of one K block for one wavefront: INT4 = one 16-byte
 // fragment per tile; MWQ = q2 (8 bytes) + d3 + d4 (4 bytes each) per tile.
 struct BRegs {
@@ -221,191 +220,22 @@ struct BRegs {
   uint32_t d3[2], d4[2];
 };
 
-template <int FMT, int EPI, int GPB>
-__global__ __launch_bounds__(kThreads) void qgemm_q_kernel(KArgs p) {
-  constexpr int SPG = 4 / GPB;  // MFMA steps per scale group
-  __shared__ u32x4 lds_a[3][2][4][64];  // [slot][row tile][step][lane], 24 KB
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = uniform(tid >> 6);
-  Ctx c;
-  if (!setup(p, c)) return;  // uniform over the workgroup
-  c.row0 = uniform(c.row0);
-  c.rows = uniform(c.rows);
-  c.e = uniform(c.e);
-  c.bits = uniform(c.bits);
-  const bool two = c.rows > 16;
-  int ct0, ct1, hch;
-  bool v1;
-  const bool wvalid = wave_tiles<EPI == 1>(p, wv, ct0, ct1, v1, hch);
-  const int KB = p.K / 128, NT = p.N / 16;
-
-  // activation staging: this thread carries (row tile rt, step wv, lane) of each K block
-  const rsrc_t ar = make_rsrc(p.A, p.A_bytes);
-  uint32_t aoff[2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-    aoff[rt] = (uint32_t)((src_row(p, c, rt * 16 + (lane & 15)) * p.K + 32 * wv + 8 * (lane >> 4)) * 2);
-  // weight and scale streams of this wavefront's two tiles
-  constexpr uint32_t CB = FMT == 1 ? 1024 : 512;  // code bytes per tile block
-  rsrc_t br[2], r3[2], r4[2], sr[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const size_t tile = (size_t)c.e * NT + (u ? ct1 : ct0);
-    br[u] = make_rsrc(p.codes + tile * KB * CB, KB * CB);
-    r3[u] = make_rsrc(FMT == 2 ? p.p3 + tile * KB * 256 : nullptr, FMT == 2 ? KB * 256 : 0);
-    r4[u] = make_rsrc(FMT == 2 ? p.p4 + tile * KB * 256 : nullptr, FMT == 2 ? KB * 256 : 0);
-    sr[u] = make_rsrc(p.scales + (tile * 16) * (size_t)(KB * GPB), 16 * KB * GPB * 2);
-  }
-  const uint32_t soff = (uint32_t)((lane & 15) * KB * GPB * 2);
-
-  const uint32_t negc = (0xC300u | (uint32_t)p.z) * 0x00010001u;
-  const bf16x8 neg = as_bf16x8(u32x4{negc, negc, negc, negc});
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) acc[rt][u] = f32x4{};
-
-  // Register rings: weights run PFB K blocks ahead in a ring of RB = PFB + 1
-  // slots, activations PFA = 3 ahead in a ring of RA = 4 slots; the loop is
-  // unrolled by 8 so every ring index is a compile-time constant.  Activation
-  // loads are issued before the weight loads of the same iteration: the memory
-  // counter retires loads in issue order, so waiting for the activations of
-  // block i+1 then never waits for weights beyond block i.
-  // Scales travel in chunks of 4 consecutive groups of a channel (one 8-byte
-  // load per tile per CPK = 4 / GPB K blocks) in a ring of RS chunk slots; when
-  // K / G is not a multiple of 4 the chunk is filled one group at a time.
-  constexpr int PFB = 3, RB = PFB + 1, RA = 4;
-  constexpr int CPK = 4 / GPB, RS = CPK == 4 ? 2 : 4;
-  static_assert(8 % RB == 0 && 8 % RA == 0 && (8 / CPK) % RS == 0, "ring sizes must divide the unroll factor");
-  const bool sc_wide = ((KB * GPB) & 3) == 0;
-  u32x4 ra[RA][2];
-  BRegs rb[RB];
-  u32x2 rsc[RS][2];
-
-#define QG_ISSUE_A(SLOT, KBI)                                                                        \
-  {                                                                                                  \
-    ra[SLOT][0] = buf_x4(ar, aoff[0], (KBI) * 256);                                                  \
-    if (TWO) ra[SLOT][1] = buf_x4(ar, aoff[1], (KBI) * 256);                                         \
-  }
-  // JJ: K block relative to kb (a multiple of 8), a compile-time constant
-#define QG_ISSUE_B(SLOT, JJ)                                                                         \
-  if (wvalid) {                                                                                      \
-    const int kbi = kb + (JJ);                                                                       \
-    _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                  \
-      if (FMT == 1) {                                                                                \
-        rb[SLOT].c[u] = buf_x4(br[u], 16 * lane, kbi * CB);                                          \
-      } else {                                                                                       \
-        rb[SLOT].q[u] = buf_x2(br[u], 8 * lane, kbi * CB);                                           \
-        rb[SLOT].d3[u] = c.bits >= 3 ? buf_x1(r3[u], 4 * lane, kbi * 256) : 0u;                      \
-        rb[SLOT].d4[u] = c.bits == 4 ? buf_x1(r4[u], 4 * lane, kbi * 256) : 0u;                      \
-      }                                                                                              \
-      if (sc_wide) {                                                                                 \
-        if (((JJ) * GPB) % 4 == 0) rsc[((JJ) * GPB / 4) % RS][u] = buf_x2(sr[u], soff, kbi * GPB * 2); \
-      } else {                                                                                       \
-        _Pragma("unroll") for (int g = 0; g < GPB; ++g) {                                            \
-          const int lg = (JJ) * GPB + g;                                                             \
-          const uint32_t v = buf_u16(sr[u], soff, (kbi * GPB + g) * 2);                              \
-          const uint32_t wd = rsc[(lg / 4) % RS][u][(lg % 4) >> 1];                                  \
-          rsc[(lg / 4) % RS][u][(lg % 4) >> 1] =                                                     \
-              (lg & 1) ? ((wd & 0xFFFFu) | (v << 16)) : ((wd & 0xFFFF0000u) | v);                    \
-        }                                                                                            \
-      }                                                                                              \
-    }                                                                                                \
-  }
-#define QG_STAGE(SLOT, KBI)                                                                          \
-  {                                                                                                  \
-    lds_a[(KBI) % 3][0][wv][lane] = ra[SLOT][0];                                                     \
-    if (TWO) lds_a[(KBI) % 3][1][wv][lane] = ra[SLOT][1];                                            \
-  }
-  // one scale group (SPG steps starting at T0) for both row tiles: the
-  // correction chains first, then each tile's chain starts from them (each
-  // weight fragment is dequantised once and used for both row tiles);
-  // acc += scale * chain
-#define QG_GROUP(J, T0, SLOT3)                                                                       \
-  {                                                                                                  \
-    f32x4 cr0 = f32x4{}, cr1 = f32x4{};                                                              \
-    _Pragma("unroll") for (int t = T0; t < T0 + SPG; ++t) {                                          \
-      cr0 = mfma16(as_bf16x8(lds_a[SLOT3][0][t][lane]), neg, cr0);                                   \
-      if (TWO) cr1 = mfma16(as_bf16x8(lds_a[SLOT3][1][t][lane]), neg, cr1);                          \
-    }                                                                                                \
-    _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                  \
-      f32x4 tm0 = cr0, tm1 = cr1;                                                                    \
-      _Pragma("unroll") for (int t = T0; t < T0 + SPG; ++t) {                                        \
-        const bf16x8 bv = (FMT == 1) ? deq_u4(rb[(J) % RB].c[u], t)                                  \
-                                     : deq_mwq(rb[(J) % RB].q[u], rb[(J) % RB].d3[u], rb[(J) % RB].d4[u], t, c.bits); \
-        tm0 = mfma16(as_bf16x8(lds_a[SLOT3][0][t][lane]), bv, tm0);                                  \
-        if (TWO) tm1 = mfma16(as_bf16x8(lds_a[SLOT3][1][t][lane]), bv, tm1);                         \
-      }                                                                                              \
-      const int lg = (J) * GPB + (T0) / SPG;                                                         \
-      const float sv = f16_to_f32((uint16_t)(rsc[(lg / 4) % RS][u][(lg % 4) >> 1] >> (16 * (lg & 1)))); \
-      _Pragma("unroll") for (int r = 0; r < 4; ++r) acc[0][u][r] = __builtin_fmaf(sv, tm0[r], acc[0][u][r]); \
-      if (TWO)                                                                                       \
-        _Pragma("unroll") for (int r = 0; r < 4; ++r) acc[1][u][r] = __builtin_fmaf(sv, tm1[r], acc[1][u][r]); \
-    }                                                                                                \
-  }
-#define QG_STEP(J)                                                                                   \
-  if (kb + J < KB) {                                                                                 \
-    const int i = kb + J;                                                                            \
-    if (i + 3 < KB) QG_ISSUE_A((J + 3) % RA, i + 3);                                                 \
-    if (i + PFB < KB) QG_ISSUE_B(((J) + PFB) % RB, (J) + PFB);                                       \
-    if (i + 1 < KB) QG_STAGE((J + 1) % RA, i + 1);                                                   \
-    __syncthreads();                                                                                 \
-    if (wvalid) {                                                                                    \
-      const int sl = i % 3;                                                                          \
-      _Pragma("unroll") for (int t0 = 0; t0 < 4; t0 += SPG) QG_GROUP(J, t0, sl);                     \
-    }                                                                                                \
-  }
-
-  // The K loop, instantiated for one or two 16-row MFMA tiles (uniform branch).
-  auto k_loop = [&](auto two_tag) {
-  constexpr bool TWO = decltype(two_tag)::value;
-  // prologue: activations of K blocks 0..2, then weights of 0..PFB-1 in flight; block 0 staged
-  int kb = 0;
-#pragma unroll
-  for (int j = 0; j < 3; ++j)
-    if (j < KB) QG_ISSUE_A(j, j);
-#pragma unroll
-  for (int j = 0; j < PFB; ++j)
-    if (j < KB) QG_ISSUE_B(j % RB, j);
-  QG_STAGE(0, 0);
-  for (; kb < KB; kb += 8) {
-    QG_STEP(0)
-    QG_STEP(1)
-    QG_STEP(2)
-    QG_STEP(3)
-    QG_STEP(4)
-    QG_STEP(5)
-    QG_STEP(6)
-    QG_STEP(7)
-  }
-  };
-  if (two) k_loop(std::true_type{});
-  else k_loop(std::false_type{});
-#undef QG_ISSUE_A
-#undef QG_ISSUE_B
-#undef QG_STAGE
-#undef QG_GROUP
-#undef QG_STEP
-  if (wvalid) store_tiles<EPI>(p, c, acc, ct0, ct1, v1, hch, two);
-}
-
 // ------------------------------------------------------------ decode, deep
 // One workgroup per (16-row tile of one segment, channel group of 64 SwiGLU /
 // 128 plain channels); each wavefront owns two 16-channel tiles and streams
-// all of K.  Weights and activations both run PF = 7 K blocks ahead in
+// all of K.  Weights and activations both run PF = 3 K blocks ahead in
 // register rings (the memory counter retires loads in issue order, so the
 // activations, issued first, never make a wavefront wait for weights it does
-// not need yet).  Each step's activation fragment is read from LDS once and
-// feeds, per tile, the bias-correction MFMA with -(128 + z) and the MFMA on
-// the dequantised codes, so no fragment stays live across steps.  Workgroups
+// not need yet).  Per scale group, one bias-correction chain (the activation
+// fragments times -(128 + z)) seeds the chains of both tiles on the
+// dequantised codes.  Workgroups
 // are numbered so that the row tiles of one segment and channel group run on
 // one XCD, back to back: a segment of more than 16 rows reads its weights
 // from HBM once and from that XCD's L2 after.
 template <int FMT, int EPI, int GPB>
 __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, int n_rt) {
   constexpr int SPG = 4 / GPB;                 // MFMA steps per scale group
-  constexpr int PF = 7, R = 8;                 // prefetch distance, ring size
+  constexpr int PF = 3, R = 4;                 // prefetch distance, ring size
   // Scales: chunks of 4 groups of a channel (one 8-byte load per tile per CPK
   // K blocks), loaded with the weights, in a ring of RS chunk slots that
   // covers every chunk alive across the PF + 1 blocks in flight.  The loop
@@ -495,13 +325,14 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
     if (wvalid) {                                                                                    \
       const int sl = i % 3;                                                                          \
       _Pragma("unroll") for (int t0 = 0; t0 < 4; t0 += SPG) {                                        \
-        f32x4 tm[2] = {f32x4{}, f32x4{}};                                                            \
+        f32x4 cr = f32x4{};                                                                          \
+        _Pragma("unroll") for (int t = t0; t < t0 + SPG; ++t) cr = mfma16(as_bf16x8(lds_a[sl][t][lane]), neg, cr); \
+        f32x4 tm[2] = {cr, cr};                                                                      \
         _Pragma("unroll") for (int t = t0; t < t0 + SPG; ++t) {                                      \
           const bf16x8 av = as_bf16x8(lds_a[sl][t][lane]);                                           \
           _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                            \
             const bf16x8 bv = (FMT == 1) ? deq_u4(rb[(J) % R].c[u], t)                               \
                                          : deq_mwq(rb[(J) % R].q[u], rb[(J) % R].d3[u], rb[(J) % R].d4[u], t, c.bits); \
-            tm[u] = mfma16(av, neg, tm[u]);                                                          \
             tm[u] = mfma16(av, bv, tm[u]);                                                           \
           }                                                                                          \
         }                                                                                            \
@@ -895,15 +726,6 @@ __global__ __launch_bounds__(256, 2) void qgemm_p_kernel(KArgs p, int n_nblk, in
 }
 
 template <int FMT, int EPI>
-void launch_q(const KArgs& ka, dim3 grid, hipStream_t s) {
-  switch (ka.G) {
-    case 128: hipLaunchKernelGGL((qgemm_q_kernel<FMT, EPI, 1>), grid, dim3(kThreads), 0, s, ka); break;
-    case 64: hipLaunchKernelGGL((qgemm_q_kernel<FMT, EPI, 2>), grid, dim3(kThreads), 0, s, ka); break;
-    default: hipLaunchKernelGGL((qgemm_q_kernel<FMT, EPI, 4>), grid, dim3(kThreads), 0, s, ka); break;
-  }
-}
-
-template <int FMT, int EPI>
 void launch_d(const KArgs& ka, int n_cg, int n_rt, hipStream_t s) {
   const int items = n_cg * n_rt;
   const dim3 grid((unsigned)(((items + 7) / 8) * 8));  // multiple of 8: one equal share per XCD
@@ -928,7 +750,7 @@ void launch_p(const KArgs& ka, int n_nblk, int n_mt, hipStream_t s) {
 // path: 0 = small-row-tile kernel, 64 / 128 = large-row-tile kernel with that tile height
 template <int EPI>
 void launch_epi(const KArgs& ka, int fmt, int path, int M_total, hipStream_t s) {
-  if (fmt != 3 && path > 0) {
+  if (fmt != 3 && path != 0) {
     const int n_nblk = EPI == 1 ? (ka.N / 2 + 63) / 64 : (ka.N + 127) / 128;
     const int n_mt = (M_total + path - 1) / path + ka.nseg;
     if (fmt == 1) {
@@ -947,12 +769,6 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, hipStream_t s) 
     hipLaunchKernelGGL((qgemm_delta_kernel<EPI>), dim3(gx, gy), dim3(kThreads), 0, s, ka);
     return;
   }
-  if (path == -32) {
-    const dim3 grid(gx, (M_total + kRows - 1) / kRows + ka.nseg);
-    if (fmt == 1) launch_q<1, EPI>(ka, grid, s);
-    else launch_q<2, EPI>(ka, grid, s);
-    return;
-  }
   const int n_rt = (M_total + 15) / 16 + ka.nseg;
   if (fmt == 1) launch_d<1, EPI>(ka, gx, n_rt, s);
   else launch_d<2, EPI>(ka, gx, n_rt, s);
@@ -965,7 +781,6 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, hipStream_t s) 
 int pick_path(int M_total, int nseg, int G) {
   if (const char* f = getenv("MOE_QGEMM_PATH")) {
     if (!strcmp(f, "small")) return 0;
-    if (!strcmp(f, "small32")) return -32;
     if (!strcmp(f, "64")) return 64;
     if (!strcmp(f, "128")) return 128;
   }
