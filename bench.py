@@ -12,8 +12,8 @@ Default workload: the decode-shaped OLMoE-like layer (32 tokens, 64 experts,
 top-8, hidden 2048, SwiGLU 1024, INT4 g128, Zipf(1.1) popularity).
 
 Prints one JSON line.  The dominant kernel's duration comes from HIP events
-around its own launches on the stream it runs on (the queue is kept busy
-first so the events time the kernel, not the host).
+around batches of its own launches on the stream it runs on (the queue is
+kept busy first so the events time the kernels, not the host).
 """
 from __future__ import annotations
 
@@ -174,17 +174,22 @@ def main():
     ms_per_step = elapsed * 1e3 / max(args.steps, 1)
     tokens_per_s = T * args.steps / elapsed
 
-    # ---- dominant kernel: HIP events around its own launches on its stream
+    # ---- dominant kernel: HIP events on its own stream around batches of
+    # back-to-back launches (weight copies rotated); the queue is kept busy
+    # first, so the events time the kernels and not the host.  Per launch =
+    # batch time / batch size (one event pair per launch would add the
+    # dispatch latency of every launch to a ~20 us kernel).
     stream = torch.cuda.current_stream()
-    nmeas = max(20, min(args.steps, 200))
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nmeas)]
-    for i in range(nmeas):
-        torch.cuda._sleep(200_000)          # GPU busy while the three launches are queued
+    batch, nbatch = 20, max(5, min(args.steps // 20, 20))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nbatch)]
+    for i in range(nbatch):
+        torch.cuda._sleep(1_000_000)
         evs[i][0].record(stream)
-        dominant(i % ncopies)
+        for j in range(batch):
+            dominant((i * batch + j) % ncopies)
         evs[i][1].record(stream)
     torch.cuda.synchronize()
-    durs_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    durs_ms = np.array([a.elapsed_time(b) for a, b in evs]) / batch
     dom_ms = float(np.mean(durs_ms))
 
     # algorithmic bytes / flops of one dominant launch
