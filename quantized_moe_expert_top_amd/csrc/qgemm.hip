@@ -499,36 +499,35 @@ __global__ __launch_bounds__(kThreads) void qgemm_delta_kernel(KArgs p) {
 }
 
 // ------------------------------------------------------------------ prefill
-// Large row tiles: MT rows (64 or 128) x 64 SwiGLU channels / 128 plain
-// channels per workgroup of 4 wavefronts (2 x 2: row half x channel half).
-// Each wavefront dequantises its 4 weight tiles once per K block and reuses
-// them for MT/2 rows.  The activation rows are gathered once per K block into
-// a double-buffered LDS tile; while staging them the loader threads also sum
-// each row over every scale group (v_dot2 with (1, 1)), and that row sum times
-// -(128 + z) starts each group's MFMA chain, which removes the +128 bias of the
-// dequantised codes without a separate correction chain.  Workgroups are
-// numbered so that all row tiles of one weight tile land on the same XCD (one
-// L2) and read the weights from HBM once.
-template <int MT>
-struct PTile {
-  int row0, rows, e, bits;
-};
-
-template <int FMT, int EPI, int GPB, int MT>
-__global__ __launch_bounds__(256, 2) void qgemm_p_kernel(KArgs p, int n_nblk, int n_mt) {
-  constexpr int RT = MT / 32;          // 16-row MFMA tiles per wavefront (MT/2 rows)
+// Large row tiles for segments with many rows.  A workgroup of WR x 4
+// wavefronts covers MT = 64 * WR rows x 64 SwiGLU channels (128 plain
+// channels); wavefront (wm, wn) owns 64 rows (4 MFMA row tiles) and two
+// 16-channel tiles (the gate tile and its up tile for SwiGLU, else two
+// neighbouring tiles), so each dequantised weight fragment feeds 4 MFMAs.
+// The activation rows of a K block are gathered once per workgroup into a
+// double-buffered LDS tile; while staging them the loader threads also sum
+// each row over every scale group (v_dot2 with (1, 1)), and that row sum
+// times -(128 + z) starts each group's MFMA chain, which removes the +128 bias
+// of the dequantised codes without a separate correction chain.  Workgroups
+// are numbered so that all row tiles of one weight tile land on the same XCD
+// (one L2) and read the weights from HBM once.
+template <int FMT, int EPI, int GPB, int WR>
+__global__ __launch_bounds__(256 * WR) void qgemm_p_kernel(KArgs p, int n_nblk, int n_mt) {
+  constexpr int NT_ = 256 * WR;        // threads
+  constexpr int RT = 4, UT = 2;        // MFMA row tiles, channel tiles per wavefront
+  constexpr int MT = 64 * WR;          // rows per workgroup
   constexpr int SPG = 4 / GPB;         // MFMA steps per scale group
-  constexpr int TPR = 256 / MT;        // loader threads per row
-  constexpr int NCH = 16 / TPR;        // 16-byte chunks per loader thread per K block
+  constexpr int NCH = 4;               // 16-byte chunks per loader thread per K block
+  constexpr int TPR = 16 / NCH;        // loader threads per row
+  static_assert(NT_ == MT * TPR, "one loader thread per (row, chunk group)");
   __shared__ u32x4 lds_a[2][MT / 16][4][64];
   __shared__ __attribute__((aligned(16))) float lds_r[2][GPB][MT];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = uniform(tid >> 6), wm = wv & 1, wn = wv >> 1;
+  const int wv = uniform(tid >> 6), wm = wv / 4, wn = wv % 4;
 
   // XCD-aware numbering: workgroup L runs on XCD L % 8; give each XCD a
   // contiguous range of (weight tile, row tile) items, weight-tile major.
-  const int total = gridDim.x;
-  const int per_xcd = total / 8;
+  const int per_xcd = gridDim.x / 8;
   const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
   const int nb = item / n_mt, mt = item % n_mt;
   if (nb >= n_nblk) return;
@@ -540,38 +539,33 @@ __global__ __launch_bounds__(256, 2) void qgemm_p_kernel(KArgs p, int n_nblk, in
   const int bits = uniform(4 - (seg % p.S));
   const int KB = p.K / 128, NT = p.N / 16;
 
-  // this wavefront's 4 channel tiles: SwiGLU = 2 gate + the 2 matching up tiles
-  int ct[4];
-  bool cv[4];
+  // this wavefront's 2 channel tiles
+  int ct[UT];
+  bool cv;
   int hch0 = 0;
   if (EPI == 1) {
-    hch0 = nb * 64 + 32 * wn;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      ct[u] = hch0 / 16 + u;
-      ct[2 + u] = NT / 2 + hch0 / 16 + u;
-      cv[u] = cv[2 + u] = hch0 + 16 * u < p.N / 2;
-    }
+    hch0 = nb * 64 + 16 * wn;
+    ct[0] = hch0 / 16;
+    ct[1] = NT / 2 + hch0 / 16;
+    cv = hch0 < p.N / 2;
   } else {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      ct[u] = nb * 8 + 4 * wn + u;
-      cv[u] = ct[u] < NT;
-    }
+    ct[0] = nb * 8 + 2 * wn;
+    ct[1] = ct[0] + 1;
+    cv = ct[0] < NT;
   }
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    if (!cv[u]) ct[u] = 0;  // never stored; keeps the loads in bounds
+  const bool cv1 = EPI == 1 ? cv : ct[1] < NT;
+  if (!cv) ct[0] = 0;  // never stored; keeps the loads in bounds
+  if (!cv1) ct[1] = 0;
 
-  // activation loader: thread -> row r, chunks [part*NCH, part*NCH + NCH) of each K block
+  // activation loader: thread -> row lr, chunks [part*NCH, part*NCH + NCH) of each K block
   const int lr = tid / TPR, part = tid % TPR;
   const rsrc_t ar = make_rsrc(p.A, p.A_bytes);
   const uint32_t aoff = (uint32_t)((src_row(p, Ctx{row0, rows, e, bits}, lr) * p.K + 8 * part * NCH) * 2);
 
   constexpr uint32_t CB = FMT == 1 ? 1024 : 512;
-  rsrc_t br[4], r3[4], r4[4], sr[4];
+  rsrc_t br[UT], r3[UT], r4[UT], sr[UT];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < UT; ++u) {
     const size_t tile = (size_t)e * NT + ct[u];
     br[u] = make_rsrc(p.codes + tile * KB * CB, KB * CB);
     r3[u] = make_rsrc(FMT == 2 ? p.p3 + tile * KB * 256 : nullptr, FMT == 2 ? KB * 256 : 0);
@@ -581,15 +575,15 @@ __global__ __launch_bounds__(256, 2) void qgemm_p_kernel(KArgs p, int n_nblk, in
   const uint32_t soff = (uint32_t)((lane & 15) * KB * GPB * 2);
   const float negz = -(128.0f + (float)p.z);
 
-  f32x4 acc[RT][4];
+  f32x4 acc[RT][UT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[rt][u] = f32x4{};
+    for (int u = 0; u < UT; ++u) acc[rt][u] = f32x4{};
 
   u32x4 ra[NCH];
-  BRegs rb[2][2];       // [ring][tile pair]: tiles 2q, 2q+1 in rb[.][q]
-  uint16_t rs[2][4][GPB];
+  BRegs rb[2];          // [ring]: tiles 0, 1 in c[0], c[1] (or q / d3 / d4)
+  uint16_t rs[2][UT][GPB];
 
   auto issue_a = [&](int kb) {
 #pragma unroll
@@ -620,58 +614,53 @@ __global__ __launch_bounds__(256, 2) void qgemm_p_kernel(KArgs p, int n_nblk, in
   };
   auto issue_b = [&](int slot, int kb) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int u = 2 * q + h;
-        if (FMT == 1) {
-          rb[slot][q].c[h] = buf_x4(br[u], 16 * lane, kb * CB);
-        } else {
-          rb[slot][q].q[h] = buf_x2(br[u], 8 * lane, kb * CB);
-          rb[slot][q].d3[h] = bits >= 3 ? buf_x1(r3[u], 4 * lane, kb * 256) : 0u;
-          rb[slot][q].d4[h] = bits == 4 ? buf_x1(r4[u], 4 * lane, kb * 256) : 0u;
-        }
-#pragma unroll
-        for (int g = 0; g < GPB; ++g) rs[slot][u][g] = buf_u16(sr[u], soff, (kb * GPB + g) * 2);
+    for (int u = 0; u < UT; ++u) {
+      if (FMT == 1) {
+        rb[slot].c[u] = buf_x4(br[u], 16 * lane, kb * CB);
+      } else {
+        rb[slot].q[u] = buf_x2(br[u], 8 * lane, kb * CB);
+        rb[slot].d3[u] = bits >= 3 ? buf_x1(r3[u], 4 * lane, kb * 256) : 0u;
+        rb[slot].d4[u] = bits == 4 ? buf_x1(r4[u], 4 * lane, kb * 256) : 0u;
       }
+#pragma unroll
+      for (int g = 0; g < GPB; ++g) rs[slot][u][g] = buf_u16(sr[u], soff, (kb * GPB + g) * 2);
+    }
   };
   auto compute = [&](int slot, int buf) {
 #pragma unroll
     for (int g = 0; g < GPB; ++g) {
-      // bias correction of this group for each of this wavefront's row tiles
-      f32x4 cinit[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const f32x4 rv = *reinterpret_cast<const f32x4*>(&lds_r[buf][g][wm * (MT / 2) + 16 * rt + 4 * (lane >> 4)]);
-        cinit[rt] = rv * negz;
-      }
-      f32x4 tmp[RT][4];
+      // this group's activation fragments for the wavefront's 4 row tiles
+      bf16x8 av[RT][SPG];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) tmp[rt][u] = cinit[rt];
+        for (int tt = 0; tt < SPG; ++tt) av[rt][tt] = as_bf16x8(lds_a[buf][wm * RT + rt][g * SPG + tt][lane]);
+      // bias correction of this group for each row tile
+      f32x4 cinit[RT];
 #pragma unroll
-      for (int t = g * SPG; t < (g + 1) * SPG; ++t) {
-        bf16x8 bv[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const BRegs& b = rb[slot][u >> 1];
-          bv[u] = (FMT == 1) ? deq_u4(b.c[u & 1], t) : deq_mwq(b.q[u & 1], b.d3[u & 1], b.d4[u & 1], t, bits);
-        }
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const bf16x8 av = as_bf16x8(lds_a[buf][wm * (RT) + rt][t][lane]);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) tmp[rt][u] = mfma16(av, bv[u], tmp[rt][u]);
-        }
+      for (int rt = 0; rt < RT; ++rt) {
+        const f32x4 rv = *reinterpret_cast<const f32x4*>(&lds_r[buf][g][wm * 64 + 16 * rt + 4 * (lane >> 4)]);
+        cinit[rt] = rv * negz;
       }
+      // one channel tile at a time: each dequantised fragment feeds RT MFMAs
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < UT; ++u) {
+        f32x4 tmp[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) tmp[rt] = cinit[rt];
+#pragma unroll
+        for (int tt = 0; tt < SPG; ++tt) {
+          const int t = g * SPG + tt;
+          const bf16x8 bv = (FMT == 1) ? deq_u4(rb[slot].c[u], t)
+                                       : deq_mwq(rb[slot].q[u], rb[slot].d3[u], rb[slot].d4[u], t, bits);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) tmp[rt] = mfma16(av[rt][tt], bv, tmp[rt]);
+        }
         const float sv = f16_to_f32(rs[slot][u][g]);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[rt][u][r] = __builtin_fmaf(sv, tmp[rt][u][r], acc[rt][u][r]);
+          for (int r = 0; r < 4; ++r) acc[rt][u][r] = __builtin_fmaf(sv, tmp[rt][r], acc[rt][u][r]);
       }
     }
   };
@@ -702,20 +691,17 @@ __global__ __launch_bounds__(256, 2) void qgemm_p_kernel(KArgs p, int n_nblk, in
   for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = wm * (MT / 2) + 16 * rt + 4 * (lane >> 4) + r;
+      const int row = wm * 64 + 16 * rt + 4 * (lane >> 4) + r;
       if (row >= rows) continue;
       if (EPI == 1) {
+        if (!cv) continue;
         uint16_t* orow = static_cast<uint16_t*>(p.out) + (size_t)(row0 + row) * p.n_out;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          if (!cv[u]) continue;
-          const float g = acc[rt][u][r], up = acc[rt][2 + u][r];
-          orow[hch0 + 16 * u + col] = f32_to_bf16(g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * up);
-        }
+        const float g = acc[rt][0][r], up = acc[rt][1][r];
+        orow[hch0 + col] = f32_to_bf16(g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * up);
       } else {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (!cv[u]) continue;
+        for (int u = 0; u < UT; ++u) {
+          if (!(u ? cv1 : cv)) continue;
           const size_t o = (size_t)(row0 + row) * p.n_out + ct[u] * 16 + col;
           if (EPI == 2) static_cast<float*>(p.out)[o] = acc[rt][u][r];
           else static_cast<uint16_t*>(p.out)[o] = f32_to_bf16(acc[rt][u][r]);
@@ -736,14 +722,15 @@ void launch_d(const KArgs& ka, int n_cg, int n_rt, hipStream_t s) {
   }
 }
 
-template <int FMT, int EPI, int MT>
+template <int FMT, int EPI, int WR>
 void launch_p(const KArgs& ka, int n_nblk, int n_mt, hipStream_t s) {
   const int items = n_nblk * n_mt;
   const dim3 grid((unsigned)(((items + 7) / 8) * 8));  // multiple of 8: one equal share per XCD
+  const dim3 block(256 * WR);
   switch (ka.G) {
-    case 128: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 1, MT>), grid, dim3(256), 0, s, ka, n_nblk, n_mt); break;
-    case 64: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 2, MT>), grid, dim3(256), 0, s, ka, n_nblk, n_mt); break;
-    default: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 4, MT>), grid, dim3(256), 0, s, ka, n_nblk, n_mt); break;
+    case 128: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 1, WR>), grid, block, 0, s, ka, n_nblk, n_mt); break;
+    case 64: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 2, WR>), grid, block, 0, s, ka, n_nblk, n_mt); break;
+    default: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 4, WR>), grid, block, 0, s, ka, n_nblk, n_mt); break;
   }
 }
 
@@ -754,11 +741,11 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, hipStream_t s) 
     const int n_nblk = EPI == 1 ? (ka.N / 2 + 63) / 64 : (ka.N + 127) / 128;
     const int n_mt = (M_total + path - 1) / path + ka.nseg;
     if (fmt == 1) {
-      if (path == 64) launch_p<1, EPI, 64>(ka, n_nblk, n_mt, s);
-      else launch_p<1, EPI, 128>(ka, n_nblk, n_mt, s);
+      if (path == 64) launch_p<1, EPI, 1>(ka, n_nblk, n_mt, s);
+      else launch_p<1, EPI, 2>(ka, n_nblk, n_mt, s);
     } else {
-      if (path == 64) launch_p<2, EPI, 64>(ka, n_nblk, n_mt, s);
-      else launch_p<2, EPI, 128>(ka, n_nblk, n_mt, s);
+      if (path == 64) launch_p<2, EPI, 1>(ka, n_nblk, n_mt, s);
+      else launch_p<2, EPI, 2>(ka, n_nblk, n_mt, s);
     }
     return;
   }
@@ -775,18 +762,18 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, hipStream_t s) 
 }
 
 // Row-tile height from the mean rows per segment (the host never sees the
-// device counts): few rows per segment -> 32-row tiles that skip empty MFMA
-// row tiles; many -> 64 / 128-row tiles that reuse each dequantised weight
-// fragment for more rows.  MOE_QGEMM_PATH=small|64|128 forces a path.
-int pick_path(int M_total, int nseg, int G) {
+// device counts): few rows per segment -> 16-row tiles (decode kernel); many
+// -> 64 / 128-row tiles that reuse each dequantised weight fragment for more
+// rows.  MOE_QGEMM_PATH=small|64|128 forces a path.
+int pick_path(int M_total, int nseg) {
   if (const char* f = getenv("MOE_QGEMM_PATH")) {
     if (!strcmp(f, "small")) return 0;
     if (!strcmp(f, "64")) return 64;
     if (!strcmp(f, "128")) return 128;
   }
-  if (G < 64) return 0;  // four scale groups per K block do not fit the large tile's registers
   const double avg = (double)M_total / (double)(nseg > 0 ? nseg : 1);
-  return avg < 24.0 ? 0 : 64;
+  if (avg < 24.0) return 0;
+  return avg < 96.0 ? 64 : 128;
 }
 }  // namespace
 
@@ -819,7 +806,7 @@ hipError_t launch_qgemm(const QGemmArgs& a, hipStream_t s) {
   const bool swiglu = a.epilogue == 1;
   ka.n_out = swiglu ? w.N / 2 : w.N;
   (void)swiglu;
-  const int path = pick_path(a.M_total, a.nseg, w.G);
+  const int path = pick_path(a.M_total, a.nseg);
   if (a.epilogue == 1) launch_epi<1>(ka, w.fmt, path, a.M_total, s);
   else if (a.epilogue == 2) launch_epi<2>(ka, w.fmt, path, a.M_total, s);
   else launch_epi<0>(ka, w.fmt, path, a.M_total, s);
