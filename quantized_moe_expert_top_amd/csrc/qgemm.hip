@@ -509,10 +509,16 @@ __global__ __launch_bounds__(kThreads) void qgemm_delta_kernel(KArgs p) {
 // each row over every scale group (v_dot2 with (1, 1)), and that row sum
 // times -(128 + z) starts each group's MFMA chain, which removes the +128 bias
 // of the dequantised codes without a separate correction chain.  Workgroups
-// are numbered so that all row tiles of one weight tile land on the same XCD
-// (one L2) and read the weights from HBM once.
+// are numbered in groups of row tiles per XCD (L2 reuse of both operands).
+//
+// LDS slot of (row r of a 16-row tile, MFMA step t, 8-wide k group g4) in a
+// staged activation block: the MFMA operand layout (slot = r + 16 * g4) with
+// the row rotated by 4 * t, so that the loader's stores (four rows x four
+// steps per 16 lanes) fall in distinct banks; readers apply the same map.
+__device__ __forceinline__ int a_slot(int r, int t, int g4) { return ((r + 4 * t) & 15) + 16 * g4; }
+
 template <int FMT, int EPI, int GPB, int WR>
-__global__ __launch_bounds__(256 * WR) void qgemm_p_kernel(KArgs p, int n_nblk, int n_mt) {
+__global__ __launch_bounds__(256 * WR, 2 / WR) void qgemm_p_kernel(KArgs p, int n_nblk, int n_mt, int GM) {
   constexpr int NT_ = 256 * WR;        // threads
   constexpr int RT = 4, UT = 2;        // MFMA row tiles, channel tiles per wavefront
   constexpr int MT = 64 * WR;          // rows per workgroup
@@ -525,12 +531,16 @@ __global__ __launch_bounds__(256 * WR) void qgemm_p_kernel(KArgs p, int n_nblk, 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = uniform(tid >> 6), wm = wv / 4, wn = wv % 4;
 
-  // XCD-aware numbering: workgroup L runs on XCD L % 8; give each XCD a
-  // contiguous range of (weight tile, row tile) items, weight-tile major.
+  // XCD-aware numbering: workgroup L runs on XCD L % 8; each XCD gets a
+  // contiguous range of items, ordered (group of GM row tiles, channel block,
+  // row tile): the GM row tiles of a group share each channel block's weights
+  // and keep their activation rows in that XCD's L2 across channel blocks
+  // (GM = all row tiles when the weights outweigh the activations).
   const int per_xcd = gridDim.x / 8;
   const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  const int nb = item / n_mt, mt = item % n_mt;
-  if (nb >= n_nblk) return;
+  const int grp = item / (GM * n_nblk), rem = item % (GM * n_nblk);
+  const int nb = rem / GM, mt = grp * GM + rem % GM;
+  if (mt >= n_mt) return;
   int seg, m0;
   if (!find_tile(p.seg_offsets, p.nseg, mt, seg, m0, MT)) return;
   const int row0 = uniform(p.seg_offsets[seg] + m0);
@@ -581,15 +591,19 @@ __global__ __launch_bounds__(256 * WR) void qgemm_p_kernel(KArgs p, int n_nblk, 
 #pragma unroll
     for (int u = 0; u < UT; ++u) acc[rt][u] = f32x4{};
 
-  u32x4 ra[NCH];
-  BRegs rb[2];          // [ring]: tiles 0, 1 in c[0], c[1] (or q / d3 / d4)
-  uint16_t rs[2][UT][GPB];
+  // Register rings: activations and weights run PF K blocks ahead (the
+  // activations issued first: the memory counter retires loads in issue
+  // order); the loop is unrolled by R so that ring slots are constants.
+  constexpr int PF = 3, R = 4;
+  u32x4 ra[R][NCH];
+  BRegs rb[R];          // per slot: tiles 0, 1 in c[0], c[1] (or q / d3 / d4)
+  uint16_t rs[R][UT][GPB];
 
-  auto issue_a = [&](int kb) {
+  auto issue_a = [&](int slot, int kb) {
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) ra[c] = buf_x4(ar, aoff + 16 * c, kb * 256);
+    for (int c = 0; c < NCH; ++c) ra[slot][c] = buf_x4(ar, aoff + 16 * c, kb * 256);
   };
-  auto stage_a = [&](int buf) {
+  auto stage_a = [&](int slot, int buf) {
     float part_sum[GPB];
 #pragma unroll
     for (int g = 0; g < GPB; ++g) part_sum[g] = 0.f;
@@ -597,19 +611,20 @@ __global__ __launch_bounds__(256 * WR) void qgemm_p_kernel(KArgs p, int n_nblk, 
     for (int c = 0; c < NCH; ++c) {
       const int ch = part * NCH + c;        // 16-byte chunk of the 128-wide K block
       const int t = ch / 4, g4 = ch % 4;
-      lds_a[buf][lr / 16][t][(lr % 16) + 16 * g4] = ra[c];
+      lds_a[buf][lr / 16][t][a_slot(lr % 16, t, g4)] = ra[slot][c];
       const int grp = (8 * ch) / (128 / GPB);
       float sacc = part_sum[grp];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) sacc = add_bf16_pair(ra[c][h], sacc);
+      for (int h = 0; h < 4; ++h) sacc = add_bf16_pair(ra[slot][c][h], sacc);
       part_sum[grp] = sacc;
     }
+    // the TPR = 4 threads of a row are lanes 4j..4j+3: reduce with quad DPP
 #pragma unroll
     for (int g = 0; g < GPB; ++g) {
       float v = part_sum[g];
-#pragma unroll
-      for (int o = 1; o < TPR; o <<= 1) v += __shfl_xor(v, o, 64);
-      if (part == 0) lds_r[buf][g][lr] = v;
+      v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
+      v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+      if (part == 0) lds_r[buf][g][lr] = v * negz;
     }
   };
   auto issue_b = [&](int slot, int kb) {
@@ -629,61 +644,70 @@ __global__ __launch_bounds__(256 * WR) void qgemm_p_kernel(KArgs p, int n_nblk, 
   auto compute = [&](int slot, int buf) {
 #pragma unroll
     for (int g = 0; g < GPB; ++g) {
-      // this group's activation fragments for the wavefront's 4 row tiles
-      bf16x8 av[RT][SPG];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int tt = 0; tt < SPG; ++tt) av[rt][tt] = as_bf16x8(lds_a[buf][wm * RT + rt][g * SPG + tt][lane]);
-      // bias correction of this group for each row tile
-      f32x4 cinit[RT];
+      // bias correction of this group (row sum * -(128 + z)) seeds both tiles' chains
+      f32x4 tmp[RT][UT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const f32x4 rv = *reinterpret_cast<const f32x4*>(&lds_r[buf][g][wm * 64 + 16 * rt + 4 * (lane >> 4)]);
-        cinit[rt] = rv * negz;
+#pragma unroll
+        for (int u = 0; u < UT; ++u) tmp[rt][u] = rv;
       }
-      // one channel tile at a time: each dequantised fragment feeds RT MFMAs
+      // per step: both tiles' fragments dequantised once, each used by 4 MFMAs
+#pragma unroll
+      for (int tt = 0; tt < SPG; ++tt) {
+        const int t = g * SPG + tt;
+        bf16x8 bv[UT];
+#pragma unroll
+        for (int u = 0; u < UT; ++u)
+          bv[u] = (FMT == 1) ? deq_u4(rb[slot].c[u], t)
+                             : deq_mwq(rb[slot].q[u], rb[slot].d3[u], rb[slot].d4[u], t, bits);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const bf16x8 av = as_bf16x8(lds_a[buf][wm * RT + rt][t][a_slot(lane & 15, t, lane >> 4)]);
+#pragma unroll
+          for (int u = 0; u < UT; ++u) tmp[rt][u] = mfma16(av, bv[u], tmp[rt][u]);
+        }
+      }
 #pragma unroll
       for (int u = 0; u < UT; ++u) {
-        f32x4 tmp[RT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) tmp[rt] = cinit[rt];
-#pragma unroll
-        for (int tt = 0; tt < SPG; ++tt) {
-          const int t = g * SPG + tt;
-          const bf16x8 bv = (FMT == 1) ? deq_u4(rb[slot].c[u], t)
-                                       : deq_mwq(rb[slot].q[u], rb[slot].d3[u], rb[slot].d4[u], t, bits);
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) tmp[rt] = mfma16(av[rt][tt], bv, tmp[rt]);
-        }
         const float sv = f16_to_f32(rs[slot][u][g]);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[rt][u][r] = __builtin_fmaf(sv, tmp[rt][r], acc[rt][u][r]);
+          for (int r = 0; r < 4; ++r) acc[rt][u][r] = __builtin_fmaf(sv, tmp[rt][u][r], acc[rt][u][r]);
       }
     }
   };
 
-  // prologue: activations of block 0 staged, weights of blocks 0 and 1 in flight
-  issue_a(0);
-  issue_b(0, 0);
-  if (1 < KB) issue_b(1, 1);
-  stage_a(0);
-  __syncthreads();
-  for (int kb = 0; kb < KB; kb += 2) {
+
+  // prologue: activations and weights of blocks 0..PF-1 in flight, block 0 staged
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int i = kb + j;
-      if (i < KB) {
-        if (i + 1 < KB) issue_a(i + 1);
-        compute(j, j);
-        if (i + 2 < KB) issue_b(j, i + 2);
-        if (i + 1 < KB) stage_a(1 - j);
-        __syncthreads();
-      }
+  for (int j = 0; j < PF; ++j)
+    if (j < KB) {
+      issue_a(j, j);
+      issue_b(j, j);
     }
+  stage_a(0, 0);
+  __syncthreads();
+#define QP_STEP(J)                                      \
+  if (kb + (J) < KB) {                                  \
+    const int i = kb + (J);                             \
+    if (i + PF < KB) {                                  \
+      issue_a(((J) + PF) % R, i + PF);                  \
+      issue_b(((J) + PF) % R, i + PF);                  \
+    }                                                   \
+    compute((J) % R, i & 1);                            \
+    if (i + 1 < KB) stage_a(((J) + 1) % R, (i + 1) & 1); \
+    __syncthreads();                                    \
   }
+  for (int kb = 0; kb < KB; kb += R) {
+    static_assert(R == 4, "the loop below is unrolled by 4");
+    QP_STEP(0)
+    QP_STEP(1)
+    QP_STEP(2)
+    QP_STEP(3)
+  }
+#undef QP_STEP
 
   // epilogue
   const int col = lane & 15;
@@ -722,15 +746,27 @@ void launch_d(const KArgs& ka, int n_cg, int n_rt, hipStream_t s) {
   }
 }
 
+// Row tiles per ordering group: all of them (channel-block major) when the
+// weights are the larger operand, else as many as keep about 2 MB of
+// activation rows in an XCD's L2.
+int group_rows(const KArgs& ka, int M_total, int n_mt, int MT, int fmt) {
+  const double a_bytes = (double)M_total * ka.K * 2.0;
+  const double w_bytes = (double)(ka.nseg / ka.S) * ka.N * ka.K * (fmt == 1 ? 0.5 : 0.25);
+  if (a_bytes < w_bytes) return n_mt;
+  const int gm = (int)((2u << 20) / ((size_t)MT * ka.K * 2));
+  return gm < 1 ? 1 : (gm > n_mt ? n_mt : gm);
+}
+
 template <int FMT, int EPI, int WR>
-void launch_p(const KArgs& ka, int n_nblk, int n_mt, hipStream_t s) {
-  const int items = n_nblk * n_mt;
-  const dim3 grid((unsigned)(((items + 7) / 8) * 8));  // multiple of 8: one equal share per XCD
+void launch_p(const KArgs& ka, int n_nblk, int n_mt, int M_total, hipStream_t s) {
+  const int GM = group_rows(ka, M_total, n_mt, 64 * WR, FMT);
+  const int items = n_nblk * ((n_mt + GM - 1) / GM) * GM;  // whole groups
+  const dim3 grid((unsigned)(((items + 7) / 8) * 8));        // multiple of 8: one equal share per XCD
   const dim3 block(256 * WR);
   switch (ka.G) {
-    case 128: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 1, WR>), grid, block, 0, s, ka, n_nblk, n_mt); break;
-    case 64: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 2, WR>), grid, block, 0, s, ka, n_nblk, n_mt); break;
-    default: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 4, WR>), grid, block, 0, s, ka, n_nblk, n_mt); break;
+    case 128: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 1, WR>), grid, block, 0, s, ka, n_nblk, n_mt, GM); break;
+    case 64: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 2, WR>), grid, block, 0, s, ka, n_nblk, n_mt, GM); break;
+    default: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 4, WR>), grid, block, 0, s, ka, n_nblk, n_mt, GM); break;
   }
 }
 
@@ -741,11 +777,11 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, hipStream_t s) 
     const int n_nblk = EPI == 1 ? (ka.N / 2 + 63) / 64 : (ka.N + 127) / 128;
     const int n_mt = (M_total + path - 1) / path + ka.nseg;
     if (fmt == 1) {
-      if (path == 64) launch_p<1, EPI, 1>(ka, n_nblk, n_mt, s);
-      else launch_p<1, EPI, 2>(ka, n_nblk, n_mt, s);
+      if (path == 64) launch_p<1, EPI, 1>(ka, n_nblk, n_mt, M_total, s);
+      else launch_p<1, EPI, 2>(ka, n_nblk, n_mt, M_total, s);
     } else {
-      if (path == 64) launch_p<2, EPI, 1>(ka, n_nblk, n_mt, s);
-      else launch_p<2, EPI, 2>(ka, n_nblk, n_mt, s);
+      if (path == 64) launch_p<2, EPI, 1>(ka, n_nblk, n_mt, M_total, s);
+      else launch_p<2, EPI, 2>(ka, n_nblk, n_mt, M_total, s);
     }
     return;
   }
@@ -763,8 +799,8 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, hipStream_t s) 
 
 // Row-tile height from the mean rows per segment (the host never sees the
 // device counts): few rows per segment -> 16-row tiles (decode kernel); many
-// -> 64 / 128-row tiles that reuse each dequantised weight fragment for more
-// rows.  MOE_QGEMM_PATH=small|64|128 forces a path.
+// -> 64-row tiles (two workgroups per CU; the 128-row, one-per-CU variant
+// measured slower).  MOE_QGEMM_PATH=small|64|128 forces a path.
 int pick_path(int M_total, int nseg) {
   if (const char* f = getenv("MOE_QGEMM_PATH")) {
     if (!strcmp(f, "small")) return 0;
@@ -772,8 +808,7 @@ int pick_path(int M_total, int nseg) {
     if (!strcmp(f, "128")) return 128;
   }
   const double avg = (double)M_total / (double)(nseg > 0 ? nseg : 1);
-  if (avg < 24.0) return 0;
-  return avg < 96.0 ? 64 : 128;
+  return avg < 24.0 ? 0 : 64;
 }
 }  // namespace
 
