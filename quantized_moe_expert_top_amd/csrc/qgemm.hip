@@ -499,9 +499,9 @@ __global__ __launch_bounds__(kThreads) void qgemm_delta_kernel(KArgs p) {
 }
 
 // ------------------------------------------------------------------ prefill
-// Large row tiles for segments with many rows.  A workgroup of WR x 4
-// wavefronts covers MT = 64 * WR rows x 64 SwiGLU channels (128 plain
-// channels); wavefront (wm, wn) owns 64 rows (4 MFMA row tiles) and two
+// Large row tiles for segments with many rows.  A workgroup of WR x WC
+// wavefronts covers MT = 64 * WR rows x 16 * WC SwiGLU channels (32 * WC
+// plain channels); wavefront (wm, wn) owns 64 rows (4 MFMA row tiles) and two
 // 16-channel tiles (the gate tile and its up tile for SwiGLU, else two
 // neighbouring tiles), so each dequantised weight fragment feeds 4 MFMAs.
 // The activation rows of a K block are gathered once per workgroup into a
@@ -517,19 +517,20 @@ __global__ __launch_bounds__(kThreads) void qgemm_delta_kernel(KArgs p) {
 // steps per 16 lanes) fall in distinct banks; readers apply the same map.
 __device__ __forceinline__ int a_slot(int r, int t, int g4) { return ((r + 4 * t) & 15) + 16 * g4; }
 
-template <int FMT, int EPI, int GPB, int WR>
-__global__ __launch_bounds__(256 * WR, 2 / WR) void qgemm_p_kernel(KArgs p, int n_nblk, int n_mt, int GM) {
-  constexpr int NT_ = 256 * WR;        // threads
+template <int FMT, int EPI, int GPB, int WR, int WC>
+__global__ __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) void qgemm_p_kernel(KArgs p, int n_nblk, int n_mt, int GM) {
+  constexpr int NT_ = 64 * WR * WC;    // threads
   constexpr int RT = 4, UT = 2;        // MFMA row tiles, channel tiles per wavefront
   constexpr int MT = 64 * WR;          // rows per workgroup
   constexpr int SPG = 4 / GPB;         // MFMA steps per scale group
-  constexpr int NCH = 4;               // 16-byte chunks per loader thread per K block
-  constexpr int TPR = 16 / NCH;        // loader threads per row
+  constexpr int NCH = MT * 16 / NT_;   // 16-byte chunks per loader thread per K block
+  constexpr int TPR = 16 / NCH;        // loader threads per row (4 or 8)
+  static_assert(TPR == 4 || TPR == 8, "row sums reduce over 4 or 8 lanes");
   static_assert(NT_ == MT * TPR, "one loader thread per (row, chunk group)");
   __shared__ u32x4 lds_a[2][MT / 16][4][64];
   __shared__ __attribute__((aligned(16))) float lds_r[2][GPB][MT];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = uniform(tid >> 6), wm = wv / 4, wn = wv % 4;
+  const int wv = uniform(tid >> 6), wm = wv / WC, wn = wv % WC;
 
   // XCD-aware numbering: workgroup L runs on XCD L % 8; each XCD gets a
   // contiguous range of items, ordered (group of GM row tiles, channel block,
@@ -554,12 +555,12 @@ __global__ __launch_bounds__(256 * WR, 2 / WR) void qgemm_p_kernel(KArgs p, int 
   bool cv;
   int hch0 = 0;
   if (EPI == 1) {
-    hch0 = nb * 64 + 16 * wn;
+    hch0 = nb * 16 * WC + 16 * wn;
     ct[0] = hch0 / 16;
     ct[1] = NT / 2 + hch0 / 16;
     cv = hch0 < p.N / 2;
   } else {
-    ct[0] = nb * 8 + 2 * wn;
+    ct[0] = nb * 2 * WC + 2 * wn;
     ct[1] = ct[0] + 1;
     cv = ct[0] < NT;
   }
@@ -618,12 +619,17 @@ __global__ __launch_bounds__(256 * WR, 2 / WR) void qgemm_p_kernel(KArgs p, int 
       for (int h = 0; h < 4; ++h) sacc = add_bf16_pair(ra[slot][c][h], sacc);
       part_sum[grp] = sacc;
     }
-    // the TPR = 4 threads of a row are lanes 4j..4j+3: reduce with quad DPP
+    // the TPR threads of a row are lanes TPR*j .. TPR*j + TPR-1: after two
+    // quad permutes every lane holds its quad's total; for TPR = 8 a
+    // half-row mirror (lane i <- lane 7 - i within each 8 lanes) adds the
+    // other quad, so lane 0 of the 8 holds the row's total
 #pragma unroll
     for (int g = 0; g < GPB; ++g) {
       float v = part_sum[g];
       v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
       v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+      if (TPR == 8)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));  // row_half_mirror
       if (part == 0) lds_r[buf][g][lr] = v * negz;
     }
   };
@@ -757,16 +763,18 @@ int group_rows(const KArgs& ka, int M_total, int n_mt, int MT, int fmt) {
   return gm < 1 ? 1 : (gm > n_mt ? n_mt : gm);
 }
 
-template <int FMT, int EPI, int WR>
-void launch_p(const KArgs& ka, int n_nblk, int n_mt, int M_total, hipStream_t s) {
+template <int FMT, int EPI, int WR, int WC>
+void launch_p(const KArgs& ka, int M_total, hipStream_t s) {
+  const int n_nblk = EPI == 1 ? (ka.N / 2 + 16 * WC - 1) / (16 * WC) : (ka.N + 32 * WC - 1) / (32 * WC);
+  const int n_mt = (M_total + 64 * WR - 1) / (64 * WR) + ka.nseg;
   const int GM = group_rows(ka, M_total, n_mt, 64 * WR, FMT);
   const int items = n_nblk * ((n_mt + GM - 1) / GM) * GM;  // whole groups
   const dim3 grid((unsigned)(((items + 7) / 8) * 8));        // multiple of 8: one equal share per XCD
-  const dim3 block(256 * WR);
+  const dim3 block(64 * WR * WC);
   switch (ka.G) {
-    case 128: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 1, WR>), grid, block, 0, s, ka, n_nblk, n_mt, GM); break;
-    case 64: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 2, WR>), grid, block, 0, s, ka, n_nblk, n_mt, GM); break;
-    default: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 4, WR>), grid, block, 0, s, ka, n_nblk, n_mt, GM); break;
+    case 128: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 1, WR, WC>), grid, block, 0, s, ka, n_nblk, n_mt, GM); break;
+    case 64: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 2, WR, WC>), grid, block, 0, s, ka, n_nblk, n_mt, GM); break;
+    default: hipLaunchKernelGGL((qgemm_p_kernel<FMT, EPI, 4, WR, WC>), grid, block, 0, s, ka, n_nblk, n_mt, GM); break;
   }
 }
 
@@ -774,14 +782,22 @@ void launch_p(const KArgs& ka, int n_nblk, int n_mt, int M_total, hipStream_t s)
 template <int EPI>
 void launch_epi(const KArgs& ka, int fmt, int path, int M_total, hipStream_t s) {
   if (fmt != 3 && path != 0) {
-    const int n_nblk = EPI == 1 ? (ka.N / 2 + 63) / 64 : (ka.N + 127) / 128;
-    const int n_mt = (M_total + path - 1) / path + ka.nseg;
+    // 64 rows per workgroup; 8 wavefront columns (wide channel blocks: the
+    // activations are read fewer times) when the activations outweigh the
+    // weights, else 4.  path 65 forces 4 columns, 128 two rows of 4.
+    if (path == 64) {
+      const double a_bytes = (double)M_total * ka.K * 2.0;
+      const double w_bytes = (double)(ka.nseg / ka.S) * ka.N * ka.K * (fmt == 1 ? 0.5 : 0.25);
+      if (a_bytes < w_bytes && !getenv("MOE_QGEMM_PATH")) path = 65;
+    }
     if (fmt == 1) {
-      if (path == 64) launch_p<1, EPI, 1>(ka, n_nblk, n_mt, M_total, s);
-      else launch_p<1, EPI, 2>(ka, n_nblk, n_mt, M_total, s);
+      if (path == 64) launch_p<1, EPI, 1, 8>(ka, M_total, s);
+      else if (path == 65) launch_p<1, EPI, 1, 4>(ka, M_total, s);
+      else launch_p<1, EPI, 2, 4>(ka, M_total, s);
     } else {
-      if (path == 64) launch_p<2, EPI, 1>(ka, n_nblk, n_mt, M_total, s);
-      else launch_p<2, EPI, 2>(ka, n_nblk, n_mt, M_total, s);
+      if (path == 64) launch_p<2, EPI, 1, 8>(ka, M_total, s);
+      else if (path == 65) launch_p<2, EPI, 1, 4>(ka, M_total, s);
+      else launch_p<2, EPI, 2, 4>(ka, M_total, s);
     }
     return;
   }
@@ -805,6 +821,7 @@ int pick_path(int M_total, int nseg) {
   if (const char* f = getenv("MOE_QGEMM_PATH")) {
     if (!strcmp(f, "small")) return 0;
     if (!strcmp(f, "64")) return 64;
+    if (!strcmp(f, "64n")) return 65;
     if (!strcmp(f, "128")) return 128;
   }
   const double avg = (double)M_total / (double)(nseg > 0 ? nseg : 1);
