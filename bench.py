@@ -225,7 +225,7 @@ def main():
         dom_name = "qgemm gate_up + SwiGLU"
     gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
     tflops = dom_flops / (dom_ms * 1e-3) / 1e12
-    hbm_bound = cfg.name in ("olmoe_decode", "tiny")
+    hbm_bound = cfg.name in ("olmoe_decode", "mixtral_mwq_decode", "tiny")
     roofline = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                  "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
                 if hbm_bound else
@@ -267,7 +267,7 @@ def cpu_baseline(cfg, data, target_s):
     T = cfg.T
     # sample: whole batches for small workloads, else a token subset
     sample_tokens = None
-    if cfg.name not in ("olmoe_decode", "tiny"):
+    if cfg.name not in ("olmoe_decode", "mixtral_mwq_decode", "tiny"):
         sample_tokens = np.arange(0, T, max(1, T // 16))[:16]
     done = 0
     t0 = time.perf_counter()

@@ -18,6 +18,7 @@ five summarised systems; no page fixes a seed, so the seeds are ours):
   olmoe_prefill_zipf  same with the Zipf(1.1) bias
   mixtral_mwq     512 tok, H 4096, I 14336, 8 experts, top-2, nested INT2+d3+d4
                   planes g128, per-pair bit-width from {2:0.40, 3:0.35, 4:0.25}
+  mixtral_mwq_decode  the same layer at a decode batch of 16 tokens
   meswitch_delta  256 requests x 16 tok, linear 4096 -> 14336, 16 experts,
                   shared bf16 base N(0,0.02), 2-bit delta codes with per-output
                   channel fp16 step U(0.0005,0.002), 41 salient input channels
@@ -101,6 +102,8 @@ CONFIGS = {
     "olmoe_prefill_zipf": MoeConfig("olmoe_prefill_zipf", 8192, 2048, 1024, 64, 8, 128, "int4", 0.002, 0.01, 1.1, 304),
     "mixtral_mwq": MoeConfig("mixtral_mwq", 512, 4096, 14336, 8, 2, 128, "mwq", 0.002, 0.01, None, 404,
                              bit_probs=(0.40, 0.35, 0.25)),
+    "mixtral_mwq_decode": MoeConfig("mixtral_mwq_decode", 16, 4096, 14336, 8, 2, 128, "mwq", 0.002, 0.01, None,
+                                    406, bit_probs=(0.40, 0.35, 0.25)),
     "meswitch_delta": DeltaConfig("meswitch_delta", 256, 16, 4096, 14336, 16, 41, 0.02, 0.002,
                                   0.0005, 0.002, 1.0, 505),
 }

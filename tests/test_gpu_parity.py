@@ -165,6 +165,13 @@ def test_layer_mwq_full_size_sampled(G):
     _layer_parity(G, cfg, tokens=np.array([0, 211, 377, 510]))
 
 
+def test_layer_mwq_decode_full(G):
+    """Nested planes at a decode batch (16 tokens): most bit-width segments hold
+    one or two rows, and a segment loads only the planes its width needs."""
+    _layer_parity(G, gen.config("mixtral_mwq_decode", H=1024, I=2048))       # every token
+    _layer_parity(G, gen.config("mixtral_mwq_decode"), tokens=np.array([3, 12]))  # full size, sampled
+
+
 # ------------------------------------------------------------------- delta
 def _delta_parity(G, cfg, tokens=None):
     d = gen.generate(cfg)
