@@ -125,6 +125,21 @@ moe_status moe_permute(const int32_t* topk_ids, const uint8_t* pair_bits,
                        const uint16_t* x, int32_t H, uint16_t* x_perm,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* Routing and grouping in one call: the same outputs as moe_route_topk
+ * followed by moe_permute (without the x gather), bit for bit.  With
+ * E <= 64 and T*k <= 4096 it is a single launch: each workgroup routes 4
+ * tokens and the last workgroup to finish groups all pairs; otherwise it
+ * issues the two separate launches.  Arguments and errors as for those two
+ * calls.  workspace: moe_permute_workspace_size(T, k, E, pair_bits ? 3 : 1)
+ * bytes, 16-byte aligned, whose second 32-bit word (an arrival counter) must
+ * be zero before the first call; every call leaves it zero.  Calls that
+ * share one workspace must not overlap on the device.
+ */
+moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k, const uint8_t* pair_bits,
+                             int32_t* topk_ids, float* topk_w, int32_t* expert_counts, int32_t* seg_offsets,
+                             int32_t* sorted_pair, int32_t* pair_pos, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /* ----------------------------------------------------------- weight formats
  * MOE_W_INT4_GROUP   W4A16 (ExactMoE page): w[n][k] = s[n][k/G] * (c - z),
  *                    c in [0,15].  codes u8 [E][N][K/2] (canonical: even k in

@@ -26,7 +26,7 @@ MOE_DTYPE_BF16, MOE_DTYPE_F32 = 0, 1
 
 EXPORTED = [
     "moe_status_string", "moe_last_error_detail", "moe_abi_version", "moe_route_topk",
-    "moe_permute_workspace_size", "moe_permute", "moe_weight_field_bytes", "moe_repack_weights",
+    "moe_permute_workspace_size", "moe_permute", "moe_route_permute", "moe_weight_field_bytes", "moe_repack_weights",
     "moe_grouped_qgemm_workspace_size", "moe_grouped_qgemm", "moe_unpermute_combine",
 ]
 
@@ -62,6 +62,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_route_topk": (i32, [vp, i32, i32, i32, vp, vp, vp]),
         "moe_permute_workspace_size": (sz, [i32, i32, i32, i32]),
         "moe_permute": (i32, [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]),
+        "moe_route_permute": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moe_weight_field_bytes": (sz, [ctypes.POINTER(WDesc), i32]),
         "moe_repack_weights": (i32, [ctypes.POINTER(WDesc), ctypes.POINTER(WDesc), vp]),
         "moe_grouped_qgemm_workspace_size": (sz, [ctypes.POINTER(WDesc), i32, i32]),
@@ -145,7 +146,7 @@ def moe_permute(ids: torch.Tensor, E: int, pair_bits: torch.Tensor = None, x: to
             seg_offsets=torch.empty(E * S + 1, dtype=torch.int32, device=dev),
             sorted_pair=torch.empty(T * k, dtype=torch.int32, device=dev),
             pair_pos=torch.empty(T * k, dtype=torch.int32, device=dev),
-            workspace=torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev),
+            workspace=torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev),
             x_perm=(torch.empty((T * k, x.shape[1]), dtype=x.dtype, device=dev) if want_x_perm else None),
         )
     H = x.shape[1] if x is not None else 0
@@ -153,6 +154,30 @@ def moe_permute(ids: torch.Tensor, E: int, pair_bits: torch.Tensor = None, x: to
                              _ptr(out.sorted_pair), _ptr(out.pair_pos), _ptr(x), H, _ptr(out.x_perm),
                              _ptr(out.workspace), out.workspace.numel(), _stream(stream)), "moe_permute")
     return out
+
+
+def moe_route_permute(logits: torch.Tensor, k: int, pair_bits: torch.Tensor = None, ids: torch.Tensor = None,
+                      w: torch.Tensor = None, out: Permutation = None, stream=None):
+    """Routing + grouping in one call (one launch for small batches); returns (ids, w, Permutation).
+    The Permutation's workspace must start zero-filled (as allocated here and by moe_permute)."""
+    assert logits.dtype == torch.float32 and logits.dim() == 2
+    T, E = logits.shape
+    dev = logits.device
+    S = 3 if pair_bits is not None else 1
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev) if ids is None else ids
+    w = torch.empty((T, k), dtype=torch.float32, device=dev) if w is None else w
+    if out is None:
+        ws_bytes = lib().moe_permute_workspace_size(T, k, E, S)
+        out = Permutation(
+            counts=torch.empty(E, dtype=torch.int32, device=dev),
+            seg_offsets=torch.empty(E * S + 1, dtype=torch.int32, device=dev),
+            sorted_pair=torch.empty(T * k, dtype=torch.int32, device=dev),
+            pair_pos=torch.empty(T * k, dtype=torch.int32, device=dev),
+            workspace=torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev))
+    _check(lib().moe_route_permute(_ptr(logits), T, E, k, _ptr(pair_bits), _ptr(ids), _ptr(w), _ptr(out.counts),
+                                   _ptr(out.seg_offsets), _ptr(out.sorted_pair), _ptr(out.pair_pos),
+                                   _ptr(out.workspace), out.workspace.numel(), _stream(stream)), "moe_route_permute")
+    return ids, w, out
 
 
 @dataclass
@@ -279,7 +304,7 @@ def alloc_layer(T: int, E: int, k: int, H: int, I: int, mwq: bool, device) -> La
         seg_offsets=torch.empty(E * S + 1, dtype=torch.int32, device=device),
         sorted_pair=torch.empty(T * k, dtype=torch.int32, device=device),
         pair_pos=torch.empty(T * k, dtype=torch.int32, device=device),
-        workspace=torch.empty(max(ws, 16), dtype=torch.uint8, device=device))
+        workspace=torch.zeros(max(ws, 16), dtype=torch.uint8, device=device))
     return LayerBuffers(
         ids=torch.empty((T, k), dtype=torch.int32, device=device),
         w=torch.empty((T, k), dtype=torch.float32, device=device),
@@ -298,8 +323,7 @@ def moe_layer_forward(x: torch.Tensor, logits: torch.Tensor, k: int, gate_up: Qu
     I = gate_up.N // 2
     if buf is None:
         buf = alloc_layer(T, E, k, H, I, pair_bits is not None, x.device)
-    moe_route_topk(logits, k, ids=buf.ids, w=buf.w, stream=stream)
-    moe_permute(buf.ids, E, pair_bits=pair_bits, out=buf.perm, stream=stream)
+    moe_route_permute(logits, k, pair_bits=pair_bits, ids=buf.ids, w=buf.w, out=buf.perm, stream=stream)
     moe_grouped_qgemm(gate_up, x, buf.perm.seg_offsets, T * k, MOE_EPI_SWIGLU, gather_pair=buf.perm.sorted_pair,
                       k=k, out=buf.h, stream=stream)
     moe_grouped_qgemm(down, buf.h, buf.perm.seg_offsets, T * k, MOE_EPI_NONE_F32, out=buf.y_perm, stream=stream)

@@ -178,6 +178,40 @@ moe_status moe_permute(const int32_t* topk_ids, const uint8_t* pair_bits, int32_
   return hip_status(moe::launch_permute(a, (hipStream_t)stream), "permute launch");
 }
 
+moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k, const uint8_t* pair_bits,
+                             int32_t* topk_ids, float* topk_w, int32_t* expert_counts, int32_t* seg_offsets,
+                             int32_t* sorted_pair, int32_t* pair_pos, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (T < 0) return fail(MOE_ERR_BAD_SHAPE, "T=%d < 0", T);
+  if (E < 1 || E > 1024) return fail(MOE_ERR_BAD_SHAPE, "E=%d outside 1..1024", E);
+  if (k < 1 || k > E) return fail(MOE_ERR_BAD_SHAPE, "k=%d outside 1..E (E=%d)", k, E);
+  if ((int64_t)T * k >= ((int64_t)1 << 31)) return fail(MOE_ERR_BAD_SHAPE, "T*k too large");
+  const int S = pair_bits ? 3 : 1;
+  if (!expert_counts || !seg_offsets || !workspace) return fail(MOE_ERR_NULL_ARG, "counts, offsets and workspace are required");
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !sorted_pair || !pair_pos))
+    return fail(MOE_ERR_NULL_ARG, "logits, ids, gates, sorted_pair and pair_pos are required");
+  const size_t need = moe::permute_workspace_bytes(T * k, E, S);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, %zu needed", workspace_bytes, need);
+  if (!aligned(workspace, 16)) return fail(MOE_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  if (T > 0 && (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)))
+    return fail(MOE_ERR_MISALIGNED, "route buffers must be 4-byte aligned");
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  if (T > 0 && moe::route_permute_fusable(T, k, E))
+    return hip_status(moe::launch_route_permute(logits, T, E, k, pair_bits, topk_ids, topk_w, expert_counts,
+                                                seg_offsets, sorted_pair, pair_pos, workspace, s),
+                      "route_permute launch");
+  if (T > 0) {
+    st = hip_status(moe::launch_route_topk(logits, T, E, k, topk_ids, topk_w, s), "route_topk launch");
+    if (st != MOE_OK) return st;
+  }
+  moe::PermuteArgs a{topk_ids, pair_bits, T * k, k, E, S, expert_counts, seg_offsets, sorted_pair, pair_pos,
+                     nullptr, 0, nullptr, workspace};
+  return hip_status(moe::launch_permute(a, s), "permute launch");
+}
+
 size_t moe_weight_field_bytes(const moe_wdesc* w, int32_t field) {
   if (check_desc(w, w ? w->layout : 0, false) != MOE_OK) return 0;
   const size_t ENK = (size_t)w->E * w->N * w->K;

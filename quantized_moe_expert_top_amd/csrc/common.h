@@ -126,6 +126,11 @@ struct PermuteArgs {
 };
 size_t permute_workspace_bytes(int P, int E, int S);
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+// Routing + grouping in one launch (E <= 64 experts, T*k <= 4096 pairs).
+bool route_permute_fusable(int T, int k, int E);
+hipError_t launch_route_permute(const float* logits, int T, int E, int k, const uint8_t* bits, int32_t* ids,
+                                float* w, int32_t* counts, int32_t* seg_offsets, int32_t* sorted_pair,
+                                int32_t* pair_pos, void* ws, hipStream_t s);
 
 
 hipError_t launch_combine(const void* y, bool y_f32, const int32_t* pos, const float* w, int T, int k, int H,

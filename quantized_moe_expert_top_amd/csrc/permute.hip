@@ -133,6 +133,35 @@ __device__ void scatter_chunk(const Keyer& kr, int p0, int p1, int* base, int* t
   }
 }
 
+// All three phases in one workgroup of NT threads.  hist: NK+1 ints,
+// tagbuf: NT/64 * (NK+1) ints, scratch: NT/64 + 1 ints (all LDS).
+template <int NT>
+__device__ void permute_block(const Keyer& kr, int P, int32_t* counts, int32_t* seg_offsets, int32_t* sorted_pair,
+                              int32_t* pair_pos, uint32_t* flag, int* hist, int* tagbuf, int* scratch,
+                              uint32_t* sbad) {
+  const int tid = threadIdx.x;
+  const int nk1 = kr.NK + 1;
+  for (int i = tid; i < nk1; i += NT) hist[i] = 0;
+  for (int i = tid; i < (NT / 64) * nk1; i += NT) tagbuf[i] = -1;  // tag 0xffff never matches step 0..
+  if (tid == 0) *sbad = 0;
+  __syncthreads();
+  uint32_t bad = 0;
+  for (int p = tid; p < P; p += NT) atomicAdd(&hist[kr.key(p, bad)], 1);
+  if (bad) atomicOr(sbad, 1u);
+  __syncthreads();
+  for (int e = tid; e < kr.E; e += NT) {
+    int c = 0;
+    for (int s = 0; s < kr.S; ++s) c += hist[e * kr.S + s];
+    counts[e] = c;
+  }
+  __syncthreads();
+  block_exclusive_scan<NT>(hist, nk1, scratch);
+  for (int i = tid; i < nk1; i += NT) seg_offsets[i] = hist[i];
+  if (tid == 0) flag[0] = *sbad;
+  __syncthreads();
+  scatter_chunk<NT>(kr, 0, P, hist, tagbuf, sorted_pair, pair_pos);
+}
+
 __global__ __launch_bounds__(kThreads) void permute_small_kernel(Keyer kr, int P, int32_t* counts,
                                                                  int32_t* seg_offsets, int32_t* sorted_pair,
                                                                  int32_t* pair_pos, uint32_t* flag) {
@@ -140,27 +169,44 @@ __global__ __launch_bounds__(kThreads) void permute_small_kernel(Keyer kr, int P
   __shared__ int tagbuf[4 * kMaxKeys];
   __shared__ int scratch[8];
   __shared__ uint32_t sbad;
-  const int tid = threadIdx.x;
-  const int nk1 = kr.NK + 1;
-  for (int i = tid; i < nk1; i += kThreads) hist[i] = 0;
-  for (int i = tid; i < 4 * nk1; i += kThreads) tagbuf[i] = -1;  // tag 0xffff never matches step 0..
-  if (tid == 0) sbad = 0;
-  __syncthreads();
-  uint32_t bad = 0;
-  for (int p = tid; p < P; p += kThreads) atomicAdd(&hist[kr.key(p, bad)], 1);
-  if (bad) atomicOr(&sbad, 1u);
-  __syncthreads();
-  for (int e = tid; e < kr.E; e += kThreads) {
-    int c = 0;
-    for (int s = 0; s < kr.S; ++s) c += hist[e * kr.S + s];
-    counts[e] = c;
+  permute_block<kThreads>(kr, P, counts, seg_offsets, sorted_pair, pair_pos, flag, hist, tagbuf, scratch, &sbad);
+}
+
+// Routing and grouping of a small batch in one launch: every workgroup routes
+// 4 tokens (one wavefront each, the rank method of the routing kernel), makes
+// its ids visible device-wide and counts itself in; the last workgroup to
+// arrive groups all pairs and resets the counter.  Outputs are identical to
+// moe_route_topk followed by moe_permute.
+constexpr int kRPMaxE = 64, kRPMaxKeys = 3 * kRPMaxE + 1;
+__global__ __launch_bounds__(kThreads) void route_permute_kernel(const float* __restrict__ logits, int T, int E,
+                                                                 int k, const uint8_t* bits, int32_t* ids, float* w,
+                                                                 int32_t* counts, int32_t* seg_offsets,
+                                                                 int32_t* sorted_pair, int32_t* pair_pos,
+                                                                 uint32_t* ws) {
+  __shared__ float sel_val[4][64];
+  __shared__ double sel_exp[4][64];
+  __shared__ int hist[kRPMaxKeys];
+  __shared__ int tagbuf[4 * kRPMaxKeys];
+  __shared__ int scratch[8];
+  __shared__ uint32_t sbad;
+  __shared__ int last;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wv;
+  if (t < T) {
+    const float v = lane < E ? logits[(size_t)t * E + lane] : -__builtin_inff();
+    route_token_rank(v, E, k, ids + (size_t)t * k, w + (size_t)t * k, sel_val[wv], sel_exp[wv], nullptr);
   }
+  __threadfence();  // release this workgroup's ids and gates device-wide
   __syncthreads();
-  block_exclusive_scan<kThreads>(hist, nk1, scratch);
-  for (int i = tid; i < nk1; i += kThreads) seg_offsets[i] = hist[i];
-  if (tid == 0) flag[0] = sbad;
+  uint32_t* counter = ws + 1;  // ws[0] is the invalid-id flag
+  if (threadIdx.x == 0) last = atomicAdd(counter, 1u) == gridDim.x - 1;
   __syncthreads();
-  scatter_chunk<kThreads>(kr, 0, P, hist, tagbuf, sorted_pair, pair_pos);
+  if (!last) return;
+  __threadfence();  // acquire every workgroup's ids
+  const int S = bits ? 3 : 1;
+  const Keyer kr{ids, bits, E, S, E * S};
+  permute_block<kThreads>(kr, T * k, counts, seg_offsets, sorted_pair, pair_pos, ws, hist, tagbuf, scratch, &sbad);
+  if (threadIdx.x == 0) *counter = 0u;  // ready for the next call
 }
 
 // ---- multi-block path -------------------------------------------------------
@@ -249,6 +295,16 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(const uint16_t* _
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 }  // namespace
+
+bool route_permute_fusable(int T, int k, int E) { return E <= kRPMaxE && (int64_t)T * k <= kSmallMax; }
+
+hipError_t launch_route_permute(const float* logits, int T, int E, int k, const uint8_t* bits, int32_t* ids,
+                                float* w, int32_t* counts, int32_t* seg_offsets, int32_t* sorted_pair,
+                                int32_t* pair_pos, void* ws, hipStream_t s) {
+  hipLaunchKernelGGL(route_permute_kernel, dim3((unsigned)((T + 3) / 4)), dim3(kThreads), 0, s, logits, T, E, k, bits,
+                     ids, w, counts, seg_offsets, sorted_pair, pair_pos, static_cast<uint32_t*>(ws));
+  return hipGetLastError();
+}
 
 size_t permute_workspace_bytes(int P, int E, int S) {
   const size_t nk1 = (size_t)E * S + 1;

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     names = declared_functions()
-    for n in ("moe_route_topk", "moe_permute", "moe_grouped_qgemm", "moe_unpermute_combine",
+    for n in ("moe_route_topk", "moe_permute", "moe_route_permute", "moe_grouped_qgemm", "moe_unpermute_combine",
               "moe_repack_weights", "moe_permute_workspace_size"):
         assert n in names
     assert set(names) == set(q.EXPORTED)
@@ -80,6 +80,20 @@ def test_permute_validation(lib):
     # x_perm requested without x / with bad H
     assert lib.moe_permute(A, None, 16, 2, 8, A, A, A, A, None, 64, A, A, 1 << 20, None) == NULL_ARG
     assert lib.moe_permute(A, None, 16, 2, 8, A, A, A, A, A, 12, A, A, 1 << 20, None) == BAD_SHAPE
+
+
+def test_route_permute_validation(lib):
+    A = fake(0x1000)
+    need = lib.moe_permute_workspace_size(32, 8, 64, 1)
+    args = lambda T=32, E=64, k=8, ws=A, ws_bytes=need: (A, T, E, k, None, A, A, A, A, A, A, ws, ws_bytes, None)  # noqa: E731
+    assert lib.moe_route_permute(*args(T=-1)) == BAD_SHAPE
+    assert lib.moe_route_permute(*args(E=2000)) == BAD_SHAPE
+    assert lib.moe_route_permute(*args(k=65)) == BAD_SHAPE
+    assert lib.moe_route_permute(*args(ws_bytes=need - 1)) == WS_SMALL
+    assert lib.moe_route_permute(*args(ws=None)) == NULL_ARG
+    assert lib.moe_route_permute(*args(ws=fake(0x1004))) == MISALIGNED
+    assert lib.moe_route_permute(None, 32, 64, 8, None, A, A, A, A, A, A, A, need, None) == NULL_ARG
+    assert lib.moe_route_permute(fake(0x1002), 32, 64, 8, None, A, A, A, A, A, A, A, need, None) == MISALIGNED
 
 
 def desc(fmt=q.MOE_W_INT4_GROUP, layout=q.MOE_LAYOUT_TILED, E=8, N=256, K=512, G=128, z=8, ns=0, **ptrs):

@@ -85,6 +85,32 @@ def test_permute_flags_invalid_ids(G):
     assert p.counts.cpu().numpy().sum() == 5
 
 
+@pytest.mark.parametrize("T,E,k,mwq", [(1, 8, 2, False), (32, 64, 8, False), (64, 64, 8, True), (512, 8, 8, False),
+                                        (513, 8, 8, False), (300, 128, 4, True)])
+def test_route_permute_matches_oracle(G, T, E, k, mwq):
+    """One-call routing + grouping: a single launch when E <= 64 and T*k <= 4096
+    (the last workgroup groups), two launches otherwise; called twice on one
+    workspace, so the arrival counter must come back to zero."""
+    rng = np.random.default_rng(T * 31 + E + k)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, 3 % E] = logits[:, 1 % E]                      # exact ties
+    bits = rng.integers(2, 5, size=T * k).astype(np.uint8) if mwq else None
+    rid, rw = oracle.route_topk(logits.astype(np.float64), k)
+    counts, offsets, sorted_pair, pair_pos = oracle.permute(rid, E, pair_bits=bits)
+    p = None
+    for _ in range(2):
+        ids, w, p = G.q.moe_route_permute(G.t(logits), k, pair_bits=None if bits is None else G.t(bits), out=p)
+        torch.cuda.synchronize()
+        assert np.array_equal(ids.cpu().numpy(), rid)
+        np.testing.assert_allclose(w.cpu().numpy().astype(np.float64), rw, rtol=G.GATE_RTOL, atol=0)
+        assert np.array_equal(p.counts.cpu().numpy(), counts)
+        assert np.array_equal(p.seg_offsets.cpu().numpy(), offsets)
+        assert np.array_equal(p.sorted_pair.cpu().numpy(), sorted_pair)
+        assert np.array_equal(p.pair_pos.cpu().numpy(), pair_pos)
+        flag_and_counter = p.workspace[:8].view(torch.int32).cpu().numpy()
+        assert flag_and_counter[0] == 0 and flag_and_counter[1] == 0
+
+
 # --------------------------------------------------------------- full layers
 def _layer_parity(G, cfg, tokens=None):
     d = gen.generate(cfg)
