@@ -280,6 +280,7 @@ moe_status moe_grouped_qgemm(const moe_wdesc* w, const uint16_t* A, int32_t A_ro
   if (workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, %zu needed", workspace_bytes, need);
   if (need && !workspace) return fail(MOE_ERR_NULL_ARG, "workspace is NULL");
+  if (need && !aligned(workspace, 16)) return fail(MOE_ERR_MISALIGNED, "workspace must be 16-byte aligned");
   st = check_device();
   if (st != MOE_OK) return st;
   if ((int64_t)A_rows * w->K * 2 >= ((int64_t)1 << 32))

@@ -741,6 +741,243 @@ __global__ __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) void qgemm_p_kernel(KA
   }
 }
 
+// ------------------------------------------------------- prefill, LDS-DMA
+// INT4 with many rows per segment.  One workgroup of 8 wavefronts per
+// (128-row tile, 256-channel block); wavefront (wm, wn) owns 64 rows x 4
+// channel tiles, so every activation fragment read from LDS feeds 4 MFMAs and
+// every dequantised weight fragment 4.  Activations, weight codes and the
+// activation row sums of each K block go straight from memory into one of
+// three LDS stages (global_load_lds, no register staging), two blocks ahead
+// of the block being multiplied: each wavefront waits for its own loads with
+// an explicit vmcnt, and one barrier per K block publishes the stage to the
+// others and retires the stage the next loads overwrite.  The group scales
+// (two bytes per channel and group) come through registers.  The row sums are
+// those of the bias correction, -(128 + z) * sum_k a_k per scale group,
+// written by rowsum_kernel into the workspace.
+constexpr int kP2Threads = 512, kP2Rows = 128;
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));  // expcnt, lgkmcnt: no wait
+}
+
+// out[row][g] = -(128 + z) * (sum of the bf16 values of group g of A's row);
+// one wavefront per row, lane l sums 16-byte chunks l, l + 64, ...
+__global__ __launch_bounds__(256) void rowsum_kernel(const uint16_t* __restrict__ A, int rows, int K, int G,
+                                                     float negz, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(A + (size_t)row * K);
+  const int nch = K / 8, cpg = G / 8, ng = K / G;
+  for (int c0 = 0; c0 < nch; c0 += 64) {
+    const int c = c0 + lane;
+    float s = 0.f;
+    if (c < nch) {
+      const u32x4 v = src[c];
+      const uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
+      s = add_bf16_pair(w3, add_bf16_pair(w2, add_bf16_pair(w1, add_bf16_pair(w0, s))));
+    }
+    for (int o = 1; o < cpg; o <<= 1) s += __shfl_xor(s, o, 64);
+    if (c < nch && (lane & (cpg - 1)) == 0) out[(size_t)row * ng + c / cpg] = s * negz;
+  }
+}
+
+struct __attribute__((aligned(16))) P2Stage {
+  u32x4 a[8][4][64];  // activations [row tile][MFMA step][lane], 32 KB
+  u32x4 b[16][64];    // codes [workgroup tile][lane], 16 KB
+  float r[512];       // row sums [group][row] (+ padding), 2 KB
+};
+
+template <int EPI, int GPB>
+__global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const float* __restrict__ rowsum, int n_nblk,
+                                                              int n_mt, int GM) {
+  constexpr int RT = 4, UT = 4, SPG = 4 / GPB;
+  constexpr int V = 7 + UT * GPB;  // vector-memory instructions per K block and wavefront
+  // one object per stage: the compiler tracks outstanding LDS-DMA writes per
+  // LDS object, and only a few objects at a time
+  __shared__ P2Stage st0, st1, st2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = uniform(tid >> 6), wm = wv >> 2, wn = wv & 3;
+
+  const int per_xcd = gridDim.x / 8;
+  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  const int grp = item / (GM * n_nblk), rem = item % (GM * n_nblk);
+  const int nb = rem / GM, mt = grp * GM + rem % GM;
+  if (mt >= n_mt) return;
+  int seg, m0;
+  if (!find_tile(p.seg_offsets, p.nseg, mt, seg, m0, kP2Rows)) return;
+  const Ctx c{uniform(p.seg_offsets[seg] + m0), uniform(min(kP2Rows, p.seg_offsets[seg + 1] - p.seg_offsets[seg] - m0)),
+              uniform(seg), 4};
+  const int KB = p.K / 128, NT = p.N / 16;
+
+  // workgroup tile j = 4 * (consumer wavefront wn) + u; SwiGLU: u = 0, 1 gate, 2, 3 up
+  auto wg_tile = [&](int j, bool& valid) -> int {
+    const int w4 = j >> 2, u = j & 3;
+    int t;
+    if (EPI == 1) {
+      const int hch = nb * 128 + 32 * w4 + 16 * (u & 1);
+      t = (u < 2 ? 0 : NT / 2) + hch / 16;
+      valid = hch < p.N / 2;
+    } else {
+      t = nb * 16 + j;
+      valid = t < NT;
+    }
+    return valid ? t : 0;  // invalid tiles load tile 0 and are never stored
+  };
+
+  // loads issued by this wavefront: activation row tile wv (4 steps), workgroup
+  // tiles 2wv, 2wv + 1, row-sum entries 64wv .. 64wv + 63.  Buffer loads: the
+  // per-lane offset stays fixed and each K block only moves the scalar offset.
+  const rsrc_t ar = make_rsrc(p.A, p.A_bytes);
+  const uint32_t a_off = (uint32_t)(src_row(p, c, 16 * wv + (lane & 15)) * (size_t)p.K * 2 + 16 * (lane >> 4));
+  rsrc_t br[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    bool v;
+    const int t = wg_tile(2 * wv + q, v);
+    br[q] = make_rsrc(p.codes + ((size_t)c.e * NT + t) * (size_t)KB * 1024, KB * 1024);
+  }
+  const int ng = KB * GPB;
+  const int en = 64 * wv + lane;
+  const bool ren = en < 128 * GPB;
+  const rsrc_t rr = make_rsrc(rowsum, (p.A_bytes / (2u * p.K)) * ng * 4);
+  const uint32_t r_off = (uint32_t)((src_row(p, c, ren ? (en & 127) : 0) * (size_t)ng + (ren ? (en >> 7) : 0)) * 4);
+
+  // this wavefront's own tiles (consumer side): scales and stores
+  int ct[UT];
+  bool cval[UT];
+#pragma unroll
+  for (int u = 0; u < UT; ++u) ct[u] = wg_tile(4 * wn + u, cval[u]);
+  rsrc_t sr[UT];
+#pragma unroll
+  for (int u = 0; u < UT; ++u) sr[u] = make_rsrc(p.scales + ((size_t)c.e * NT + ct[u]) * 16 * (size_t)ng, 16 * ng * 2);
+  const uint32_t soff = (uint32_t)((lane & 15) * ng * 2);
+
+  f32x4 acc[RT][UT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int u = 0; u < UT; ++u) acc[rt][u] = f32x4{};
+  uint32_t rsc[3][UT][GPB];  // one register per scale: packing two would wait for both loads
+
+#define P2_ISSUE(S, ST, KBI)                                                                           \
+  {                                                                                                    \
+    const int kbi = (KBI);                                                                             \
+    /* offsets go in the scalar operand: the immediate one would move the LDS address too */          \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, &ST.a[wv][0][0], 16, a_off, kbi * 256, 0, 0);        \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, &ST.a[wv][1][0], 16, a_off, kbi * 256 + 64, 0, 0);   \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, &ST.a[wv][2][0], 16, a_off, kbi * 256 + 128, 0, 0);  \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, &ST.a[wv][3][0], 16, a_off, kbi * 256 + 192, 0, 0);  \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(br[0], &ST.b[2 * wv][0], 16, 16 * lane, kbi * 1024, 0, 0); \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(br[1], &ST.b[2 * wv + 1][0], 16, 16 * lane, kbi * 1024, 0, 0); \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, &ST.r[64 * wv], 4, r_off, kbi * GPB * 4, 0, 0);       \
+    _Pragma("unroll") for (int u = 0; u < UT; ++u) _Pragma("unroll") for (int g = 0; g < GPB; ++g)     \
+        rsc[S][u][g] = buf_u16(sr[u], soff, (kbi * GPB + g) * 2);                                      \
+  }
+// Per scale group: the correction (row sums) is the C input of the first
+// MFMA of each chain; the activation fragments of the next MFMA step are read
+// from LDS while the current step's MFMAs run.
+#define P2_COMPUTE(S, ST)                                                                                  \
+  {                                                                                                        \
+    _Pragma("unroll") for (int g = 0; g < GPB; ++g) {                                                      \
+      f32x4 rv[RT];                                                                                        \
+      _Pragma("unroll") for (int rt = 0; rt < RT; ++rt)                                                    \
+          rv[rt] = *reinterpret_cast<const f32x4*>(&ST.r[g * 128 + 64 * wm + 16 * rt + 4 * (lane >> 4)]); \
+      u32x4 av[2][RT];                                                                                     \
+      _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) av[0][rt] = ST.a[4 * wm + rt][g * SPG][lane];      \
+      f32x4 tmp[RT][UT];                                                                                   \
+      _Pragma("unroll") for (int tt = 0; tt < SPG; ++tt) {                                                 \
+        const int t = g * SPG + tt;                                                                        \
+        if (tt + 1 < SPG) {                                                                                \
+          _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) av[(tt + 1) & 1][rt] = ST.a[4 * wm + rt][t + 1][lane]; \
+          __builtin_amdgcn_sched_barrier(0); /* keep these reads ahead of this step's MFMAs */              \
+        }                                                                                                  \
+        bf16x8 bv[UT];                                                                                     \
+        _Pragma("unroll") for (int u = 0; u < UT; ++u) bv[u] = deq_u4(cb[u], t);                           \
+        _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                                \
+          const bf16x8 a = as_bf16x8(av[tt & 1][rt]);                                                      \
+          _Pragma("unroll") for (int u = 0; u < UT; ++u)                                                   \
+              tmp[rt][u] = mfma16(a, bv[u], tt == 0 ? rv[rt] : tmp[rt][u]);                                \
+        }                                                                                                  \
+      }                                                                                                    \
+      _Pragma("unroll") for (int u = 0; u < UT; ++u) {                                                     \
+        const float sv = f16_to_f32((uint16_t)rsc[S][u][g]);                                               \
+        _Pragma("unroll") for (int rt = 0; rt < RT; ++rt)                                                  \
+            _Pragma("unroll") for (int r = 0; r < 4; ++r) acc[rt][u][r] = __builtin_fmaf(sv, tmp[rt][u][r], acc[rt][u][r]); \
+      }                                                                                                    \
+    }                                                                                                      \
+  }
+  // Block i sits in stage i % 3.  Before block i this wavefront waits for its
+  // own loads of block i, and the barrier makes every wavefront's loads
+  // visible and retires stage (i - 1) % 3, into which block i + 2 is then
+  // issued.  Each step reads its codes before issuing: at the loop header the
+  // compiler loses track of which stage the loads in flight write and waits
+  // for all of them before the first LDS read, which is then only block i + 1.
+#define P2_READY(I)                  \
+  {                                  \
+    __builtin_amdgcn_sched_barrier(0); \
+    if ((I) + 1 < KB) vm_wait<V>();  \
+    else vm_wait<0>();               \
+    __builtin_amdgcn_s_barrier();    \
+  }
+#define P2_STEP(J, CS, IS, I)                                                       \
+  {                                                                                 \
+    u32x4 cb[UT];                                                                   \
+    _Pragma("unroll") for (int u = 0; u < UT; ++u) cb[u] = CS.b[4 * wn + u][lane];  \
+    if ((I) + 2 < KB) P2_ISSUE(((J) + 2) % 3, IS, (I) + 2);                         \
+    P2_COMPUTE(J, CS);                                                              \
+  }
+
+  P2_ISSUE(0, st0, 0);
+  if (1 < KB) P2_ISSUE(1, st1, 1);
+  P2_READY(0)
+  for (int kb0 = 0; kb0 < KB; kb0 += 3) {
+    P2_STEP(0, st0, st2, kb0)
+    if (kb0 + 1 < KB) {
+      P2_READY(kb0 + 1)
+      P2_STEP(1, st1, st0, kb0 + 1)
+    }
+    if (kb0 + 2 < KB) {
+      P2_READY(kb0 + 2)
+      P2_STEP(2, st2, st1, kb0 + 2)
+    }
+    if (kb0 + 3 < KB) P2_READY(kb0 + 3)
+  }
+#undef P2_STEP
+#undef P2_READY
+#undef P2_COMPUTE
+#undef P2_ISSUE
+
+  const int col = lane & 15;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 64 * wm + 16 * rt + 4 * (lane >> 4) + r;
+      if (row >= c.rows) continue;
+      if (EPI == 1) {
+        uint16_t* orow = static_cast<uint16_t*>(p.out) + (size_t)(c.row0 + row) * p.n_out;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (!cval[h]) continue;
+          const float g = acc[rt][h][r], up = acc[rt][h + 2][r];
+          orow[nb * 128 + 32 * wn + 16 * h + col] = f32_to_bf16(g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * up);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < UT; ++u) {
+          if (!cval[u]) continue;
+          const size_t o = (size_t)(c.row0 + row) * p.n_out + ct[u] * 16 + col;
+          if (EPI == 2) static_cast<float*>(p.out)[o] = acc[rt][u][r];
+          else static_cast<uint16_t*>(p.out)[o] = f32_to_bf16(acc[rt][u][r]);
+        }
+      }
+    }
+  }
+}
+
 template <int FMT, int EPI>
 void launch_d(const KArgs& ka, int n_cg, int n_rt, hipStream_t s) {
   const int items = n_cg * n_rt;
@@ -778,9 +1015,33 @@ void launch_p(const KArgs& ka, int M_total, hipStream_t s) {
   }
 }
 
-// path: 0 = small-row-tile kernel, 64 / 128 = large-row-tile kernel with that tile height
 template <int EPI>
-void launch_epi(const KArgs& ka, int fmt, int path, int M_total, hipStream_t s) {
+void launch_p2(const KArgs& ka, const float* rowsum, int M_total, hipStream_t s) {
+  const int n_nblk = EPI == 1 ? (ka.N / 2 + 127) / 128 : (ka.N + 255) / 256;
+  const int n_mt = (M_total + kP2Rows - 1) / kP2Rows + ka.nseg;
+  const int GM = group_rows(ka, M_total, n_mt, kP2Rows, 1);
+  const int items = n_nblk * ((n_mt + GM - 1) / GM) * GM;
+  const dim3 grid((unsigned)(((items + 7) / 8) * 8));
+  const dim3 block(kP2Threads);
+  switch (ka.G) {
+    case 128: hipLaunchKernelGGL((qgemm_p2_kernel<EPI, 1>), grid, block, 0, s, ka, rowsum, n_nblk, n_mt, GM); break;
+    case 64: hipLaunchKernelGGL((qgemm_p2_kernel<EPI, 2>), grid, block, 0, s, ka, rowsum, n_nblk, n_mt, GM); break;
+    default: hipLaunchKernelGGL((qgemm_p2_kernel<EPI, 4>), grid, block, 0, s, ka, rowsum, n_nblk, n_mt, GM); break;
+  }
+}
+
+// path: 0 = small-row-tile kernel, 64 / 128 = large-row-tile kernel with that
+// tile height, 2 = 128-row LDS-DMA kernel (INT4; row sums in `ws`)
+template <int EPI>
+void launch_epi(const KArgs& ka, int fmt, int path, int M_total, int A_rows, void* ws, hipStream_t s) {
+  if (path == 2) {
+    float* rs = static_cast<float*>(ws);
+    const int rows = A_rows;
+    hipLaunchKernelGGL(rowsum_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, ka.A, rows, ka.K, ka.G,
+                       -(128.0f + (float)ka.z), rs);
+    launch_p2<EPI>(ka, rs, M_total, s);
+    return;
+  }
   if (fmt != 3 && path != 0) {
     // 64 rows per workgroup; 8 wavefront columns (wide channel blocks: the
     // activations are read fewer times) when the activations outweigh the
@@ -813,23 +1074,29 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, hipStream_t s) 
   else launch_d<2, EPI>(ka, gx, n_rt, s);
 }
 
-// Row-tile height from the mean rows per segment (the host never sees the
-// device counts): few rows per segment -> 16-row tiles (decode kernel); many
-// -> 64-row tiles (two workgroups per CU; the 128-row, one-per-CU variant
-// measured slower).  MOE_QGEMM_PATH=small|64|128 forces a path.
-int pick_path(int M_total, int nseg) {
+// Kernel from the mean rows per segment (the host never sees the device
+// counts): few rows per segment -> 16-row tiles (decode kernel); many -> the
+// 128-row LDS-DMA kernel for INT4, 64-row tiles otherwise (and for INT4
+// segments of under ~96 rows, where 128-row tiles would be mostly padding).
+// MOE_QGEMM_PATH=small|64|64n|128|dma forces a path.
+int pick_path(int M_total, int nseg, int fmt) {
   if (const char* f = getenv("MOE_QGEMM_PATH")) {
     if (!strcmp(f, "small")) return 0;
     if (!strcmp(f, "64")) return 64;
     if (!strcmp(f, "64n")) return 65;
     if (!strcmp(f, "128")) return 128;
+    if (!strcmp(f, "dma") && fmt == 1) return 2;
   }
   const double avg = (double)M_total / (double)(nseg > 0 ? nseg : 1);
-  return avg < 24.0 ? 0 : 64;
+  if (avg < 24.0) return 0;
+  return (fmt == 1 && avg >= 96.0) ? 2 : 64;
 }
 }  // namespace
 
-size_t qgemm_workspace_bytes(const QWeights&, int, int) { return 0; }
+size_t qgemm_workspace_bytes(const QWeights& w, int A_rows, int M_total) {
+  if (w.fmt != 1 || pick_path(M_total, w.E, w.fmt) != 2) return 0;
+  return ((size_t)A_rows * (w.K / w.G) * 4 + 255) & ~(size_t)255;
+}
 
 hipError_t launch_qgemm(const QGemmArgs& a, hipStream_t s) {
   if (a.M_total == 0) return hipSuccess;
@@ -858,10 +1125,10 @@ hipError_t launch_qgemm(const QGemmArgs& a, hipStream_t s) {
   const bool swiglu = a.epilogue == 1;
   ka.n_out = swiglu ? w.N / 2 : w.N;
   (void)swiglu;
-  const int path = pick_path(a.M_total, a.nseg);
-  if (a.epilogue == 1) launch_epi<1>(ka, w.fmt, path, a.M_total, s);
-  else if (a.epilogue == 2) launch_epi<2>(ka, w.fmt, path, a.M_total, s);
-  else launch_epi<0>(ka, w.fmt, path, a.M_total, s);
+  const int path = pick_path(a.M_total, a.nseg, w.fmt);
+  if (a.epilogue == 1) launch_epi<1>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, s);
+  else if (a.epilogue == 2) launch_epi<2>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, s);
+  else launch_epi<0>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, s);
   return hipGetLastError();
 }
 

@@ -138,6 +138,23 @@ def test_grouped_qgemm_validation(lib):
     assert gemm(lib, desc(), M=0, A=0, seg=0, out=0) == OK           # empty problem
 
 
+def test_grouped_qgemm_workspace(lib):
+    # many rows per expert (INT4): the 128-row kernel keeps activation row sums in the workspace
+    d = desc(E=8, N=256, K=512, G=128)
+    need = lib.moe_grouped_qgemm_workspace_size(ctypes.byref(d), 4096, 8192)
+    assert need == 4096 * (512 // 128) * 4
+    assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(d), 32, 64) == 0          # decode-sized: none
+    mwq = desc(fmt=q.MOE_W_MWQ_2_3_4, E=8, N=256, K=512, G=128)
+    assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(mwq), 4096, 8192) == 0
+    call = lambda ws, nbytes: lib.moe_grouped_qgemm(ctypes.byref(d), fake(0x1000), 4096, fake(0x2000), 2,  # noqa
+                                                    fake(0x3000), 8192, q.MOE_EPI_SWIGLU, fake(0x4000), ws, nbytes,
+                                                    None)
+    assert call(None, 0) == WS_SMALL
+    assert call(fake(0x5000), need - 1) == WS_SMALL
+    assert call(None, need) == NULL_ARG
+    assert call(fake(0x5008), need) == MISALIGNED
+
+
 def test_weight_field_bytes_and_nested_storage(lib):
     H, I, E, G = 4096, 14336, 8, 128
     mwq = desc(fmt=q.MOE_W_MWQ_2_3_4, layout=q.MOE_LAYOUT_CANONICAL, E=E, N=2 * I, K=H, G=G)

@@ -173,6 +173,20 @@ def test_layer_prefill_zipf_sampled(G):
     _layer_parity(G, cfg, tokens=np.sort(tokens))
 
 
+@pytest.mark.parametrize("over", [
+    dict(T=300, E=4, k=2, H=256, I=512, G=64, seed=61),     # 2 scale groups per K block
+    dict(T=200, E=6, k=2, H=384, I=384, G=32, seed=62),     # 4 groups; 3 K blocks; half-empty channel block
+    dict(T=97, E=8, k=3, H=256, I=256, G=128, seed=63),     # ragged: about 36 rows per expert
+    dict(T=64, E=2, k=1, H=128, I=128, G=128, seed=64),     # a single K block
+    dict(T=150, E=5, k=2, H=1024, I=640, G=128, seed=65),   # 8 / 5 K blocks
+])
+def test_layer_prefill_dma_kernel(G, over, monkeypatch):
+    """The 128-row LDS-DMA kernel forced on small layers (it is chosen by
+    itself for INT4 segments of about 96 rows and more)."""
+    monkeypatch.setenv("MOE_QGEMM_PATH", "dma")
+    _layer_parity(G, gen.config("tiny", **over))
+
+
 def test_layer_mwq_small_full(G):
     _layer_parity(G, gen.config("mixtral_mwq", T=96, H=512, I=1024, E=4, k=2, seed=41))
 
