@@ -788,13 +788,19 @@ struct __attribute__((aligned(16))) P2Stage {
   u32x4 a[8][4][64];  // activations [row tile][MFMA step][lane], 32 KB
   u32x4 b[16][64];    // codes [workgroup tile][lane], 16 KB
   float r[512];       // row sums [group][row] (+ padding), 2 KB
+  uint32_t s[512];    // group scales, one dword (two fp16) per channel and group pair, 2 KB
 };
 
-template <int EPI, int GPB>
+// SL: the group scales of each K block travel by LDS-DMA with the block, one
+// aligned dword per channel (and pair of groups), so that the loop issues
+// nothing but LDS-DMA loads.  It needs an even number of groups per channel
+// (K/G); otherwise every K block loads its scales into registers.
+
+template <int EPI, int GPB, bool SL>
 __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const float* __restrict__ rowsum, int n_nblk,
                                                               int n_mt, int GM) {
   constexpr int RT = 4, UT = 4, SPG = 4 / GPB;
-  constexpr int V = 7 + UT * GPB;  // vector-memory instructions per K block and wavefront
+  constexpr int V = SL ? 8 : 7 + UT * GPB;  // vector-memory instructions per K block and wavefront
   // one object per stage: the compiler tracks outstanding LDS-DMA writes per
   // LDS object, and only a few objects at a time
   __shared__ P2Stage st0, st1, st2;
@@ -845,6 +851,19 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
   const rsrc_t rr = make_rsrc(rowsum, (p.A_bytes / (2u * p.K)) * ng * 4);
   const uint32_t r_off = (uint32_t)((src_row(p, c, ren ? (en & 127) : 0) * (size_t)ng + (ren ? (en >> 7) : 0)) * 4);
 
+  // scale entries: dword 64wv + lane of the stage holds, for GPB <= 2,
+  // channel (j, c) = (entry / 16, entry % 16) (entries 256.. are padding, they
+  // reload entry 0), for GPB = 4 the group pair entry % 2 of channel entry / 2
+  const rsrc_t scr = make_rsrc(p.scales, (uint32_t)((size_t)(p.nseg / p.S) * p.N * ng * 2));
+  uint32_t s_off;
+  {
+    const int se = 64 * wv + lane;
+    const int ch = GPB == 4 ? se >> 1 : (se < 256 ? se : 0);
+    bool v;
+    const int t = wg_tile(ch >> 4, v);
+    s_off = (uint32_t)((((size_t)c.e * p.N + t * 16 + (ch & 15)) * ng + (GPB == 4 ? 2 * (se & 1) : 0)) * 2);
+  }
+
   // this wavefront's own tiles (consumer side): scales and stores
   int ct[UT];
   bool cval[UT];
@@ -873,13 +892,39 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
     __builtin_amdgcn_raw_ptr_buffer_load_lds(br[0], &ST.b[2 * wv][0], 16, 16 * lane, kbi * 1024, 0, 0); \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(br[1], &ST.b[2 * wv + 1][0], 16, 16 * lane, kbi * 1024, 0, 0); \
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, &ST.r[64 * wv], 4, r_off, kbi * GPB * 4, 0, 0);       \
+    if (SL)                                                                                            \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(scr, &ST.s[64 * wv], 4, s_off,                          \
+                                               GPB == 1 ? 4 * (kbi >> 1) : 4 * kbi * (GPB / 2), 0, 0); \
     _Pragma("unroll") for (int u = 0; u < UT; ++u) _Pragma("unroll") for (int g = 0; g < GPB; ++g)     \
-        rsc[S][u][g] = buf_u16(sr[u], soff, (kbi * GPB + g) * 2);                                      \
+        if (!SL) rsc[S][u][g] = buf_u16(sr[u], soff, (kbi * GPB + g) * 2);                             \
   }
+// Part Q (0..7) of the loads of block KBI into stage ST: activations step
+// 0..3, the two code tiles, row sums, scales; with register scales (!SL) part
+// 7 loads them into slot S.
+#define P2_PART(S, ST, KBI, Q)                                                                         \
+  {                                                                                                    \
+    const int kbi = (KBI);                                                                             \
+    if ((Q) < 4)                                                                                       \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, &ST.a[wv][(Q) & 3][0], 16, a_off, kbi * 256 + 64 * ((Q) & 3), 0, 0); \
+    else if ((Q) < 6)                                                                                  \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(br[(Q) - 4], &ST.b[2 * wv + (Q) - 4][0], 16, 16 * lane, kbi * 1024, 0, 0); \
+    else if ((Q) == 6)                                                                                 \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, &ST.r[64 * wv], 4, r_off, kbi * GPB * 4, 0, 0);     \
+    else if (SL)                                                                                       \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(scr, &ST.s[64 * wv], 4, s_off,                          \
+                                               GPB == 1 ? 4 * (kbi >> 1) : 4 * kbi * (GPB / 2), 0, 0); \
+    else                                                                                               \
+      _Pragma("unroll") for (int u = 0; u < UT; ++u) _Pragma("unroll") for (int g = 0; g < GPB; ++g)   \
+          rsc[S][u][g] = buf_u16(sr[u], soff, (kbi * GPB + g) * 2);                                    \
+  }
+// With one scale group per K block the eight load instructions of block i + 2
+// are spread over the four MFMA steps of block i (a burst of them right after
+// the barrier kept every wavefront waiting at issue); with more groups they
+// are issued together before the block (spreading them costs registers).
 // Per scale group: the correction (row sums) is the C input of the first
 // MFMA of each chain; the activation fragments of the next MFMA step are read
 // from LDS while the current step's MFMAs run.
-#define P2_COMPUTE(S, ST)                                                                                  \
+#define P2_COMPUTE(S, ST, KBI, DO_ISSUE, IS_, IS, IKB)                                                     \
   {                                                                                                        \
     _Pragma("unroll") for (int g = 0; g < GPB; ++g) {                                                      \
       f32x4 rv[RT];                                                                                        \
@@ -894,6 +939,11 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
           _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) av[(tt + 1) & 1][rt] = ST.a[4 * wm + rt][t + 1][lane]; \
           __builtin_amdgcn_sched_barrier(0); /* keep these reads ahead of this step's MFMAs */              \
         }                                                                                                  \
+        if (DO_ISSUE) {                                                                                    \
+          P2_PART(IS_, IS, IKB, 2 * t)                                                                     \
+          P2_PART(IS_, IS, IKB, 2 * t + 1)                                                                 \
+          __builtin_amdgcn_sched_barrier(0); /* spread the loads over the block's MFMA steps */            \
+        }                                                                                                  \
         bf16x8 bv[UT];                                                                                     \
         _Pragma("unroll") for (int u = 0; u < UT; ++u) bv[u] = deq_u4(cb[u], t);                           \
         _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                                \
@@ -903,7 +953,7 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
         }                                                                                                  \
       }                                                                                                    \
       _Pragma("unroll") for (int u = 0; u < UT; ++u) {                                                     \
-        const float sv = f16_to_f32((uint16_t)rsc[S][u][g]);                                               \
+        const float sv = f16_to_f32(SL ? sc16[u][g] : (uint16_t)rsc[S][u][g]);                             \
         _Pragma("unroll") for (int rt = 0; rt < RT; ++rt)                                                  \
             _Pragma("unroll") for (int r = 0; r < 4; ++r) acc[rt][u][r] = __builtin_fmaf(sv, tmp[rt][u][r], acc[rt][u][r]); \
       }                                                                                                    \
@@ -922,18 +972,61 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
     else vm_wait<0>();               \
     __builtin_amdgcn_s_barrier();    \
   }
+#define P2_READY_U                     \
+  {                                    \
+    __builtin_amdgcn_sched_barrier(0); \
+    vm_wait<V>();                      \
+    __builtin_amdgcn_s_barrier();      \
+  }
+#define P2_STEP_U(J, CS, IS, I)                                                     \
+  {                                                                                 \
+    u32x4 cb[UT];                                                                   \
+    _Pragma("unroll") for (int u = 0; u < UT; ++u) cb[u] = CS.b[4 * wn + u][lane];  \
+    uint16_t sc16[UT][GPB];                                                         \
+    if (SL)                                                                         \
+      _Pragma("unroll") for (int u = 0; u < UT; ++u) _Pragma("unroll") for (int g = 0; g < GPB; ++g) { \
+        const int chn = (4 * wn + u) * 16 + (lane & 15);                            \
+        const uint32_t d = CS.s[GPB == 4 ? 2 * chn + (g >> 1) : chn];              \
+        const int half = GPB == 1 ? ((I) & 1) : (g & 1);                            \
+        sc16[u][g] = (uint16_t)(d >> (16 * half));                                   \
+      }                                                                             \
+    if (GPB != 1) P2_ISSUE(((J) + 2) % 3, IS, (I) + 2);                             \
+    P2_COMPUTE(J, CS, I, GPB == 1, ((J) + 2) % 3, IS, (I) + 2);                     \
+  }
 #define P2_STEP(J, CS, IS, I)                                                       \
   {                                                                                 \
     u32x4 cb[UT];                                                                   \
     _Pragma("unroll") for (int u = 0; u < UT; ++u) cb[u] = CS.b[4 * wn + u][lane];  \
-    if ((I) + 2 < KB) P2_ISSUE(((J) + 2) % 3, IS, (I) + 2);                         \
-    P2_COMPUTE(J, CS);                                                              \
+    uint16_t sc16[UT][GPB];                                                         \
+    if (SL)                                                                         \
+      _Pragma("unroll") for (int u = 0; u < UT; ++u) _Pragma("unroll") for (int g = 0; g < GPB; ++g) { \
+        const int chn = (4 * wn + u) * 16 + (lane & 15);                            \
+        const uint32_t d = CS.s[GPB == 4 ? 2 * chn + (g >> 1) : chn];              \
+        const int half = GPB == 1 ? ((I) & 1) : (g & 1);                            \
+        sc16[u][g] = (uint16_t)(d >> (16 * half));                                   \
+      }                                                                             \
+    if (GPB != 1 && (I) + 2 < KB) P2_ISSUE(((J) + 2) % 3, IS, (I) + 2);             \
+    P2_COMPUTE(J, CS, I, GPB == 1 && (I) + 2 < KB, ((J) + 2) % 3, IS, (I) + 2);     \
   }
 
   P2_ISSUE(0, st0, 0);
   if (1 < KB) P2_ISSUE(1, st1, 1);
   P2_READY(0)
-  for (int kb0 = 0; kb0 < KB; kb0 += 3) {
+  // Steady state: three blocks per iteration with no branch inside (every
+  // load it issues is in range): the compiler then keeps track of which stage
+  // each load in flight writes and waits only for the stage read next (a
+  // merge of control-flow paths, or more load instructions per loop body,
+  // makes it wait for every load in flight); then the tail.
+  int kb0 = 0;
+  for (; kb0 + 5 <= KB; kb0 += 3) {
+    P2_STEP_U(0, st0, st2, kb0)
+    P2_READY_U
+    P2_STEP_U(1, st1, st0, kb0 + 1)
+    P2_READY_U
+    P2_STEP_U(2, st2, st1, kb0 + 2)
+    P2_READY_U
+  }
+  for (; kb0 < KB; kb0 += 3) {
     P2_STEP(0, st0, st2, kb0)
     if (kb0 + 1 < KB) {
       P2_READY(kb0 + 1)
@@ -945,10 +1038,13 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
     }
     if (kb0 + 3 < KB) P2_READY(kb0 + 3)
   }
+#undef P2_STEP_U
+#undef P2_READY_U
 #undef P2_STEP
 #undef P2_READY
 #undef P2_COMPUTE
 #undef P2_ISSUE
+#undef P2_PART
 
   const int col = lane & 15;
 #pragma unroll
@@ -990,13 +1086,13 @@ void launch_d(const KArgs& ka, int n_cg, int n_rt, hipStream_t s) {
 }
 
 // Row tiles per ordering group: all of them (channel-block major) when the
-// weights are the larger operand, else as many as keep about 2 MB of
-// activation rows in an XCD's L2.
-int group_rows(const KArgs& ka, int M_total, int n_mt, int MT, int fmt) {
+// weights are the larger operand, else as many as hold about `a_target` bytes
+// of activation rows (2 MB for the 64-row kernel, 4 MB for the 128-row one).
+int group_rows(const KArgs& ka, int M_total, int n_mt, int MT, int fmt, size_t a_target = 2u << 20) {
   const double a_bytes = (double)M_total * ka.K * 2.0;
   const double w_bytes = (double)(ka.nseg / ka.S) * ka.N * ka.K * (fmt == 1 ? 0.5 : 0.25);
   if (a_bytes < w_bytes) return n_mt;
-  const int gm = (int)((2u << 20) / ((size_t)MT * ka.K * 2));
+  const int gm = (int)(a_target / ((size_t)MT * ka.K * 2));
   return gm < 1 ? 1 : (gm > n_mt ? n_mt : gm);
 }
 
@@ -1019,15 +1115,19 @@ template <int EPI>
 void launch_p2(const KArgs& ka, const float* rowsum, int M_total, hipStream_t s) {
   const int n_nblk = EPI == 1 ? (ka.N / 2 + 127) / 128 : (ka.N + 255) / 256;
   const int n_mt = (M_total + kP2Rows - 1) / kP2Rows + ka.nseg;
-  const int GM = group_rows(ka, M_total, n_mt, kP2Rows, 1);
+  const int GM = group_rows(ka, M_total, n_mt, kP2Rows, 1, 4u << 20);  // measured best: about 4 MB
   const int items = n_nblk * ((n_mt + GM - 1) / GM) * GM;
   const dim3 grid((unsigned)(((items + 7) / 8) * 8));
   const dim3 block(kP2Threads);
+#define P2_LAUNCH(GPB, SL) \
+  hipLaunchKernelGGL((qgemm_p2_kernel<EPI, GPB, SL>), grid, block, 0, s, ka, rowsum, n_nblk, n_mt, GM)
+  const bool sl = ((ka.K / ka.G) & 1) == 0;
   switch (ka.G) {
-    case 128: hipLaunchKernelGGL((qgemm_p2_kernel<EPI, 1>), grid, block, 0, s, ka, rowsum, n_nblk, n_mt, GM); break;
-    case 64: hipLaunchKernelGGL((qgemm_p2_kernel<EPI, 2>), grid, block, 0, s, ka, rowsum, n_nblk, n_mt, GM); break;
-    default: hipLaunchKernelGGL((qgemm_p2_kernel<EPI, 4>), grid, block, 0, s, ka, rowsum, n_nblk, n_mt, GM); break;
+    case 128: if (sl) P2_LAUNCH(1, true); else P2_LAUNCH(1, false); break;
+    case 64: if (sl) P2_LAUNCH(2, true); else P2_LAUNCH(2, false); break;
+    default: if (sl) P2_LAUNCH(4, true); else P2_LAUNCH(4, false); break;
   }
+#undef P2_LAUNCH
 }
 
 // path: 0 = small-row-tile kernel, 64 / 128 = large-row-tile kernel with that
