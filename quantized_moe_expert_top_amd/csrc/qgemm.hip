@@ -223,27 +223,25 @@ struct BRegs {
 // ------------------------------------------------------------ decode, deep
 // One workgroup per (16-row tile of one segment, channel group of 64 SwiGLU /
 // 128 plain channels); each wavefront owns two 16-channel tiles and streams
-// all of K.  Weights and activations both run PF = 3 K blocks ahead in
+// all of K.  Weights, scales and activations run PF = 3 K blocks ahead in
 // register rings (the memory counter retires loads in issue order, so the
 // activations, issued first, never make a wavefront wait for weights it does
 // not need yet).  Per scale group, one bias-correction chain (the activation
 // fragments times -(128 + z)) seeds the chains of both tiles on the
-// dequantised codes.  Workgroups
-// are numbered so that the row tiles of one segment and channel group run on
-// one XCD, back to back: a segment of more than 16 rows reads its weights
-// from HBM once and from that XCD's L2 after.
+// dequantised codes.  Workgroups are numbered so that the row tiles of one
+// segment and channel group run on one XCD, back to back: a segment of more
+// than 16 rows reads its weights from HBM once and from that XCD's L2 after.
+//
+// The steady-state loop has no branch: every load is issued unconditionally
+// (a wavefront without a tile, and a bit plane the segment's width does not
+// use, read through a zero-size buffer resource, which returns zeros without
+// touching memory), so the compiler can count the loads in flight and wait
+// only for the one a step needs; a branch in the loop makes it wait for all
+// of them.  The last blocks run in a guarded tail.
 template <int FMT, int EPI, int GPB>
 __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, int n_rt) {
   constexpr int SPG = 4 / GPB;                 // MFMA steps per scale group
   constexpr int PF = 3, R = 4;                 // prefetch distance, ring size
-  // Scales: chunks of 4 groups of a channel (one 8-byte load per tile per CPK
-  // K blocks), loaded with the weights, in a ring of RS chunk slots that
-  // covers every chunk alive across the PF + 1 blocks in flight.  The loop
-  // is unrolled by 16 so that every ring index is a compile-time constant.
-  constexpr int U = 16;
-  constexpr int CPK = 4 / GPB, RS = CPK == 4 ? 4 : 8;
-  static_assert(U % R == 0 && (U / CPK) % RS == 0, "rings must divide the unroll factor");
-  static_assert(RS >= (PF + CPK) / CPK + (CPK > 1 ? 1 : 0), "scale ring too short for the prefetch distance");
   __shared__ u32x4 lds_a[3][4][64];            // [slot][step][lane], 12 KB
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = uniform(tid >> 6);
@@ -271,109 +269,99 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
   rsrc_t br[2], r3[2], r4[2], sr[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const size_t tile = (size_t)c.e * NT + (u ? ct1 : ct0);
-    br[u] = make_rsrc(p.codes + tile * KB * CB, KB * CB);
-    r3[u] = make_rsrc(FMT == 2 ? p.p3 + tile * KB * 256 : nullptr, FMT == 2 ? KB * 256 : 0);
-    r4[u] = make_rsrc(FMT == 2 ? p.p4 + tile * KB * 256 : nullptr, FMT == 2 ? KB * 256 : 0);
-    sr[u] = make_rsrc(p.scales + (tile * 16) * (size_t)(KB * GPB), 16 * KB * GPB * 2);
+    const size_t tile = (size_t)c.e * NT + (wvalid ? (u ? ct1 : ct0) : 0);
+    br[u] = make_rsrc(p.codes + tile * KB * CB, wvalid ? KB * CB : 0);
+    r3[u] = make_rsrc(FMT == 2 ? p.p3 + tile * KB * 256 : nullptr, FMT == 2 && wvalid && c.bits >= 3 ? KB * 256 : 0);
+    r4[u] = make_rsrc(FMT == 2 ? p.p4 + tile * KB * 256 : nullptr, FMT == 2 && wvalid && c.bits == 4 ? KB * 256 : 0);
+    sr[u] = make_rsrc(p.scales + (tile * 16) * (size_t)(KB * GPB), wvalid ? 16 * KB * GPB * 2 : 0);
   }
   const uint32_t soff = (uint32_t)((lane & 15) * KB * GPB * 2);
-  const bool sc_wide = ((KB * GPB) & 3) == 0;
   const uint32_t negc = (0xC300u | (uint32_t)p.z) * 0x00010001u;
   const bf16x8 neg = as_bf16x8(u32x4{negc, negc, negc, negc});
 
   f32x4 acc[2] = {f32x4{}, f32x4{}};
   u32x4 ra[R];
   BRegs rb[R];
-  u32x2 rsc[RS][2];
+  uint32_t rsc[R][2][GPB];  // one register per scale: packing two would wait for both loads
 
-#define QD_ISSUE_A(SLOT, KBI) ra[SLOT] = buf_x4(ar, aoff, (KBI) * 256);
-  // JJ: K block relative to kb (a multiple of U), a compile-time constant
-#define QD_ISSUE_B(SLOT, JJ)                                                                         \
-  if (wvalid) {                                                                                      \
-    const int kbi = kb + (JJ);                                                                       \
-    _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                  \
-      if (FMT == 1) {                                                                                \
-        rb[SLOT].c[u] = buf_x4(br[u], 16 * lane, kbi * CB);                                          \
-      } else {                                                                                       \
-        rb[SLOT].q[u] = buf_x2(br[u], 8 * lane, kbi * CB);                                           \
-        rb[SLOT].d3[u] = c.bits >= 3 ? buf_x1(r3[u], 4 * lane, kbi * 256) : 0u;                      \
-        rb[SLOT].d4[u] = c.bits == 4 ? buf_x1(r4[u], 4 * lane, kbi * 256) : 0u;                      \
-      }                                                                                              \
-      if (sc_wide) {                                                                                 \
-        if (((JJ) * GPB) % 4 == 0) rsc[((JJ) * GPB / 4) % RS][u] = buf_x2(sr[u], soff, kbi * GPB * 2); \
-      } else {                                                                                       \
-        _Pragma("unroll") for (int g = 0; g < GPB; ++g) {                                            \
-          const int lg = (JJ) * GPB + g;                                                             \
-          const uint32_t v = buf_u16(sr[u], soff, (kbi * GPB + g) * 2);                              \
-          const uint32_t wd = rsc[(lg / 4) % RS][u][(lg % 4) >> 1];                                  \
-          rsc[(lg / 4) % RS][u][(lg % 4) >> 1] =                                                     \
-              (lg & 1) ? ((wd & 0xFFFFu) | (v << 16)) : ((wd & 0xFFFF0000u) | v);                    \
-        }                                                                                            \
-      }                                                                                              \
-    }                                                                                                \
+#define QD_ISSUE(SLOT, KBI)                                                              \
+  {                                                                                      \
+    const int kbi = (KBI);                                                               \
+    ra[SLOT] = buf_x4(ar, aoff, kbi * 256);                                              \
+    _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                      \
+      if (FMT == 1) {                                                                    \
+        rb[SLOT].c[u] = buf_x4(br[u], 16 * lane, kbi * CB);                              \
+      } else {                                                                           \
+        rb[SLOT].q[u] = buf_x2(br[u], 8 * lane, kbi * CB);                               \
+        rb[SLOT].d3[u] = buf_x1(r3[u], 4 * lane, kbi * 256);                             \
+        rb[SLOT].d4[u] = buf_x1(r4[u], 4 * lane, kbi * 256);                             \
+      }                                                                                  \
+      _Pragma("unroll") for (int g = 0; g < GPB; ++g)                                    \
+          rsc[SLOT][u][g] = buf_u16(sr[u], soff, (kbi * GPB + g) * 2);                   \
+    }                                                                                    \
   }
-#define QD_STEP(J)                                                                                   \
-  if (kb + J < KB) {                                                                                 \
-    const int i = kb + J;                                                                            \
-    if (i + PF < KB) {                                                                               \
-      QD_ISSUE_A(((J) + PF) % R, i + PF);                                                            \
-      QD_ISSUE_B(((J) + PF) % R, (J) + PF);                                                          \
-    }                                                                                                \
-    if (i + 1 < KB) lds_a[(i + 1) % 3][wv][lane] = ra[((J) + 1) % R];                                 \
-    __syncthreads();                                                                                 \
-    if (wvalid) {                                                                                    \
-      const int sl = i % 3;                                                                          \
-      _Pragma("unroll") for (int t0 = 0; t0 < 4; t0 += SPG) {                                        \
-        f32x4 cr = f32x4{};                                                                          \
-        _Pragma("unroll") for (int t = t0; t < t0 + SPG; ++t) cr = mfma16(as_bf16x8(lds_a[sl][t][lane]), neg, cr); \
-        f32x4 tm[2] = {cr, cr};                                                                      \
-        _Pragma("unroll") for (int t = t0; t < t0 + SPG; ++t) {                                      \
-          const bf16x8 av = as_bf16x8(lds_a[sl][t][lane]);                                           \
-          _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                            \
-            const bf16x8 bv = (FMT == 1) ? deq_u4(rb[(J) % R].c[u], t)                               \
-                                         : deq_mwq(rb[(J) % R].q[u], rb[(J) % R].d3[u], rb[(J) % R].d4[u], t, c.bits); \
-            tm[u] = mfma16(av, bv, tm[u]);                                                           \
-          }                                                                                          \
-        }                                                                                            \
-        const int lg = (J) * GPB + t0 / SPG;                                                         \
-        _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                              \
-          const float sv = f16_to_f32((uint16_t)(rsc[(lg / 4) % RS][u][(lg % 4) >> 1] >> (16 * (lg & 1)))); \
-          _Pragma("unroll") for (int r = 0; r < 4; ++r) acc[u][r] = __builtin_fmaf(sv, tm[u][r], acc[u][r]); \
-        }                                                                                            \
-      }                                                                                              \
-    }                                                                                                \
+  // block I (ring slot J) from LDS stage I % 3
+#define QD_COMPUTE(J, I)                                                                                 \
+  {                                                                                                      \
+    const int sl = (I) % 3;                                                                              \
+    _Pragma("unroll") for (int t0 = 0; t0 < 4; t0 += SPG) {                                              \
+      f32x4 cr = f32x4{};                                                                                \
+      _Pragma("unroll") for (int t = t0; t < t0 + SPG; ++t) cr = mfma16(as_bf16x8(lds_a[sl][t][lane]), neg, cr); \
+      f32x4 tm[2] = {cr, cr};                                                                            \
+      _Pragma("unroll") for (int t = t0; t < t0 + SPG; ++t) {                                            \
+        const bf16x8 av = as_bf16x8(lds_a[sl][t][lane]);                                                 \
+        _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                  \
+          const bf16x8 bv = (FMT == 1) ? deq_u4(rb[J].c[u], t)                                           \
+                                       : deq_mwq(rb[J].q[u], rb[J].d3[u], rb[J].d4[u], t, c.bits);       \
+          tm[u] = mfma16(av, bv, tm[u]);                                                                 \
+        }                                                                                                \
+      }                                                                                                  \
+      const int g = t0 / SPG;                                                                            \
+      _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                    \
+        const float sv = f16_to_f32((uint16_t)rsc[J][u][g]);                                             \
+        _Pragma("unroll") for (int r = 0; r < 4; ++r) acc[u][r] = __builtin_fmaf(sv, tm[u][r], acc[u][r]); \
+      }                                                                                                  \
+    }                                                                                                    \
+  }
+  // steady state: blocks i + PF and i + 1 exist
+#define QD_STEP_U(J)                                                   \
+  {                                                                    \
+    const int i = kb0 + (J);                                           \
+    QD_ISSUE(((J) + PF) % R, i + PF);                                  \
+    lds_a[(i + 1) % 3][wv][lane] = ra[((J) + 1) % R];                  \
+    __syncthreads();                                                   \
+    QD_COMPUTE(J, i);                                                  \
+  }
+#define QD_STEP(J)                                                     \
+  if (kb0 + (J) < KB) {                                                \
+    const int i = kb0 + (J);                                           \
+    if (i + PF < KB) QD_ISSUE(((J) + PF) % R, i + PF);                 \
+    if (i + 1 < KB) lds_a[(i + 1) % 3][wv][lane] = ra[((J) + 1) % R];  \
+    __syncthreads();                                                   \
+    QD_COMPUTE(J, i);                                                  \
   }
 
   // prologue: activations and weights of K blocks 0..PF-1 in flight, block 0 staged
-  int kb = 0;
 #pragma unroll
   for (int j = 0; j < PF; ++j)
-    if (j < KB) {
-      QD_ISSUE_A(j, j);
-      QD_ISSUE_B(j, j);
-    }
+    if (j < KB) QD_ISSUE(j, j);
   lds_a[0][wv][lane] = ra[0];
-  for (; kb < KB; kb += U) {
+  int kb0 = 0;
+  for (; kb0 + R + PF <= KB; kb0 += R) {
+    QD_STEP_U(0)
+    QD_STEP_U(1)
+    QD_STEP_U(2)
+    QD_STEP_U(3)
+  }
+  for (; kb0 < KB; kb0 += R) {
     QD_STEP(0)
     QD_STEP(1)
     QD_STEP(2)
     QD_STEP(3)
-    QD_STEP(4)
-    QD_STEP(5)
-    QD_STEP(6)
-    QD_STEP(7)
-    QD_STEP(8)
-    QD_STEP(9)
-    QD_STEP(10)
-    QD_STEP(11)
-    QD_STEP(12)
-    QD_STEP(13)
-    QD_STEP(14)
-    QD_STEP(15)
   }
-#undef QD_ISSUE_A
-#undef QD_ISSUE_B
+#undef QD_ISSUE
+#undef QD_COMPUTE
+#undef QD_STEP_U
 #undef QD_STEP
   if (!wvalid) return;
   const int col = lane & 15;
