@@ -391,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
 // a bf16 MFMA on the base fragments, the biased 2-bit codes with the
 // -(128+z) correction chain, the per-channel step applied once at the end,
 // and the salient channels as one more exact bf16 K chunk.
-template <int EPI>
+template <int EPI, bool BASE>
 __global__ __launch_bounds__(kThreads) void qgemm_delta_kernel(KArgs p) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   Ctx c;
@@ -412,38 +412,69 @@ __global__ __launch_bounds__(kThreads) void qgemm_delta_kernel(KArgs p) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) accb[rt][u] = tmp[rt][u] = f32x4{};
   }
-  for (int kb = 0; kb < KB; ++kb) {
+  // Operands of one K block; block kb + 1 is loaded while block kb is
+  // multiplied.  No branch in the loop (a branch makes the compiler wait for
+  // every load in flight): buffer loads with per-lane offsets fixed and the
+  // K block in the scalar offset; the second row tile is always loaded (its
+  // rows are clamped into the segment and never stored).
+  struct DBlk {
     u32x4 a[2][4], bb[2][4];
     u32x2 cd[2];
+  };
+  const rsrc_t ar = make_rsrc(p.A, p.A_bytes);
+  const uint32_t aoff[2] = {(uint32_t)(arow[0] * p.K * 2 + 16 * (lane >> 4)),
+                            (uint32_t)(arow[1] * p.K * 2 + 16 * (lane >> 4))};
+  rsrc_t crs[2], brs[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int ct = u ? ct1 : ct0;
-      cd[u] = *reinterpret_cast<const u32x2*>(p.codes + (((size_t)c.e * NT + ct) * KB + kb) * 512 + 8 * lane);
-      if (p.base) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          bb[u][t] = *reinterpret_cast<const u32x4*>(p.base + ((size_t)ct * KB + kb) * 2048 + 512 * t + 8 * lane);
-      }
-    }
+  for (int u = 0; u < 2; ++u) {
+    const int ct = u ? ct1 : ct0;
+    crs[u] = make_rsrc(p.codes + ((size_t)c.e * NT + ct) * KB * 512, KB * 512);
+    brs[u] = make_rsrc(BASE ? p.base + (size_t)ct * KB * 2048 : nullptr, BASE ? KB * 4096 : 0);
+  }
+  auto load_blk = [&](DBlk& d, int kb) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      a[0][t] = *reinterpret_cast<const u32x4*>(Ap[0] + kb * 128 + 32 * t);
-      a[1][t] = two ? *reinterpret_cast<const u32x4*>(Ap[1] + kb * 128 + 32 * t) : u32x4{0u, 0u, 0u, 0u};
+      d.a[0][t] = buf_x4(ar, aoff[0], kb * 256 + 64 * t);
+      d.a[1][t] = buf_x4(ar, aoff[1], kb * 256 + 64 * t);
     }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      d.cd[u] = buf_x2(crs[u], 8 * lane, kb * 512);
+      if (BASE)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) d.bb[u][t] = buf_x4(brs[u], 16 * lane, kb * 4096 + 1024 * t);
+    }
+  };
+  auto mul_blk = [&](const DBlk& d) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        if (rt == 1 && !two) break;
-        const bf16x8 av = as_bf16x8(a[rt][t]);
+        const bf16x8 av = as_bf16x8(d.a[rt][t]);
         corr[rt] = mfma16(av, neg, corr[rt]);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          tmp[rt][u] = mfma16(av, deq_u2(cd[u], t), tmp[rt][u]);
-          if (p.base) accb[rt][u] = mfma16(av, as_bf16x8(bb[u][t]), accb[rt][u]);
+          tmp[rt][u] = mfma16(av, deq_u2(d.cd[u], t), tmp[rt][u]);
+          if (BASE) accb[rt][u] = mfma16(av, as_bf16x8(d.bb[u][t]), accb[rt][u]);
         }
       }
     }
+  };
+  DBlk d0, d1;
+  load_blk(d0, 0);
+  int kb = 0;
+  for (; kb + 3 <= KB; kb += 2) {  // steady state: blocks kb + 1, kb + 2 exist
+    load_blk(d1, kb + 1);
+    mul_blk(d0);
+    load_blk(d0, kb + 2);
+    mul_blk(d1);
+  }
+  if (kb + 1 < KB) {
+    load_blk(d1, kb + 1);
+    mul_blk(d0);
+    mul_blk(d1);
+  } else {
+    mul_blk(d0);
   }
   // salient input channels: one more K chunk of exact bf16 values
   if (p.n_sal > 0) {
@@ -1154,7 +1185,8 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, int A_rows, voi
   const int gx = EPI == 1 ? (ka.N / 2 + 63) / 64 : (ka.N + 127) / 128;
   if (fmt == 3) {
     const int gy = (M_total + kRows - 1) / kRows + ka.nseg;
-    hipLaunchKernelGGL((qgemm_delta_kernel<EPI>), dim3(gx, gy), dim3(kThreads), 0, s, ka);
+    if (ka.base) hipLaunchKernelGGL((qgemm_delta_kernel<EPI, true>), dim3(gx, gy), dim3(kThreads), 0, s, ka);
+    else hipLaunchKernelGGL((qgemm_delta_kernel<EPI, false>), dim3(gx, gy), dim3(kThreads), 0, s, ka);
     return;
   }
   const int n_rt = (M_total + 15) / 16 + ka.nseg;
