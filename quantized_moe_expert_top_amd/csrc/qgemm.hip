@@ -1093,6 +1093,234 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
   }
 }
 
+// ------------------------------------------------- delta with base, LDS-DMA
+// y = x W_base^T + x D_e^T for many rows per expert (ME-Switch delta layer).
+// One workgroup of 8 wavefronts per (128-row tile, 128-channel block);
+// wavefront (wm, wn) owns 64 rows x 2 channel tiles, and each activation
+// fragment read from LDS feeds 4 MFMAs: the bf16 base product and the 2-bit
+// delta product of both tiles.  Per K block, two LDS stages hold the 128
+// activation rows, the bf16 base fragments and the 2-bit codes of the 8
+// tiles (68 KB), loaded by LDS-DMA one block ahead.  The delta has one step
+// per output channel, so its chain runs over all of K: it starts from the
+// row's -(128 + z) * sum_k a_k (one row sum over all of K, from
+// rowsum_full_kernel) and the step multiplies once at the end.  The salient
+// channels are one more exact bf16 K chunk: their activation values are
+// gathered into LDS after the loop.
+__global__ __launch_bounds__(256) void rowsum_full_kernel(const uint16_t* __restrict__ A, int rows, int K, float negz,
+                                                          float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(A + (size_t)row * K);
+  float s = 0.f;
+  for (int c = lane; c < K / 8; c += 64) {
+    const u32x4 v = src[c];
+    const uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
+    s = add_bf16_pair(w3, add_bf16_pair(w2, add_bf16_pair(w1, add_bf16_pair(w0, s))));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if (lane == 0) out[row] = s * negz;
+}
+
+struct __attribute__((aligned(16))) P2DStage {
+  u32x4 a[8][4][64];  // activations [row tile][MFMA step][lane], 32 KB
+  u32x4 b[8][4][64];  // base [tile][MFMA step][lane], 32 KB
+  uint32_t d[8][2][64];  // 2-bit codes [tile][dword][lane], 4 KB
+};
+
+template <int EPI>
+__global__ __launch_bounds__(kP2Threads) void qgemm_p2d_kernel(KArgs p, const float* __restrict__ rowsum, int n_nblk,
+                                                               int n_mt, int GM) {
+  constexpr int RT = 4, UT = 2, V = 10;  // V: vector-memory instructions per K block and wavefront
+  __shared__ P2DStage st0, st1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = uniform(tid >> 6), wm = wv >> 2, wn = wv & 3;
+
+  const int per_xcd = gridDim.x / 8;
+  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  const int grp = item / (GM * n_nblk), rem = item % (GM * n_nblk);
+  const int nb = rem / GM, mt = grp * GM + rem % GM;
+  if (mt >= n_mt) return;
+  int seg, m0;
+  if (!find_tile(p.seg_offsets, p.nseg, mt, seg, m0, kP2Rows)) return;
+  const Ctx c{uniform(p.seg_offsets[seg] + m0), uniform(min(kP2Rows, p.seg_offsets[seg + 1] - p.seg_offsets[seg] - m0)),
+              uniform(seg), 2};
+  const int KB = p.K / 128, NT = p.N / 16;
+  auto tile_of = [&](int j, bool& valid) -> int {  // workgroup tile j = 2 * wn + u
+    const int t = nb * 8 + j;
+    valid = t < NT;
+    return valid ? t : 0;
+  };
+
+  // loads issued by this wavefront: activation row tile wv, base and codes of workgroup tile wv
+  const rsrc_t ar = make_rsrc(p.A, p.A_bytes);
+  const uint32_t a_off = (uint32_t)(src_row(p, c, 16 * wv + (lane & 15)) * (size_t)p.K * 2 + 16 * (lane >> 4));
+  bool tv;
+  const int tw = tile_of(wv, tv);
+  const rsrc_t bsr = make_rsrc(p.base + (size_t)tw * KB * 2048, KB * 4096);
+  const rsrc_t csr = make_rsrc(p.codes + ((size_t)c.e * NT + tw) * KB * 512, KB * 512);
+
+  // consumer side: this wavefront's tiles, steps, row sums
+  int ct[UT];
+  bool cval[UT];
+  float step[UT];
+#pragma unroll
+  for (int u = 0; u < UT; ++u) {
+    ct[u] = tile_of(2 * wn + u, cval[u]);
+    step[u] = f16_to_f32(p.scales[(size_t)c.e * p.N + ct[u] * 16 + (lane & 15)]);
+  }
+  // the row sums of this lane's 16 accumulator rows: all source rows first, then all sums
+  // (one branch for the whole batch: a branch per lookup serialises the loads)
+  size_t srow[RT][4];
+  if (p.gather) {
+    int g[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) g[rt][r] = p.gather[c.row0 + min(64 * wm + 16 * rt + 4 * (lane >> 4) + r, c.rows - 1)];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) srow[rt][r] = (size_t)(g[rt][r] / p.k);
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) srow[rt][r] = (size_t)(c.row0 + min(64 * wm + 16 * rt + 4 * (lane >> 4) + r, c.rows - 1));
+  }
+  f32x4 accb[RT][UT], accd[RT][UT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    f32x4 rv;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rv[r] = rowsum[srow[rt][r]];
+#pragma unroll
+    for (int u = 0; u < UT; ++u) {
+      accb[rt][u] = f32x4{};
+      accd[rt][u] = rv;
+    }
+  }
+
+#define PD_ISSUE(ST, KBI)                                                                                  \
+  {                                                                                                        \
+    const int kbi = (KBI);                                                                                 \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q)                                                          \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, &ST.a[wv][q][0], 16, a_off, kbi * 256 + 64 * q, 0, 0);  \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q)                                                          \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(bsr, &ST.b[wv][q][0], 16, 16 * lane, kbi * 4096 + 1024 * q, 0, 0); \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h)                                                          \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(csr, &ST.d[wv][h][0], 4, 8 * lane, kbi * 512 + 4 * h, 0, 0); \
+  }
+#define PD_COMPUTE(ST)                                                                                     \
+  {                                                                                                        \
+    u32x2 cd[UT];                                                                                          \
+    _Pragma("unroll") for (int u = 0; u < UT; ++u) cd[u] = u32x2{ST.d[2 * wn + u][0][lane], ST.d[2 * wn + u][1][lane]}; \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                                        \
+      bf16x8 bb[UT], bd[UT];                                                                               \
+      _Pragma("unroll") for (int u = 0; u < UT; ++u) {                                                     \
+        bb[u] = as_bf16x8(ST.b[2 * wn + u][t][lane]);                                                      \
+        bd[u] = deq_u2(cd[u], t);                                                                          \
+      }                                                                                                    \
+      _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                                  \
+        const bf16x8 av = as_bf16x8(ST.a[4 * wm + rt][t][lane]);                                           \
+        _Pragma("unroll") for (int u = 0; u < UT; ++u) {                                                   \
+          accb[rt][u] = mfma16(av, bb[u], accb[rt][u]);                                                    \
+          accd[rt][u] = mfma16(av, bd[u], accd[rt][u]);                                                    \
+        }                                                                                                  \
+      }                                                                                                    \
+    }                                                                                                      \
+  }
+  // block i in stage i % 2: wait for this wavefront's loads of block i, the
+  // barrier publishes them and retires the other stage, then block i + 1 is
+  // issued into it and block i multiplied; the steady state has no branch
+#define PD_STEP_U(CS, IS, I)            \
+  {                                     \
+    __builtin_amdgcn_sched_barrier(0);  \
+    vm_wait<0>();                       \
+    __builtin_amdgcn_s_barrier();       \
+    PD_ISSUE(IS, (I) + 1);              \
+    PD_COMPUTE(CS);                     \
+  }
+  PD_ISSUE(st0, 0);
+  int kb0 = 0;
+  for (; kb0 + 3 <= KB; kb0 += 2) {
+    PD_STEP_U(st0, st1, kb0)
+    PD_STEP_U(st1, st0, kb0 + 1)
+  }
+  for (; kb0 < KB; kb0 += 2) {
+    __builtin_amdgcn_sched_barrier(0);
+    vm_wait<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kb0 + 1 < KB) PD_ISSUE(st1, kb0 + 1);
+    PD_COMPUTE(st0);
+    if (kb0 + 1 < KB) {
+      vm_wait<0>();
+      __builtin_amdgcn_s_barrier();
+      if (kb0 + 2 < KB) PD_ISSUE(st0, kb0 + 2);
+      PD_COMPUTE(st1);
+    }
+  }
+#undef PD_STEP_U
+#undef PD_COMPUTE
+#undef PD_ISSUE
+
+  // salient input channels: gather their activation values into stage 0 in
+  // the MFMA operand layout (2 steps of 32 slots), then one more bf16 K chunk
+  const int nsteps = (p.n_sal + 31) / 32;
+  if (nsteps > 0) {
+    __syncthreads();  // every wavefront is done with stage 0
+    for (int slot = tid; slot < 8 * 2 * 64; slot += kP2Threads) {
+      const int rt8 = slot >> 7, sstep = (slot >> 6) & 1, l = slot & 63;
+      const uint16_t* Arow = p.A + src_row(p, c, 16 * rt8 + (l & 15)) * (size_t)p.K;
+      u32x4 v;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+          const int j = 32 * sstep + 8 * (l >> 4) + 2 * h + e2;
+          const int idx = j < p.n_sal ? min(max(p.sal_idx[(size_t)c.e * p.n_sal + j], 0), p.K - 1) : -1;
+          w |= (uint32_t)(idx >= 0 ? Arow[idx] : 0) << (16 * e2);
+        }
+        v[h] = w;
+      }
+      st0.a[rt8][sstep][l] = v;
+    }
+    __syncthreads();
+    for (int ss = 0; ss < nsteps; ++ss) {
+      u32x4 sv[UT];
+#pragma unroll
+      for (int u = 0; u < UT; ++u)
+        sv[u] = *reinterpret_cast<const u32x4*>(p.sal_val + (((size_t)c.e * NT + ct[u]) * nsteps + ss) * 512 + 8 * lane);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const bf16x8 av = as_bf16x8(st0.a[4 * wm + rt][ss][lane]);
+#pragma unroll
+        for (int u = 0; u < UT; ++u) accb[rt][u] = mfma16(av, as_bf16x8(sv[u]), accb[rt][u]);
+      }
+    }
+  }
+
+  const int col = lane & 15;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 64 * wm + 16 * rt + 4 * (lane >> 4) + r;
+      if (row >= c.rows) continue;
+#pragma unroll
+      for (int u = 0; u < UT; ++u) {
+        if (!cval[u]) continue;
+        const float y = __builtin_fmaf(step[u], accd[rt][u][r], accb[rt][u][r]);
+        const size_t o = (size_t)(c.row0 + row) * p.n_out + ct[u] * 16 + col;
+        if (EPI == 2) static_cast<float*>(p.out)[o] = y;
+        else static_cast<uint16_t*>(p.out)[o] = f32_to_bf16(y);
+      }
+    }
+  }
+}
+
 template <int FMT, int EPI>
 void launch_d(const KArgs& ka, int n_cg, int n_rt, hipStream_t s) {
   const int items = n_cg * n_rt;
@@ -1152,7 +1380,24 @@ void launch_p2(const KArgs& ka, const float* rowsum, int M_total, hipStream_t s)
 // path: 0 = small-row-tile kernel, 64 / 128 = large-row-tile kernel with that
 // tile height, 2 = 128-row LDS-DMA kernel (INT4; row sums in `ws`)
 template <int EPI>
+void launch_p2d(const KArgs& ka, const float* rowsum, int M_total, hipStream_t s) {
+  const int n_nblk = (ka.N + 127) / 128;
+  const int n_mt = (M_total + kP2Rows - 1) / kP2Rows + ka.nseg;
+  const int GM = group_rows(ka, M_total, n_mt, kP2Rows, 3, 4u << 20);
+  const int items = n_nblk * ((n_mt + GM - 1) / GM) * GM;
+  const dim3 grid((unsigned)(((items + 7) / 8) * 8));
+  hipLaunchKernelGGL((qgemm_p2d_kernel<EPI>), grid, dim3(kP2Threads), 0, s, ka, rowsum, n_nblk, n_mt, GM);
+}
+
+template <int EPI>
 void launch_epi(const KArgs& ka, int fmt, int path, int M_total, int A_rows, void* ws, hipStream_t s) {
+  if (path == 3 && EPI != 1) {
+    float* rs = static_cast<float*>(ws);
+    hipLaunchKernelGGL(rowsum_full_kernel, dim3((unsigned)((A_rows + 3) / 4)), dim3(256), 0, s, ka.A, A_rows, ka.K,
+                       -(128.0f + (float)ka.z), rs);
+    launch_p2d<EPI>(ka, rs, M_total, s);
+    return;
+  }
   if (path == 2) {
     float* rs = static_cast<float*>(ws);
     const int rows = A_rows;
@@ -1201,6 +1446,7 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, int A_rows, voi
 // MOE_QGEMM_PATH=small|64|64n|128|dma forces a path.
 int pick_path(int M_total, int nseg, int fmt) {
   if (const char* f = getenv("MOE_QGEMM_PATH")) {
+    if (fmt == 3) return !strcmp(f, "dma") ? 3 : 0;
     if (!strcmp(f, "small")) return 0;
     if (!strcmp(f, "64")) return 64;
     if (!strcmp(f, "64n")) return 65;
@@ -1208,14 +1454,17 @@ int pick_path(int M_total, int nseg, int fmt) {
     if (!strcmp(f, "dma") && fmt == 1) return 2;
   }
   const double avg = (double)M_total / (double)(nseg > 0 ? nseg : 1);
+  if (fmt == 3) return avg >= 96.0 ? 3 : 0;  // delta: 128-row LDS-DMA kernel, else 32-row tiles
   if (avg < 24.0) return 0;
   return (fmt == 1 && avg >= 96.0) ? 2 : 64;
 }
 }  // namespace
 
 size_t qgemm_workspace_bytes(const QWeights& w, int A_rows, int M_total) {
-  if (w.fmt != 1 || pick_path(M_total, w.E, w.fmt) != 2) return 0;
-  return ((size_t)A_rows * (w.K / w.G) * 4 + 255) & ~(size_t)255;
+  const int path = pick_path(M_total, w.E * (w.fmt == 2 ? 3 : 1), w.fmt);
+  if (path == 2) return ((size_t)A_rows * (w.K / w.G) * 4 + 255) & ~(size_t)255;  // row sums per group
+  if (path == 3) return ((size_t)A_rows * 4 + 255) & ~(size_t)255;                 // row sums over all of K
+  return 0;
 }
 
 hipError_t launch_qgemm(const QGemmArgs& a, hipStream_t s) {

@@ -230,6 +230,18 @@ def test_delta_small_full(G):
                                 n_salient=7, seed=9))
 
 
+@pytest.mark.parametrize("over", [
+    dict(requests=12, tokens_per_request=5, K=512, N=256, E=4, n_salient=7, seed=9),
+    dict(requests=40, tokens_per_request=7, K=384, N=160, E=3, n_salient=40, seed=19),  # 3 K blocks, partial block, 2 salient steps
+    dict(requests=20, tokens_per_request=16, K=256, N=128, E=2, n_salient=1, seed=29),
+])
+def test_delta_dma_kernel(G, over, monkeypatch):
+    """The 128-row LDS-DMA delta kernel forced on small layers (it is chosen by
+    itself for about 96 rows per expert and more)."""
+    monkeypatch.setenv("MOE_QGEMM_PATH", "dma")
+    _delta_parity(G, gen.config("meswitch_delta", **over))
+
+
 def test_delta_full_size_sampled(G):
     cfg = gen.config("meswitch_delta")
     _delta_parity(G, cfg, tokens=np.array([0, 17, 1000, 2047, 3333, 4095]))
