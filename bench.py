@@ -231,6 +231,7 @@ def main():
                 if hbm_bound else
                 {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None})
+    roofline["traffic"] = measured_traffic(cfg.name)
     roofline.update({"kernel": dom_name, "kernel_ms": round(dom_ms, 5), "algorithmic_bytes": int(dom_bytes),
                      "algorithmic_flops": dom_flops, "gbs": round(gbs, 1), "tflops": round(tflops, 2)})
 
@@ -253,6 +254,24 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counters (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE per dispatch,
+    scaled by a plain copy's readings), or None when that file has no entry
+    for the workload or was taken on a different qgemm.hip."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "quantized_moe_expert_top_amd", "csrc", "qgemm.hip")
+    try:
+        t = json.load(open(path))
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != t["qgemm_hip_sha256"]:
+            return None
+        w = t["workloads"][workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    return int((w["fetch_kib"] * t["fetch_scale"] + w["write_kib"] * t["write_scale"]) * 1024)
 
 
 def cpu_baseline(cfg, data, target_s):
