@@ -244,7 +244,13 @@ moe_status moe_repack_weights(const moe_wdesc* src, const moe_wdesc* dst, void* 
  *   M_total     host upper bound of rows (T*k); grid sizing never reads the
  *               device counts back
  *   out         bf16 or fp32 (see epilogue) [M_total][N or N/2], 16-byte aligned
- *   workspace   moe_grouped_qgemm_workspace_size(...) bytes (may be 0 / NULL)
+ *   workspace   moe_grouped_qgemm_workspace_size(...) bytes, device memory,
+ *               16-byte aligned; the 128-row prefill kernels keep per-row
+ *               sums of A there (INT4: A_rows x K/G fp32; DELTA2 with base:
+ *               A_rows fp32), rewritten on every call; size 0 (NULL allowed)
+ *               for every other launch.  Calls that share one workspace must
+ *               be ordered on one stream.  Too small -> MOE_ERR_WORKSPACE_TOO_SMALL,
+ *               misaligned -> MOE_ERR_MISALIGNED
  * Supported: N % 32 == 0, K % 128 == 0, G in {32, 64, 128} for INT4 and MWQ.
  */
 size_t moe_grouped_qgemm_workspace_size(const moe_wdesc* w, int32_t A_rows, int32_t M_total);
