@@ -51,7 +51,8 @@ struct KArgs {
   const int32_t* gather;
   const int32_t* seg_offsets;
   void* out;
-  int k, nseg, S, N, K, G, z, n_sal, n_out;
+  float* part;  // split-K partial sums [n_ks][M_total][N] (decode kernel, plain epilogues)
+  int k, nseg, S, N, K, G, z, n_sal, n_out, M_total;
   uint32_t A_bytes;
 };
 
@@ -61,15 +62,17 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 // Locate the row tile `y` (in segment order; tiles of `rows_per_tile` rows)
 // -> segment and first row.
+// With `stride` > 1, segment s spans seg_offsets[s*stride] .. seg_offsets[(s+1)*stride]
+// (all bit-width sub-segments of one expert).
 __device__ __forceinline__ bool find_tile(const int32_t* seg_offsets, int nseg, int y, int& seg, int& m0,
-                                          int rows_per_tile = kRows) {
+                                          int rows_per_tile = kRows, int stride = 1) {
   const int kRows = rows_per_tile;
   const int lane = threadIdx.x & 63;
   int carry = 0;
   for (int s0 = 0; s0 < nseg; s0 += 64) {
     const int s = s0 + lane;
     int tiles = 0;
-    if (s < nseg) tiles = (seg_offsets[s + 1] - seg_offsets[s] + kRows - 1) / kRows;
+    if (s < nseg) tiles = (seg_offsets[(s + 1) * stride] - seg_offsets[s * stride] + kRows - 1) / kRows;
     int incl = tiles;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -113,7 +116,7 @@ __device__ __forceinline__ bf16x8 deq_u4(const u32x4& cd, int t) {
 
 // MWQ: c_b = 4*q2 + 2*d3*[b>=3] + d4*[b==4], placed straight into the low
 // mantissa bits (q2 at bits 2-3, d3 at bit 1, d4 at bit 0 of each half).
-__device__ __forceinline__ bf16x8 deq_mwq(const u32x2& q2, uint32_t d3, uint32_t d4, int t, int b) {
+__device__ __forceinline__ u32x4 deq_mwq_bits(const u32x2& q2, uint32_t d3, uint32_t d4, int t, int b) {
   const uint32_t Q = q2[t >> 1];
   u32x4 r;
 #pragma unroll
@@ -125,8 +128,12 @@ __device__ __forceinline__ bf16x8 deq_mwq(const u32x2& q2, uint32_t d3, uint32_t
     if (b == 4) v |= shr(d4, P3) & 0x00010001u;
     r[p] = v;
   }
-  return as_bf16x8(r);
+  return r;
 }
+__device__ __forceinline__ bf16x8 deq_mwq(const u32x2& q2, uint32_t d3, uint32_t d4, int t, int b) {
+  return as_bf16x8(deq_mwq_bits(q2, d3, d4, t, b));
+}
+__device__ __forceinline__ u32x4 and4(const u32x4& v, uint32_t m) { return u32x4{v[0] & m, v[1] & m, v[2] & m, v[3] & m}; }
 
 __device__ __forceinline__ bf16x8 deq_u2(const u32x2& c, int t) {
   const uint32_t C = c[t >> 1];
@@ -238,8 +245,25 @@ struct BRegs {
 // touching memory), so the compiler can count the loads in flight and wait
 // only for the one a step needs; a branch in the loop makes it wait for all
 // of them.  The last blocks run in a guarded tail.
+//
+// FMT 4 (nested MWQ, all widths of an expert in one tile): a tile takes 16
+// rows of the expert's three sub-segments (b = 4, 3, 2, adjacent in the
+// grouped order), loads each bit plane once for all of them, and runs one
+// MFMA per width present in the wavefront's rows: the activation rows of width
+// b (the others masked to zero) times the codes truncated to b bits.  Every
+// width has the same scale and zero point, so the one correction chain over
+// all rows still applies, and each row's sum is the one it would get in its
+// own sub-segment (the other widths add exact zeros).
+//
+// Split K (n_ks > 1, plain epilogues only): work item ks covers K blocks
+// [ks * kb_per, ...) and stores its fp32 sums in p.part[ks]; splitk_reduce_kernel
+// adds the n_ks partials in order.  It gives a long-K GEMM with few channel
+// groups and row tiles (the down projection of a decode batch) enough
+// wavefronts to keep loads in flight.
 template <int FMT, int EPI, int GPB>
-__global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, int n_rt) {
+__global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, int n_rt, int n_ks, int kb_per) {
+  constexpr bool MW = FMT != 1;                // nested bit planes
+  constexpr bool FU = FMT == 4;                // all widths of an expert per tile
   constexpr int SPG = 4 / GPB;                 // MFMA steps per scale group
   constexpr int PF = 3, R = 4;                 // prefetch distance, ring size
   __shared__ u32x4 lds_a[3][4][64];            // [slot][step][lane], 12 KB
@@ -248,34 +272,48 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
 
   const int per_xcd = gridDim.x / 8;
   const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  const int cg = item / n_rt, rtile = item % n_rt;
+  const int cgk = item / n_rt, rtile = item % n_rt;  // (channel group, K split) major, row tile minor
+  const int cg = cgk / n_ks, ks = cgk % n_ks;
   if (cg >= n_cg) return;
   int seg, m0;
-  if (!find_tile(p.seg_offsets, p.nseg, rtile, seg, m0, 16)) return;
+  const int SS = FU ? p.S : 1;  // sub-segments per tile segment
+  if (!find_tile(p.seg_offsets, p.nseg / SS, rtile, seg, m0, 16, SS)) return;
   Ctx c;
-  c.row0 = uniform(p.seg_offsets[seg] + m0);
-  c.rows = uniform(min(16, p.seg_offsets[seg + 1] - c.row0));
-  c.e = uniform(seg / p.S);
+  c.row0 = uniform(p.seg_offsets[seg * SS] + m0);
+  c.rows = uniform(min(16, p.seg_offsets[(seg + 1) * SS] - c.row0));
+  c.e = uniform(FU ? seg : seg / p.S);
   c.bits = uniform(4 - (seg % p.S));
+  // FMT 4: rows [.., o1) have b = 4, [o1, o2) b = 3, [o2, ..) b = 2
+  const int o1 = FU ? uniform(p.seg_offsets[seg * SS + 1]) : 0;
+  const int o2 = FU ? uniform(p.seg_offsets[seg * SS + 2]) : 0;
+  const bool need3 = FU ? c.row0 < o2 : c.bits >= 3;
+  const bool need4 = FU ? c.row0 < o1 : c.bits == 4;
+  const int lrow = c.row0 + (lane & 15);
+  const uint32_t m4 = lrow < o1 ? ~0u : 0u, m3 = (lrow >= o1 && lrow < o2) ? ~0u : 0u, m2 = lrow >= o2 ? ~0u : 0u;
   int ct0, ct1, hch;
   bool v1;
   const bool wvalid = wave_tiles<EPI == 1>(p, wv, ct0, ct1, v1, hch, cg);
-  const int KB = p.K / 128, NT = p.N / 16;
+  const int KBt = p.K / 128, NT = p.N / 16;
+  const int kb_lo = ks * kb_per;               // this split's first K block
+  const int KB = min(kb_per, KBt - kb_lo);     // and its number of K blocks (>= 1)
 
   // activations: this thread carries (step wv, lane) of each K block
   const rsrc_t ar = make_rsrc(p.A, p.A_bytes);
-  const uint32_t aoff = (uint32_t)((src_row(p, c, lane & 15) * p.K + 32 * wv + 8 * (lane >> 4)) * 2);
+  const uint32_t aoff = (uint32_t)((src_row(p, c, lane & 15) * p.K + 32 * wv + 8 * (lane >> 4)) * 2 + kb_lo * 256);
   constexpr uint32_t CB = FMT == 1 ? 1024 : 512;
   rsrc_t br[2], r3[2], r4[2], sr[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const size_t tile = (size_t)c.e * NT + (wvalid ? (u ? ct1 : ct0) : 0);
-    br[u] = make_rsrc(p.codes + tile * KB * CB, wvalid ? KB * CB : 0);
-    r3[u] = make_rsrc(FMT == 2 ? p.p3 + tile * KB * 256 : nullptr, FMT == 2 && wvalid && c.bits >= 3 ? KB * 256 : 0);
-    r4[u] = make_rsrc(FMT == 2 ? p.p4 + tile * KB * 256 : nullptr, FMT == 2 && wvalid && c.bits == 4 ? KB * 256 : 0);
-    sr[u] = make_rsrc(p.scales + (tile * 16) * (size_t)(KB * GPB), wvalid ? 16 * KB * GPB * 2 : 0);
+    const size_t tb = tile * KBt + kb_lo;      // first tile block of the split
+    br[u] = make_rsrc(p.codes + tb * CB, wvalid ? KB * CB : 0);
+    r3[u] = make_rsrc(MW ? p.p3 + tb * 256 : nullptr, MW && wvalid && need3 ? KB * 256 : 0);
+    r4[u] = make_rsrc(MW ? p.p4 + tb * 256 : nullptr, MW && wvalid && need4 ? KB * 256 : 0);
+    // scales [channel][group]: rows of KBt * GPB entries, this split's columns from kb_lo * GPB
+    sr[u] = make_rsrc(p.scales + (tile * 16) * (size_t)(KBt * GPB) + (size_t)kb_lo * GPB,
+                      wvalid ? (16 * KBt * GPB - kb_lo * GPB) * 2 : 0);
   }
-  const uint32_t soff = (uint32_t)((lane & 15) * KB * GPB * 2);
+  const uint32_t soff = (uint32_t)((lane & 15) * KBt * GPB * 2);
   const uint32_t negc = (0xC300u | (uint32_t)p.z) * 0x00010001u;
   const bf16x8 neg = as_bf16x8(u32x4{negc, negc, negc, negc});
 
@@ -309,11 +347,19 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
       _Pragma("unroll") for (int t = t0; t < t0 + SPG; ++t) cr = mfma16(as_bf16x8(lds_a[sl][t][lane]), neg, cr); \
       f32x4 tm[2] = {cr, cr};                                                                            \
       _Pragma("unroll") for (int t = t0; t < t0 + SPG; ++t) {                                            \
-        const bf16x8 av = as_bf16x8(lds_a[sl][t][lane]);                                                 \
+        const u32x4 araw = lds_a[sl][t][lane];                                                           \
+        const bf16x8 av = as_bf16x8(araw);                                                               \
         _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                  \
-          const bf16x8 bv = (FMT == 1) ? deq_u4(rb[J].c[u], t)                                           \
-                                       : deq_mwq(rb[J].q[u], rb[J].d3[u], rb[J].d4[u], t, c.bits);       \
-          tm[u] = mfma16(av, bv, tm[u]);                                                                 \
+          if (FU) {                                                                                      \
+            const u32x4 b4 = deq_mwq_bits(rb[J].q[u], rb[J].d3[u], rb[J].d4[u], t, 4);                   \
+            tm[u] = mfma16(as_bf16x8(and4(araw, m4)), as_bf16x8(b4), tm[u]);                             \
+            tm[u] = mfma16(as_bf16x8(and4(araw, m3)), as_bf16x8(and4(b4, 0xFFFEFFFEu)), tm[u]);          \
+            tm[u] = mfma16(as_bf16x8(and4(araw, m2)), as_bf16x8(and4(b4, 0xFFFCFFFCu)), tm[u]);          \
+          } else {                                                                                       \
+            const bf16x8 bv = (FMT == 1) ? deq_u4(rb[J].c[u], t)                                         \
+                                         : deq_mwq(rb[J].q[u], rb[J].d3[u], rb[J].d4[u], t, c.bits);     \
+            tm[u] = mfma16(av, bv, tm[u]);                                                               \
+          }                                                                                              \
         }                                                                                                \
       }                                                                                                  \
       const int g = t0 / SPG;                                                                            \
@@ -365,6 +411,18 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
 #undef QD_STEP
   if (!wvalid) return;
   const int col = lane & 15;
+  if (EPI != 1 && n_ks > 1) {
+    float* part = p.part + (size_t)ks * p.M_total * p.N;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * (lane >> 4) + r;
+      if (row >= c.rows) continue;
+      float* orow = part + (size_t)(c.row0 + row) * p.N;
+      orow[ct0 * 16 + col] = acc[0][r];
+      if (v1) orow[ct1 * 16 + col] = acc[1][r];
+    }
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = 4 * (lane >> 4) + r;
@@ -1321,14 +1379,70 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2d_kernel(KArgs p, const fl
   }
 }
 
+// out[row] = sum over ks = 0..n_ks-1 of part[ks][row], in that order, for the
+// rows the segments hold (seg_offsets[nseg]); fp32 or bf16 out.  One thread
+// per 4 outputs.
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int n_ks, int M_total,
+                                                            int N, const int32_t* __restrict__ seg_offsets, int nseg,
+                                                            void* __restrict__ out) {
+  const size_t i4 = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t rows = (size_t)seg_offsets[nseg];
+  if (i4 * 4 >= rows * N) return;
+  const size_t plane = (size_t)M_total * N;
+  f32x4 v = reinterpret_cast<const f32x4*>(part)[i4];
+  for (int ks = 1; ks < n_ks; ++ks) v += reinterpret_cast<const f32x4*>(part + ks * plane)[i4];
+  if (EPI == 2) {
+    reinterpret_cast<f32x4*>(out)[i4] = v;
+  } else {
+    uint16_t* o = static_cast<uint16_t*>(out) + i4 * 4;
+    o[0] = f32_to_bf16(v[0]);
+    o[1] = f32_to_bf16(v[1]);
+    o[2] = f32_to_bf16(v[2]);
+    o[3] = f32_to_bf16(v[3]);
+  }
+}
+
+// K splits of the decode kernel: one unless the (channel group, row tile)
+// items leave the chip short of workgroups (fewer than 3 per CU), then enough
+// to bring them to about 4 per CU, each split keeping at least 8 K blocks.
+int decode_splits(int n_items, int K) {
+  const int KBt = K / 128;
+  if (n_items >= 768 || KBt < 16) return 1;
+  int n = (1024 + n_items - 1) / n_items;
+  n = min(n, KBt / 8);
+  const int kb_per = (KBt + n - 1) / n;
+  return (KBt + kb_per - 1) / kb_per;  // every split non-empty
+}
+
+// Upper bound of the decode kernel's row tiles: one partial tile per tile
+// segment (an expert, or for MWQ on path 1 each width of an expert).
+int decode_row_tiles(int fmt, int path, int M_total, int E) {
+  return (M_total + 15) / 16 + ((fmt == 2 && path == 1) ? 3 * E : E);
+}
+
 template <int FMT, int EPI>
 void launch_d(const KArgs& ka, int n_cg, int n_rt, hipStream_t s) {
-  const int items = n_cg * n_rt;
+  const int KBt = ka.K / 128;
+  const int n_ks = (EPI == 1 || !ka.part) ? 1 : decode_splits(n_cg * n_rt, ka.K);
+  const int kb_per = (KBt + n_ks - 1) / n_ks;
+  const int items = n_cg * n_ks * n_rt;
   const dim3 grid((unsigned)(((items + 7) / 8) * 8));  // multiple of 8: one equal share per XCD
   switch (ka.G) {
-    case 128: hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 1>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt); break;
-    case 64: hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 2>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt); break;
-    default: hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 4>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt); break;
+    case 128:
+      hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 1>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt, n_ks, kb_per);
+      break;
+    case 64:
+      hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 2>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt, n_ks, kb_per);
+      break;
+    default:
+      hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 4>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt, n_ks, kb_per);
+      break;
+  }
+  if (n_ks > 1) {
+    const size_t n4 = (size_t)ka.M_total * ka.N / 4;
+    hipLaunchKernelGGL((splitk_reduce_kernel<EPI>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, ka.part,
+                       n_ks, ka.M_total, ka.N, ka.seg_offsets, ka.nseg, ka.out);
   }
 }
 
@@ -1406,7 +1520,7 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, int A_rows, voi
     launch_p2<EPI>(ka, rs, M_total, s);
     return;
   }
-  if (fmt != 3 && path != 0) {
+  if (fmt != 3 && path != 0 && path != 1) {
     // 64 rows per workgroup; 8 wavefront columns (wide channel blocks: the
     // activations are read fewer times) when the activations outweigh the
     // weights, else 4.  path 65 forces 4 columns, 128 two rows of 4.
@@ -1434,20 +1548,28 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, int A_rows, voi
     else hipLaunchKernelGGL((qgemm_delta_kernel<EPI, false>), dim3(gx, gy), dim3(kThreads), 0, s, ka);
     return;
   }
-  const int n_rt = (M_total + 15) / 16 + ka.nseg;
-  if (fmt == 1) launch_d<1, EPI>(ka, gx, n_rt, s);
-  else launch_d<2, EPI>(ka, gx, n_rt, s);
+  // row tiles: at most one partial tile per (tile) segment; the plain
+  // epilogues may split K into the workspace
+  KArgs kd = ka;
+  if (EPI != 1) kd.part = static_cast<float*>(ws);
+  const int n_rt = decode_row_tiles(fmt, path, M_total, ka.nseg / ka.S);
+  if (fmt == 1) launch_d<1, EPI>(kd, gx, n_rt, s);
+  else if (path == 1) launch_d<2, EPI>(kd, gx, n_rt, s);  // one width per tile
+  else launch_d<4, EPI>(kd, gx, n_rt, s);                 // all widths per tile
 }
 
 // Kernel from the mean rows per segment (the host never sees the device
 // counts): few rows per segment -> 16-row tiles (decode kernel); many -> the
 // 128-row LDS-DMA kernel for INT4, 64-row tiles otherwise (and for INT4
 // segments of under ~96 rows, where 128-row tiles would be mostly padding).
-// MOE_QGEMM_PATH=small|64|64n|128|dma forces a path.
+// For MWQ the 16-row tiles take all widths of an expert together (one read of
+// each bit plane) unless MOE_QGEMM_PATH=split gives each width its own tiles.
+// MOE_QGEMM_PATH=small|split|64|64n|128|dma forces a path.
 int pick_path(int M_total, int nseg, int fmt) {
   if (const char* f = getenv("MOE_QGEMM_PATH")) {
     if (fmt == 3) return !strcmp(f, "dma") ? 3 : 0;
     if (!strcmp(f, "small")) return 0;
+    if (!strcmp(f, "split")) return fmt == 2 ? 1 : 0;
     if (!strcmp(f, "64")) return 64;
     if (!strcmp(f, "64n")) return 65;
     if (!strcmp(f, "128")) return 128;
@@ -1464,6 +1586,11 @@ size_t qgemm_workspace_bytes(const QWeights& w, int A_rows, int M_total) {
   const int path = pick_path(M_total, w.E * (w.fmt == 2 ? 3 : 1), w.fmt);
   if (path == 2) return ((size_t)A_rows * (w.K / w.G) * 4 + 255) & ~(size_t)255;  // row sums per group
   if (path == 3) return ((size_t)A_rows * 4 + 255) & ~(size_t)255;                 // row sums over all of K
+  if (w.fmt != 3 && (path == 0 || path == 1)) {
+    // split-K partial sums of the plain epilogues (the SwiGLU one never splits)
+    const int n_ks = decode_splits(((w.N + 127) / 128) * decode_row_tiles(w.fmt, path, M_total, w.E), w.K);
+    if (n_ks > 1) return ((size_t)n_ks * M_total * w.N * 4 + 255) & ~(size_t)255;
+  }
   return 0;
 }
 
@@ -1483,6 +1610,8 @@ hipError_t launch_qgemm(const QGemmArgs& a, hipStream_t s) {
   ka.gather = a.gather;
   ka.seg_offsets = a.seg_offsets;
   ka.out = a.out;
+  ka.part = nullptr;
+  ka.M_total = a.M_total;
   ka.k = a.k;
   ka.nseg = a.nseg;
   ka.S = (w.fmt == 2) ? 3 : 1;

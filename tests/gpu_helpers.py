@@ -76,6 +76,18 @@ def run_delta(d, cfg, w=None):
     return perm, y_perm, out
 
 
+def check_ulp(gpu, ref, what="", floor=1e-3):
+    """|gpu - ref| <= one bf16 ulp of ref + floor * RMS(ref), element by element
+    (a bf16 output rounded once from an accurate fp32 value meets this)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    gpu = np.asarray(gpu, dtype=np.float64)
+    mag = np.abs(ref)
+    ulp = np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - 7.0) * (mag > 0)
+    tol = ulp + floor * np.sqrt(np.mean(ref * ref))
+    bad = np.abs(gpu - ref) > tol
+    assert not bad.any(), f"{what}: {int(bad.sum())} outputs beyond one bf16 ulp, first at {np.argwhere(bad)[0]}"
+
+
 def check_close(gpu, ref, what=""):
     from oracle import compare
     m = compare(gpu, ref)

@@ -146,6 +146,14 @@ def test_grouped_qgemm_workspace(lib):
     assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(d), 32, 64) == 0          # decode-sized: none
     mwq = desc(fmt=q.MOE_W_MWQ_2_3_4, E=8, N=256, K=512, G=128)
     assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(mwq), 4096, 8192) == 0
+    # long K, few channel groups and row tiles (a decode batch's down projection,
+    # 32 rows, N 4096, K 14336): 32 x (2 + 8) work items -> 4 K splits of 28 blocks,
+    # fp32 partial sums [4][32][4096]
+    for fmt in (q.MOE_W_INT4_GROUP, q.MOE_W_MWQ_2_3_4):
+        dn = desc(fmt=fmt, E=8, N=4096, K=14336, G=128)
+        assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(dn), 32, 32) == 4 * 32 * 4096 * 4
+    # enough work items without a split (64 experts, N 2048, K 1024)
+    assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(desc(E=64, N=2048, K=1024, G=128)), 256, 256) == 0
     call = lambda ws, nbytes: lib.moe_grouped_qgemm(ctypes.byref(d), fake(0x1000), 4096, fake(0x2000), 2,  # noqa
                                                     fake(0x3000), 8192, q.MOE_EPI_SWIGLU, fake(0x4000), ws, nbytes,
                                                     None)

@@ -213,6 +213,51 @@ def test_layer_mwq_decode_full(G):
     _layer_parity(G, gen.config("mixtral_mwq_decode"), tokens=np.array([3, 12]))  # full size, sampled
 
 
+@pytest.mark.parametrize("bits", ["drawn", 2, 3, 4, "cycle"])
+def test_layer_mwq_decode_widths(G, bits, monkeypatch):
+    """16-row tiles that take all widths of an expert at once: about 23 rows
+    per expert, so tiles cross the b = 4 / 3 / 2 sub-segment boundaries; some
+    widths absent; the one-width-per-tile kernel gives the same bits.  Besides
+    the layer bar, every output is within one bf16 ulp of the exact value (plus
+    1e-3 RMS for values near zero)."""
+    cfg = gen.config("mixtral_mwq_decode", T=35, H=256, I=512, E=3, k=2, seed=47)
+    d = gen.generate(cfg)
+    if bits == "cycle":
+        d["pair_bits"][:] = (4 - np.arange(d["pair_bits"].size) % 3).reshape(d["pair_bits"].shape)
+    elif bits != "drawn":
+        d["pair_bits"][:] = bits
+    ref = oracle.moe_forward(d, cfg)
+    buf = G.run_layer(d, cfg)
+    assert np.array_equal(buf.perm.seg_offsets.cpu().numpy(), ref["seg_offsets"])
+    out_fused = G.bf16_to_np(buf.out)
+    G.check_close(out_fused, ref["out"], f"mwq widths {bits}")
+    G.check_ulp(out_fused, ref["out"], f"mwq widths {bits}")
+    monkeypatch.setenv("MOE_QGEMM_PATH", "split")
+    out_split = G.bf16_to_np(G.run_layer(d, cfg).out)
+    assert np.array_equal(out_fused, out_split)
+
+
+@pytest.mark.parametrize("name,over", [
+    ("tiny", dict(T=8, E=2, k=1, H=256, I=2048, G=128, seed=71)),          # INT4: down K 2048 -> 2 K splits
+    ("mixtral_mwq_decode", dict(T=6, E=2, k=1, H=256, I=2048, seed=72)),  # nested planes, all widths per tile
+])
+def test_decode_split_k(G, name, over):
+    """A decode batch's down projection with long K and few work items runs as
+    K splits whose fp32 partial sums are added in order; the plain bf16
+    epilogue through the same split is the fp32 result rounded once."""
+    cfg = gen.config(name, **over)
+    d = gen.generate(cfg)
+    gu, dn = G.tiled_layer(d, cfg)
+    buf = G.run_layer(d, cfg, gu, dn)
+    ref = oracle.moe_forward(d, cfg)
+    assert np.array_equal(buf.perm.seg_offsets.cpu().numpy(), ref["seg_offsets"])
+    assert oracle.compare(buf.y_perm.cpu().numpy(), ref["y_perm"])["rel_l2"] < 1e-2
+    G.check_close(G.bf16_to_np(buf.out), ref["out"], name)
+    y16 = G.q.moe_grouped_qgemm(dn, buf.h, buf.perm.seg_offsets, cfg.T * cfg.k, G.q.MOE_EPI_NONE)
+    torch.cuda.synchronize()
+    assert torch.equal(y16, buf.y_perm.to(torch.bfloat16))
+
+
 # ------------------------------------------------------------------- delta
 def _delta_parity(G, cfg, tokens=None):
     d = gen.generate(cfg)
