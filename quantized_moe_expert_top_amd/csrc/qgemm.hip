@@ -273,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
   const int per_xcd = gridDim.x / 8;
   const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
   const int cgk = item / n_rt, rtile = item % n_rt;  // (channel group, K split) major, row tile minor
-  const int cg = cgk / n_ks, ks = cgk % n_ks;
+  const int cg = n_ks == 1 ? cgk : cgk / n_ks, ks = n_ks == 1 ? 0 : cgk % n_ks;
   if (cg >= n_cg) return;
   int seg, m0;
   const int SS = FU ? p.S : 1;  // sub-segments per tile segment
