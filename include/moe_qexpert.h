@@ -164,7 +164,10 @@ moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t 
  * planes, salient_val and base are re-ordered into tiles of 16 output
  * channels x 128 inputs laid out as 64-lane MFMA operand fragments (same byte
  * counts for codes / planes / base); scales, step and salient_idx keep their
- * canonical layout and may be shared between the two descriptors.
+ * canonical layout and may be shared between the two descriptors.  Tiled
+ * MWQ keeps all three planes in `codes` (ENK/2 bytes: per tile block 512 B of
+ * q2, then 256 B of d3, then 256 B of d4, so a block is one contiguous
+ * kilobyte); its plane3 / plane4 are unused (NULL).
  */
 #define MOE_W_INT4_GROUP 1
 #define MOE_W_MWQ_2_3_4 2
@@ -189,9 +192,9 @@ typedef struct moe_wdesc {
   int32_t zero_point;    /* z: 0..15 (INT4, MWQ), 0..3 (DELTA2) */
   int32_t n_salient;     /* DELTA2: salient channels per expert, 0..64 */
   int32_t reserved;
-  const uint8_t* codes;        /* INT4 nibbles | MWQ q2 plane | DELTA2 2-bit codes */
-  const uint8_t* plane3;       /* MWQ d3 plane, else NULL */
-  const uint8_t* plane4;       /* MWQ d4 plane, else NULL */
+  const uint8_t* codes;        /* INT4 nibbles | MWQ q2 plane (tiled: all planes) | DELTA2 2-bit codes */
+  const uint8_t* plane3;       /* MWQ d3 plane (canonical layout), else NULL */
+  const uint8_t* plane4;       /* MWQ d4 plane (canonical layout), else NULL */
   const uint16_t* scales;      /* fp16: [E][N][K/G] (INT4, MWQ) or [E][N] step (DELTA2) */
   const int32_t* salient_idx;  /* DELTA2 [E][n_salient] */
   const uint16_t* salient_val; /* DELTA2 bf16 */

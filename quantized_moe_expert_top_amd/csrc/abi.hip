@@ -58,7 +58,7 @@ moe_status check_desc(const moe_wdesc* w, int layout, bool need_buffers) {
   if (!w->codes || !w->scales) return fail(MOE_ERR_NULL_ARG, "codes or scales is NULL");
   if (!aligned(w->codes, 16)) return fail(MOE_ERR_MISALIGNED, "codes must be 16-byte aligned");
   if (!aligned(w->scales, 2)) return fail(MOE_ERR_MISALIGNED, "scales must be 2-byte aligned");
-  if (w->format == MOE_W_MWQ_2_3_4) {
+  if (w->format == MOE_W_MWQ_2_3_4 && layout == MOE_LAYOUT_CANONICAL) {  // tiled: all planes in codes
     if (!w->plane3 || !w->plane4) return fail(MOE_ERR_NULL_ARG, "MWQ needs plane3 and plane4");
     if (!aligned(w->plane3, 16) || !aligned(w->plane4, 16))
       return fail(MOE_ERR_MISALIGNED, "planes must be 16-byte aligned");
@@ -217,11 +217,11 @@ size_t moe_weight_field_bytes(const moe_wdesc* w, int32_t field) {
   const size_t ENK = (size_t)w->E * w->N * w->K;
   const bool tiled = w->layout == MOE_LAYOUT_TILED;
   switch (field) {
-    case MOE_FIELD_CODES:
-      return w->format == MOE_W_INT4_GROUP ? ENK / 2 : ENK / 4;
+    case MOE_FIELD_CODES:  // tiled MWQ: the three planes of a tile block side by side
+      return (w->format == MOE_W_INT4_GROUP || (tiled && w->format == MOE_W_MWQ_2_3_4)) ? ENK / 2 : ENK / 4;
     case MOE_FIELD_PLANE3:
     case MOE_FIELD_PLANE4:
-      return w->format == MOE_W_MWQ_2_3_4 ? ENK / 8 : 0;
+      return (w->format == MOE_W_MWQ_2_3_4 && !tiled) ? ENK / 8 : 0;
     case MOE_FIELD_SCALES:
       return w->format == MOE_W_DELTA2_SALIENT ? (size_t)w->E * w->N * 2
                                                : (size_t)w->E * w->N * (w->K / w->group_size) * 2;

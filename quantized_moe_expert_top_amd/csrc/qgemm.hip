@@ -300,15 +300,15 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
   // activations: this thread carries (step wv, lane) of each K block
   const rsrc_t ar = make_rsrc(p.A, p.A_bytes);
   const uint32_t aoff = (uint32_t)((src_row(p, c, lane & 15) * p.K + 32 * wv + 8 * (lane >> 4)) * 2 + kb_lo * 256);
-  constexpr uint32_t CB = FMT == 1 ? 1024 : 512;
+  constexpr uint32_t CB = 1024;  // tile block: INT4 codes, or the q2 / d3 / d4 planes at 0 / 512 / 768
   rsrc_t br[2], r3[2], r4[2], sr[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const size_t tile = (size_t)c.e * NT + (wvalid ? (u ? ct1 : ct0) : 0);
     const size_t tb = tile * KBt + kb_lo;      // first tile block of the split
     br[u] = make_rsrc(p.codes + tb * CB, wvalid ? KB * CB : 0);
-    r3[u] = make_rsrc(MW ? p.p3 + tb * 256 : nullptr, MW && wvalid && need3 ? KB * 256 : 0);
-    r4[u] = make_rsrc(MW ? p.p4 + tb * 256 : nullptr, MW && wvalid && need4 ? KB * 256 : 0);
+    r3[u] = make_rsrc(MW ? p.codes + tb * CB + 512 : nullptr, MW && wvalid && need3 ? KB * CB - 512 : 0);
+    r4[u] = make_rsrc(MW ? p.codes + tb * CB + 768 : nullptr, MW && wvalid && need4 ? KB * CB - 768 : 0);
     // scales [channel][group]: rows of KBt * GPB entries, this split's columns from kb_lo * GPB
     sr[u] = make_rsrc(p.scales + (tile * 16) * (size_t)(KBt * GPB) + (size_t)kb_lo * GPB,
                       wvalid ? (16 * KBt * GPB - kb_lo * GPB) * 2 : 0);
@@ -331,8 +331,8 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
         rb[SLOT].c[u] = buf_x4(br[u], 16 * lane, kbi * CB);                              \
       } else {                                                                           \
         rb[SLOT].q[u] = buf_x2(br[u], 8 * lane, kbi * CB);                               \
-        rb[SLOT].d3[u] = buf_x1(r3[u], 4 * lane, kbi * 256);                             \
-        rb[SLOT].d4[u] = buf_x1(r4[u], 4 * lane, kbi * 256);                             \
+        rb[SLOT].d3[u] = buf_x1(r3[u], 4 * lane, kbi * CB);                              \
+        rb[SLOT].d4[u] = buf_x1(r4[u], 4 * lane, kbi * CB);                              \
       }                                                                                  \
       _Pragma("unroll") for (int g = 0; g < GPB; ++g)                                    \
           rsc[SLOT][u][g] = buf_u16(sr[u], soff, (kbi * GPB + g) * 2);                   \
@@ -650,14 +650,14 @@ __global__ __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) void qgemm_p_kernel(KA
   const rsrc_t ar = make_rsrc(p.A, p.A_bytes);
   const uint32_t aoff = (uint32_t)((src_row(p, Ctx{row0, rows, e, bits}, lr) * p.K + 8 * part * NCH) * 2);
 
-  constexpr uint32_t CB = FMT == 1 ? 1024 : 512;
+  constexpr uint32_t CB = 1024;  // tile block: INT4 codes, or the q2 / d3 / d4 planes at 0 / 512 / 768
   rsrc_t br[UT], r3[UT], r4[UT], sr[UT];
 #pragma unroll
   for (int u = 0; u < UT; ++u) {
     const size_t tile = (size_t)e * NT + ct[u];
     br[u] = make_rsrc(p.codes + tile * KB * CB, KB * CB);
-    r3[u] = make_rsrc(FMT == 2 ? p.p3 + tile * KB * 256 : nullptr, FMT == 2 ? KB * 256 : 0);
-    r4[u] = make_rsrc(FMT == 2 ? p.p4 + tile * KB * 256 : nullptr, FMT == 2 ? KB * 256 : 0);
+    r3[u] = make_rsrc(FMT == 2 ? p.codes + tile * KB * CB + 512 : nullptr, FMT == 2 ? KB * CB - 512 : 0);
+    r4[u] = make_rsrc(FMT == 2 ? p.codes + tile * KB * CB + 768 : nullptr, FMT == 2 ? KB * CB - 768 : 0);
     sr[u] = make_rsrc(p.scales + (tile * 16) * (size_t)(KB * GPB), 16 * KB * GPB * 2);
   }
   const uint32_t soff = (uint32_t)((lane & 15) * KB * GPB * 2);
@@ -717,8 +717,8 @@ __global__ __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) void qgemm_p_kernel(KA
         rb[slot].c[u] = buf_x4(br[u], 16 * lane, kb * CB);
       } else {
         rb[slot].q[u] = buf_x2(br[u], 8 * lane, kb * CB);
-        rb[slot].d3[u] = bits >= 3 ? buf_x1(r3[u], 4 * lane, kb * 256) : 0u;
-        rb[slot].d4[u] = bits == 4 ? buf_x1(r4[u], 4 * lane, kb * 256) : 0u;
+        rb[slot].d3[u] = bits >= 3 ? buf_x1(r3[u], 4 * lane, kb * CB) : 0u;
+        rb[slot].d4[u] = bits == 4 ? buf_x1(r4[u], 4 * lane, kb * CB) : 0u;
       }
 #pragma unroll
       for (int g = 0; g < GPB; ++g) rs[slot][u][g] = buf_u16(sr[u], soff, (kb * GPB + g) * 2);

@@ -17,6 +17,10 @@
 //          i at bit 16*(i&1) + 2*P.
 //   1-bit  (256 B): dword at 4*l; with P = 4*t + (i>>1), element i at bit
 //          16*(i&1) + P.
+//   nested MWQ (1 KB, all in `codes`): the q2 plane as 2-bit at byte 0, d3 and
+//          d4 as 1-bit at bytes 512 and 768, so one tile block is one
+//          contiguous kilobyte (read whole by the prefill kernels, plane by
+//          plane by the decode kernel, which skips the planes it needs not).
 //   bf16 base (4 KB, no expert index): 16 bytes at 1024*t + 16*l hold the 8
 //          inputs in order.
 //   salient values: per (e, ct) ceil(S/32) blocks of 1 KB; lane l holds slots
@@ -61,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void repack_u4_kernel(const uint8_t* __re
 // 2-bit plane, one 128-thread workgroup per 512-byte tile block; zero_code >= 0
 // replaces the codes of salient channels (2-bit delta).
 __global__ __launch_bounds__(128) void repack_u2_kernel(const uint8_t* __restrict__ src, int N, int K,
-                                                        uint32_t* __restrict__ dst, const int32_t* sal_idx,
+                                                        uint32_t* __restrict__ dst, int blk_dw, const int32_t* sal_idx,
                                                         int n_sal, int zero_code) {
   __shared__ uint32_t salmask[4];
   const TileIdx ti = tile_of(blockIdx.x, N, K);
@@ -90,11 +94,13 @@ __global__ __launch_bounds__(128) void repack_u2_kernel(const uint8_t* __restric
       o |= f << (16 * (i & 1) + 2 * P);
     }
   }
-  dst[(size_t)blockIdx.x * 128 + threadIdx.x] = o;
+  dst[(size_t)blockIdx.x * blk_dw + threadIdx.x] = o;  // tile blocks blk_dw dwords apart
 }
 
+// d = dword index of the plane; written at dword off_dw of a tile block of blk_dw dwords
 __global__ __launch_bounds__(kThreads) void repack_u1_kernel(const uint8_t* __restrict__ src, int N, int K,
-                                                             uint32_t* __restrict__ dst, size_t ndw) {
+                                                             uint32_t* __restrict__ dst, int blk_dw, int off_dw,
+                                                             size_t ndw) {
   const size_t d = (size_t)blockIdx.x * kThreads + threadIdx.x;
   if (d >= ndw) return;
   const TileIdx ti = tile_of(d / 64, N, K);
@@ -111,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void repack_u1_kernel(const uint8_t* __re
       o |= ((v >> i) & 1u) << (16 * (i & 1) + P);
     }
   }
-  dst[d] = o;
+  dst[(d / 64) * blk_dw + off_dw + d % 64] = o;
 }
 
 __global__ __launch_bounds__(kThreads) void repack_base_kernel(const uint16_t* __restrict__ src, int N, int K,
@@ -172,14 +178,16 @@ hipError_t launch_repack(const QWeights& src, const QWeights& dst, hipStream_t s
   } else {
     const size_t nblk = ENK / (16 * 128);
     const bool delta = src.fmt == 3;
+    // DELTA2: 512-byte blocks of 2-bit codes; MWQ: 1 KB blocks, q2 at dword 0, d3 at 128, d4 at 192
+    const int blk_dw = delta ? 128 : 256;
     hipLaunchKernelGGL(repack_u2_kernel, dim3((unsigned)nblk), dim3(128), 0, s, src.codes, src.N, src.K, codes,
-                       delta ? src.sal_idx : nullptr, delta ? src.n_sal : 0, delta ? src.z : -1);
+                       blk_dw, delta ? src.sal_idx : nullptr, delta ? src.n_sal : 0, delta ? src.z : -1);
     if (src.fmt == 2) {
       const size_t ndw = ENK / 32;
-      hipLaunchKernelGGL(repack_u1_kernel, dim3(grid_for(ndw)), dim3(kThreads), 0, s, src.p3, src.N, src.K,
-                         reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(dst.p3)), ndw);
-      hipLaunchKernelGGL(repack_u1_kernel, dim3(grid_for(ndw)), dim3(kThreads), 0, s, src.p4, src.N, src.K,
-                         reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(dst.p4)), ndw);
+      hipLaunchKernelGGL(repack_u1_kernel, dim3(grid_for(ndw)), dim3(kThreads), 0, s, src.p3, src.N, src.K, codes,
+                         blk_dw, 128, ndw);
+      hipLaunchKernelGGL(repack_u1_kernel, dim3(grid_for(ndw)), dim3(kThreads), 0, s, src.p4, src.N, src.K, codes,
+                         blk_dw, 192, ndw);
     }
     if (delta) {
       if (src.n_sal > 0) {

@@ -127,7 +127,10 @@ def test_grouped_qgemm_validation(lib):
     assert gemm(lib, desc(z=16)) == BAD_SHAPE
     assert gemm(lib, desc(codes=0)) == NULL_ARG
     assert gemm(lib, desc(codes=0x10008)) == MISALIGNED
-    assert gemm(lib, desc(fmt=q.MOE_W_MWQ_2_3_4, plane3=0)) == NULL_ARG
+    # canonical nested planes need plane3 / plane4; the tiled layout keeps them in codes
+    mwq_src = desc(fmt=q.MOE_W_MWQ_2_3_4, layout=q.MOE_LAYOUT_CANONICAL, plane3=0)
+    mwq_dst = desc(fmt=q.MOE_W_MWQ_2_3_4, codes=0x70000)
+    assert lib.moe_repack_weights(ctypes.byref(mwq_src), ctypes.byref(mwq_dst), None) == NULL_ARG
     assert gemm(lib, desc(fmt=q.MOE_W_DELTA2_SALIENT, z=2, ns=65)) == UNSUPPORTED
     assert gemm(lib, desc(), epi=5) == BAD_FORMAT
     assert gemm(lib, desc(G=16)) == UNSUPPORTED
@@ -171,6 +174,9 @@ def test_weight_field_bytes_and_nested_storage(lib):
     planes = fb(mwq, q.MOE_FIELD_CODES) + fb(mwq, q.MOE_FIELD_PLANE3) + fb(mwq, q.MOE_FIELD_PLANE4)
     assert planes == fb(int4, q.MOE_FIELD_CODES) == E * 2 * I * H // 2
     assert fb(int4, q.MOE_FIELD_PLANE3) == 0
+    mwq_t = desc(fmt=q.MOE_W_MWQ_2_3_4, layout=q.MOE_LAYOUT_TILED, E=E, N=2 * I, K=H, G=G)
+    assert fb(mwq_t, q.MOE_FIELD_CODES) == planes          # tiled: the three planes of a tile block together
+    assert fb(mwq_t, q.MOE_FIELD_PLANE3) == fb(mwq_t, q.MOE_FIELD_PLANE4) == 0
     assert fb(int4, q.MOE_FIELD_SCALES) == E * 2 * I * (H // G) * 2
     tiled = desc(fmt=q.MOE_W_DELTA2_SALIENT, E=16, N=14336, K=4096, z=2, ns=41)
     assert fb(tiled, q.MOE_FIELD_SALIENT_VAL) == 16 * (14336 // 16) * 2 * 1024
