@@ -873,11 +873,50 @@ struct __attribute__((aligned(16))) P2Stage {
 // nothing but LDS-DMA loads.  It needs an even number of groups per channel
 // (K/G); otherwise every K block loads its scales into registers.
 
-template <int EPI, int GPB, bool SL>
+// Nested MWQ in the 128-row kernel: the rows of an expert are cut into
+// 16-row chunks inside each width's sub-segment (b = 4, 3, 2 in grouped
+// order), so that every MFMA row tile has one width, and a workgroup takes 8
+// chunks of one expert.  All planes of a tile block are loaded once for all
+// of them; each row tile multiplies the codes truncated to its width.
+__device__ __forceinline__ int mwq_chunks(const int32_t* so, int e) {
+  const int o0 = so[3 * e], o1 = so[3 * e + 1], o2 = so[3 * e + 2], o3 = so[3 * e + 3];
+  return (o1 - o0 + 15) / 16 + (o2 - o1 + 15) / 16 + (o3 - o2 + 15) / 16;
+}
+// Work item y (in expert order, ceil(chunks / 8) per expert) -> expert e and
+// its chunk group g.
+__device__ __forceinline__ bool find_mwq_group(const int32_t* so, int E, int y, int& e, int& g) {
+  const int lane = threadIdx.x & 63;
+  int carry = 0;
+  for (int s0 = 0; s0 < E; s0 += 64) {
+    const int s = s0 + lane;
+    const int tiles = s < E ? (mwq_chunks(so, s) + 7) / 8 : 0;
+    int incl = tiles;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    const int excl = carry + incl - tiles;
+    const uint64_t b = __ballot(s < E && y >= excl && y < excl + tiles);
+    if (b) {
+      const int src = __ffsll((unsigned long long)b) - 1;
+      e = s0 + src;
+      g = y - __shfl(excl, src, 64);
+      return true;
+    }
+    carry += __shfl(incl, 63, 64);
+  }
+  return false;
+}
+
+template <int EPI, int GPB, bool SL, bool MW>
 __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const float* __restrict__ rowsum, int n_nblk,
                                                               int n_mt, int GM) {
   constexpr int RT = 4, UT = 4, SPG = 4 / GPB;
-  constexpr int V = SL ? 8 : 7 + UT * GPB;  // vector-memory instructions per K block and wavefront
+  // vector-memory instructions per K block and wavefront (MW: four dword loads per code tile)
+  constexpr int NB = MW ? 8 : 2;
+  constexpr int V = SL ? 6 + NB : 5 + NB + UT * GPB;
+  constexpr int PPS = (6 + NB + 3) / 4;  // load parts issued per MFMA step (one scale group per block)
   // one object per stage: the compiler tracks outstanding LDS-DMA writes per
   // LDS object, and only a few objects at a time
   __shared__ P2Stage st0, st1, st2;
@@ -889,11 +928,49 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
   const int grp = item / (GM * n_nblk), rem = item % (GM * n_nblk);
   const int nb = rem / GM, mt = grp * GM + rem % GM;
   if (mt >= n_mt) return;
-  int seg, m0;
-  if (!find_tile(p.seg_offsets, p.nseg, mt, seg, m0, kP2Rows)) return;
-  const Ctx c{uniform(p.seg_offsets[seg] + m0), uniform(min(kP2Rows, p.seg_offsets[seg + 1] - p.seg_offsets[seg] - m0)),
-              uniform(seg), 4};
+  int seg = 0, m0 = 0;
+  if (MW) {
+    if (!find_mwq_group(p.seg_offsets, p.nseg / 3, mt, seg, m0)) return;  // seg = expert, m0 = chunk group
+  } else if (!find_tile(p.seg_offsets, p.nseg, mt, seg, m0, kP2Rows)) {
+    return;
+  }
+  const Ctx c = MW ? Ctx{0, 0, uniform(seg), 4}
+                   : Ctx{uniform(p.seg_offsets[seg] + m0),
+                         uniform(min(kP2Rows, p.seg_offsets[seg + 1] - p.seg_offsets[seg] - m0)), uniform(seg), 4};
   const int KB = p.K / 128, NT = p.N / 16;
+
+  // MW: chunk j (0..7) of the workgroup -> first grouped row, rows (0 past the
+  // expert's last chunk, whose loads then repeat the expert's first row), width
+  int o[4] = {0, 0, 0, 0}, nc[3] = {0, 0, 0};
+  if (MW) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = uniform(p.seg_offsets[3 * c.e + q]);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) nc[q] = (o[q + 1] - o[q] + 15) / 16;
+  }
+  auto chunk = [&](int j, int& start, int& rows, int& bits) {
+    int ci = 8 * m0 + j;
+    start = o[0];
+    rows = 0;
+    bits = 2;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      if (rows == 0 && ci >= 0 && ci < nc[q]) {
+        start = o[q] + 16 * ci;
+        rows = min(16, o[q + 1] - start);
+        bits = 4 - q;
+      }
+      ci -= nc[q];
+    }
+  };
+  // grouped row -> source row of A
+  auto a_row = [&](int gi) -> size_t { return p.gather ? (size_t)(p.gather[gi] / p.k) : (size_t)gi; };
+  // MW: source row of row r (0..127) of the workgroup tile
+  auto mw_src_row = [&](int r) -> size_t {
+    int st, rw, bt;
+    chunk(r >> 4, st, rw, bt);
+    return a_row(st + min(r & 15, max(rw, 1) - 1));
+  };
 
   // workgroup tile j = 4 * (consumer wavefront wn) + u; SwiGLU: u = 0, 1 gate, 2, 3 up
   auto wg_tile = [&](int j, bool& valid) -> int {
@@ -914,7 +991,8 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
   // tiles 2wv, 2wv + 1, row-sum entries 64wv .. 64wv + 63.  Buffer loads: the
   // per-lane offset stays fixed and each K block only moves the scalar offset.
   const rsrc_t ar = make_rsrc(p.A, p.A_bytes);
-  const uint32_t a_off = (uint32_t)(src_row(p, c, 16 * wv + (lane & 15)) * (size_t)p.K * 2 + 16 * (lane >> 4));
+  const uint32_t a_off = (uint32_t)((MW ? mw_src_row(16 * wv + (lane & 15)) : src_row(p, c, 16 * wv + (lane & 15))) *
+                                         (size_t)p.K * 2 + 16 * (lane >> 4));
   rsrc_t br[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -922,11 +1000,30 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
     const int t = wg_tile(2 * wv + q, v);
     br[q] = make_rsrc(p.codes + ((size_t)c.e * NT + t) * (size_t)KB * 1024, KB * 1024);
   }
+  // MW: the four dword loads j = 0..3 of a code tile build, in LDS, lane L's
+  // 16-byte record (q2 dwords 2L and 2L + 1, d3 dword L, d4 dword L) for
+  // L = 16 j .. 16 j + 15: load lane m writes dword m % 4 of record 16 j + m / 4
+  uint32_t bo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int L = 16 * j + (lane >> 2), w = lane & 3;
+    bo[j] = (uint32_t)(w < 2 ? 8 * L + 4 * w : 512 + 256 * (w - 2) + 4 * L);
+  }
   const int ng = KB * GPB;
   const int en = 64 * wv + lane;
   const bool ren = en < 128 * GPB;
   const rsrc_t rr = make_rsrc(rowsum, (p.A_bytes / (2u * p.K)) * ng * 4);
-  const uint32_t r_off = (uint32_t)((src_row(p, c, ren ? (en & 127) : 0) * (size_t)ng + (ren ? (en >> 7) : 0)) * 4);
+  const uint32_t r_off =
+      (uint32_t)(((MW ? mw_src_row(ren ? (en & 127) : 0) : src_row(p, c, ren ? (en & 127) : 0)) * (size_t)ng +
+                  (ren ? (en >> 7) : 0)) * 4);
+  // MW: this wavefront's row tiles (chunks 4wm + rt): codes truncated to their width
+  uint32_t mrt[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    int st, rw, bt;
+    chunk(4 * wm + rt, st, rw, bt);
+    mrt[rt] = uniform(bt == 4 ? 0xFFFFFFFFu : bt == 3 ? 0xFFFEFFFEu : 0xFFFCFFFCu);
+  }
 
   // scale entries: dword 64wv + lane of the stage holds, for GPB <= 2,
   // channel (j, c) = (entry / 16, entry % 16) (entries 256.. are padding, they
@@ -958,34 +1055,25 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
     for (int u = 0; u < UT; ++u) acc[rt][u] = f32x4{};
   uint32_t rsc[3][UT][GPB];  // one register per scale: packing two would wait for both loads
 
-#define P2_ISSUE(S, ST, KBI)                                                                           \
-  {                                                                                                    \
-    const int kbi = (KBI);                                                                             \
-    /* offsets go in the scalar operand: the immediate one would move the LDS address too */          \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, &ST.a[wv][0][0], 16, a_off, kbi * 256, 0, 0);        \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, &ST.a[wv][1][0], 16, a_off, kbi * 256 + 64, 0, 0);   \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, &ST.a[wv][2][0], 16, a_off, kbi * 256 + 128, 0, 0);  \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, &ST.a[wv][3][0], 16, a_off, kbi * 256 + 192, 0, 0);  \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(br[0], &ST.b[2 * wv][0], 16, 16 * lane, kbi * 1024, 0, 0); \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(br[1], &ST.b[2 * wv + 1][0], 16, 16 * lane, kbi * 1024, 0, 0); \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, &ST.r[64 * wv], 4, r_off, kbi * GPB * 4, 0, 0);       \
-    if (SL)                                                                                            \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(scr, &ST.s[64 * wv], 4, s_off,                          \
-                                               GPB == 1 ? 4 * (kbi >> 1) : 4 * kbi * (GPB / 2), 0, 0); \
-    _Pragma("unroll") for (int u = 0; u < UT; ++u) _Pragma("unroll") for (int g = 0; g < GPB; ++g)     \
-        if (!SL) rsc[S][u][g] = buf_u16(sr[u], soff, (kbi * GPB + g) * 2);                             \
-  }
-// Part Q (0..7) of the loads of block KBI into stage ST: activations step
-// 0..3, the two code tiles, row sums, scales; with register scales (!SL) part
-// 7 loads them into slot S.
+#define P2_ISSUE(S, ST, KBI) \
+  _Pragma("unroll") for (int q_ = 0; q_ < 6 + NB; ++q_) P2_PART(S, ST, KBI, q_)
+// Part Q (0 .. 5 + NB) of the loads of block KBI into stage ST: activations
+// step 0..3, the two code tiles (MW: four parts each), row sums, scales; with
+// register scales (!SL) the last part loads them into slot S.  Offsets go in
+// the scalar operand: the immediate one would move the LDS address too.
 #define P2_PART(S, ST, KBI, Q)                                                                         \
   {                                                                                                    \
     const int kbi = (KBI);                                                                             \
     if ((Q) < 4)                                                                                       \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, &ST.a[wv][(Q) & 3][0], 16, a_off, kbi * 256 + 64 * ((Q) & 3), 0, 0); \
-    else if ((Q) < 6)                                                                                  \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(br[(Q) - 4], &ST.b[2 * wv + (Q) - 4][0], 16, 16 * lane, kbi * 1024, 0, 0); \
-    else if ((Q) == 6)                                                                                 \
+    else if ((Q) < 4 + NB) {                                                                           \
+      if (MW)                                                                                          \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(br[((Q) - 4) >> 2], &ST.b[2 * wv + (((Q) - 4) >> 2)][16 * (((Q) - 4) & 3)], \
+                                                 4, bo[((Q) - 4) & 3], kbi * 1024, 0, 0);              \
+      else                                                                                             \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(br[((Q) - 4) & 1], &ST.b[2 * wv + (((Q) - 4) & 1)][0], 16, 16 * lane, \
+                                                 kbi * 1024, 0, 0);                                    \
+    } else if ((Q) == 4 + NB)                                                                          \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, &ST.r[64 * wv], 4, r_off, kbi * GPB * 4, 0, 0);     \
     else if (SL)                                                                                       \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(scr, &ST.s[64 * wv], 4, s_off,                          \
@@ -994,7 +1082,7 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
       _Pragma("unroll") for (int u = 0; u < UT; ++u) _Pragma("unroll") for (int g = 0; g < GPB; ++g)   \
           rsc[S][u][g] = buf_u16(sr[u], soff, (kbi * GPB + g) * 2);                                    \
   }
-// With one scale group per K block the eight load instructions of block i + 2
+// With one scale group per K block the load instructions of block i + 2
 // are spread over the four MFMA steps of block i (a burst of them right after
 // the barrier kept every wavefront waiting at issue); with more groups they
 // are issued together before the block (spreading them costs registers).
@@ -1017,16 +1105,18 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
           __builtin_amdgcn_sched_barrier(0); /* keep these reads ahead of this step's MFMAs */              \
         }                                                                                                  \
         if (DO_ISSUE) {                                                                                    \
-          P2_PART(IS_, IS, IKB, 2 * t)                                                                     \
-          P2_PART(IS_, IS, IKB, 2 * t + 1)                                                                 \
+          _Pragma("unroll") for (int qp = 0; qp < PPS; ++qp)                                               \
+              if (PPS * t + qp < 6 + NB) P2_PART(IS_, IS, IKB, PPS * t + qp)                               \
           __builtin_amdgcn_sched_barrier(0); /* spread the loads over the block's MFMA steps */            \
         }                                                                                                  \
-        bf16x8 bv[UT];                                                                                     \
-        _Pragma("unroll") for (int u = 0; u < UT; ++u) bv[u] = deq_u4(cb[u], t);                           \
+        u32x4 bv[UT];                                                                                      \
+        _Pragma("unroll") for (int u = 0; u < UT; ++u)                                                     \
+            bv[u] = MW ? deq_mwq_bits(u32x2{cb[u][0], cb[u][1]}, cb[u][2], cb[u][3], t, 4)                 \
+                       : __builtin_bit_cast(u32x4, deq_u4(cb[u], t));                                      \
         _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                                \
           const bf16x8 a = as_bf16x8(av[tt & 1][rt]);                                                      \
           _Pragma("unroll") for (int u = 0; u < UT; ++u)                                                   \
-              tmp[rt][u] = mfma16(a, bv[u], tt == 0 ? rv[rt] : tmp[rt][u]);                                \
+              tmp[rt][u] = mfma16(a, as_bf16x8(MW ? and4(bv[u], mrt[rt]) : bv[u]), tt == 0 ? rv[rt] : tmp[rt][u]); \
         }                                                                                                  \
       }                                                                                                    \
       _Pragma("unroll") for (int u = 0; u < UT; ++u) {                                                     \
@@ -1126,12 +1216,18 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
   const int col = lane & 15;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
+    // grouped rows of row tile rt: row0 + 16 rt + .. (a 16-row chunk for MW)
+    int row0 = c.row0 + 64 * wm + 16 * rt, rows = c.rows - 64 * wm - 16 * rt;
+    if (MW) {
+      int bt;
+      chunk(4 * wm + rt, row0, rows, bt);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = 64 * wm + 16 * rt + 4 * (lane >> 4) + r;
-      if (row >= c.rows) continue;
+      const int row = 4 * (lane >> 4) + r;
+      if (row >= rows) continue;
       if (EPI == 1) {
-        uint16_t* orow = static_cast<uint16_t*>(p.out) + (size_t)(c.row0 + row) * p.n_out;
+        uint16_t* orow = static_cast<uint16_t*>(p.out) + (size_t)(row0 + row) * p.n_out;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           if (!cval[h]) continue;
@@ -1142,9 +1238,9 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
 #pragma unroll
         for (int u = 0; u < UT; ++u) {
           if (!cval[u]) continue;
-          const size_t o = (size_t)(c.row0 + row) * p.n_out + ct[u] * 16 + col;
-          if (EPI == 2) static_cast<float*>(p.out)[o] = acc[rt][u][r];
-          else static_cast<uint16_t*>(p.out)[o] = f32_to_bf16(acc[rt][u][r]);
+          const size_t oi = (size_t)(row0 + row) * p.n_out + ct[u] * 16 + col;
+          if (EPI == 2) static_cast<float*>(p.out)[oi] = acc[rt][u][r];
+          else static_cast<uint16_t*>(p.out)[oi] = f32_to_bf16(acc[rt][u][r]);
         }
       }
     }
@@ -1472,16 +1568,17 @@ void launch_p(const KArgs& ka, int M_total, hipStream_t s) {
   }
 }
 
-template <int EPI>
+template <int EPI, bool MW>
 void launch_p2(const KArgs& ka, const float* rowsum, int M_total, hipStream_t s) {
   const int n_nblk = EPI == 1 ? (ka.N / 2 + 127) / 128 : (ka.N + 255) / 256;
-  const int n_mt = (M_total + kP2Rows - 1) / kP2Rows + ka.nseg;
+  // nested MWQ: at most one partial 16-row chunk per width sub-segment, 8 chunks per workgroup
+  const int n_mt = MW ? (M_total / 16 + ka.nseg + 7) / 8 + ka.nseg / 3 : (M_total + kP2Rows - 1) / kP2Rows + ka.nseg;
   const int GM = group_rows(ka, M_total, n_mt, kP2Rows, 1, 4u << 20);  // measured best: about 4 MB
   const int items = n_nblk * ((n_mt + GM - 1) / GM) * GM;
   const dim3 grid((unsigned)(((items + 7) / 8) * 8));
   const dim3 block(kP2Threads);
 #define P2_LAUNCH(GPB, SL) \
-  hipLaunchKernelGGL((qgemm_p2_kernel<EPI, GPB, SL>), grid, block, 0, s, ka, rowsum, n_nblk, n_mt, GM)
+  hipLaunchKernelGGL((qgemm_p2_kernel<EPI, GPB, SL, MW>), grid, block, 0, s, ka, rowsum, n_nblk, n_mt, GM)
   const bool sl = ((ka.K / ka.G) & 1) == 0;
   switch (ka.G) {
     case 128: if (sl) P2_LAUNCH(1, true); else P2_LAUNCH(1, false); break;
@@ -1517,7 +1614,8 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, int A_rows, voi
     const int rows = A_rows;
     hipLaunchKernelGGL(rowsum_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, ka.A, rows, ka.K, ka.G,
                        -(128.0f + (float)ka.z), rs);
-    launch_p2<EPI>(ka, rs, M_total, s);
+    if (fmt == 2) launch_p2<EPI, true>(ka, rs, M_total, s);
+    else launch_p2<EPI, false>(ka, rs, M_total, s);
     return;
   }
   if (fmt != 3 && path != 0 && path != 1) {
@@ -1562,10 +1660,16 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, int A_rows, voi
 // counts): few rows per segment -> 16-row tiles (decode kernel); many -> the
 // 128-row LDS-DMA kernel for INT4, 64-row tiles otherwise (and for INT4
 // segments of under ~96 rows, where 128-row tiles would be mostly padding).
-// For MWQ the 16-row tiles take all widths of an expert together (one read of
-// each bit plane) unless MOE_QGEMM_PATH=split gives each width its own tiles.
-// MOE_QGEMM_PATH=small|split|64|64n|128|dma forces a path.
-int pick_path(int M_total, int nseg, int fmt) {
+// Nested MWQ -> the 128-row kernel over 16-row chunks of every width from
+// about 256 rows per expert for SwiGLU and 512 for the plain epilogues
+// (measured on the Mixtral-shaped layer: with fewer rows, 64-row tiles of one
+// width are as fast or faster, the 128-row kernel leaving many chunks of its
+// last workgroup per expert empty); few rows -> the 16-row tiles, which take
+// all widths of an expert together (one read of each bit plane) unless
+// MOE_QGEMM_PATH=split gives each width its own tiles.
+// MOE_QGEMM_PATH=small|split|64|64n|128|dma forces a path.  The workspace
+// query covers both epilogues (the larger need).
+int pick_path(int M_total, int nseg, int fmt, int epi) {
   if (const char* f = getenv("MOE_QGEMM_PATH")) {
     if (fmt == 3) return !strcmp(f, "dma") ? 3 : 0;
     if (!strcmp(f, "small")) return 0;
@@ -1573,17 +1677,21 @@ int pick_path(int M_total, int nseg, int fmt) {
     if (!strcmp(f, "64")) return 64;
     if (!strcmp(f, "64n")) return 65;
     if (!strcmp(f, "128")) return 128;
-    if (!strcmp(f, "dma") && fmt == 1) return 2;
+    if (!strcmp(f, "dma")) return 2;
   }
   const double avg = (double)M_total / (double)(nseg > 0 ? nseg : 1);
   if (fmt == 3) return avg >= 96.0 ? 3 : 0;  // delta: 128-row LDS-DMA kernel, else 32-row tiles
+  // nested MWQ: the 128-row kernel takes all widths of an expert (16-row chunks per width)
+  if (fmt == 2 && 3.0 * avg >= (epi == 1 ? 256.0 : 512.0)) return 2;
   if (avg < 24.0) return 0;
   return (fmt == 1 && avg >= 96.0) ? 2 : 64;
 }
 }  // namespace
 
 size_t qgemm_workspace_bytes(const QWeights& w, int A_rows, int M_total) {
-  const int path = pick_path(M_total, w.E * (w.fmt == 2 ? 3 : 1), w.fmt);
+  const int nseg = w.E * (w.fmt == 2 ? 3 : 1);
+  // the 128-row MWQ kernel runs from fewer rows with SwiGLU than with plain epilogues
+  const int path = (w.fmt == 2 && pick_path(M_total, nseg, w.fmt, 1) == 2) ? 2 : pick_path(M_total, nseg, w.fmt, 0);
   if (path == 2) return ((size_t)A_rows * (w.K / w.G) * 4 + 255) & ~(size_t)255;  // row sums per group
   if (path == 3) return ((size_t)A_rows * 4 + 255) & ~(size_t)255;                 // row sums over all of K
   if (w.fmt != 3 && (path == 0 || path == 1)) {
@@ -1623,7 +1731,7 @@ hipError_t launch_qgemm(const QGemmArgs& a, hipStream_t s) {
   const bool swiglu = a.epilogue == 1;
   ka.n_out = swiglu ? w.N / 2 : w.N;
   (void)swiglu;
-  const int path = pick_path(a.M_total, a.nseg, w.fmt);
+  const int path = pick_path(a.M_total, a.nseg, w.fmt, a.epilogue);
   if (a.epilogue == 1) launch_epi<1>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, s);
   else if (a.epilogue == 2) launch_epi<2>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, s);
   else launch_epi<0>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, s);

@@ -76,20 +76,37 @@ def run_delta(d, cfg, w=None):
     return perm, y_perm, out
 
 
-def check_ulp(gpu, ref, what="", floor=1e-3):
-    """|gpu - ref| <= one bf16 ulp of ref + floor * RMS(ref), element by element
-    (a bf16 output rounded once from an accurate fp32 value meets this)."""
+def bf16_ulp(ref):
+    """One bf16 ulp of each value of ref (0 for 0)."""
+    mag = np.abs(np.asarray(ref, dtype=np.float64))
+    return np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - 7.0) * (mag > 0)
+
+
+def check_ulp(gpu, ref, what="", floor=5e-3):
+    """|gpu - ref| <= one bf16 ulp of ref + floor * RMS(ref), element by element:
+    a bf16 output rounded once from an accurate fp32 value, where an
+    intermediate h value may have been rounded to the other side of a bf16
+    boundary (up to about 2.5e-3 RMS of the output for one such h)."""
     ref = np.asarray(ref, dtype=np.float64)
     gpu = np.asarray(gpu, dtype=np.float64)
-    mag = np.abs(ref)
-    ulp = np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - 7.0) * (mag > 0)
-    tol = ulp + floor * np.sqrt(np.mean(ref * ref))
+    tol = bf16_ulp(ref) + floor * np.sqrt(np.mean(ref * ref))
     bad = np.abs(gpu - ref) > tol
     assert not bad.any(), f"{what}: {int(bad.sum())} outputs beyond one bf16 ulp, first at {np.argwhere(bad)[0]}"
 
 
 def check_close(gpu, ref, what=""):
+    """The layer bar for bf16 outputs against the exact (fp64) result: relative
+    L2 <= 5e-3, and max-abs <= 2e-2 x RMS counted beyond half a bf16 ulp of
+    each exact value.  That half ulp is the output's own rounding, which no
+    bf16 result avoids: where an output peaks at 9.5 RMS it alone reaches
+    2.2e-2 RMS (layers with one expert per token, or nested widths whose
+    truncated codes are biased)."""
     from oracle import compare
     m = compare(gpu, ref)
-    assert m["rel_l2"] <= REL_L2 and m["max_abs_over_rms"] <= MAX_ABS_OVER_RMS, f"{what}: {m}"
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    rms = np.sqrt(np.mean(r * r)) if r.size else 0.0
+    excess = np.maximum(np.abs(g - r) - 0.5 * bf16_ulp(r), 0.0)
+    m["max_excess_over_rms"] = float(np.max(excess, initial=0.0) / rms) if rms > 0 else float(np.max(excess, initial=0.0))
+    assert m["rel_l2"] <= REL_L2 and m["max_excess_over_rms"] <= MAX_ABS_OVER_RMS, f"{what}: {m}"
     return m

@@ -148,7 +148,9 @@ def test_grouped_qgemm_workspace(lib):
     assert need == 4096 * (512 // 128) * 4
     assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(d), 32, 64) == 0          # decode-sized: none
     mwq = desc(fmt=q.MOE_W_MWQ_2_3_4, E=8, N=256, K=512, G=128)
-    assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(mwq), 4096, 8192) == 0
+    # nested MWQ: 1024 rows per expert take the 128-row kernel; 64 do not
+    assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(mwq), 4096, 8192) == 4096 * (512 // 128) * 4
+    assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(mwq), 256, 512) == 0
     # long K, few channel groups and row tiles (a decode batch's down projection,
     # 32 rows, N 4096, K 14336): 32 x (2 + 8) work items -> 4 K splits of 28 blocks,
     # fp32 partial sums [4][32][4096]

@@ -213,13 +213,48 @@ def test_layer_mwq_decode_full(G):
     _layer_parity(G, gen.config("mixtral_mwq_decode"), tokens=np.array([3, 12]))  # full size, sampled
 
 
+@pytest.mark.parametrize("over", [
+    dict(T=300, E=4, k=2, H=512, I=512, G=64, seed=81),    # ~150 rows per expert: two chunk groups each
+    dict(T=200, E=3, k=2, H=512, I=384, G=32, seed=82),    # 4 scale groups per K block
+    dict(T=150, E=8, k=4, H=512, I=256, G=128, seed=83),   # ~75 rows per expert, ragged chunks
+    dict(T=64, E=2, k=2, H=128, I=128, G=128, seed=84),    # one K block: odd groups per channel, register scales
+])
+def test_layer_mwq_prefill_dma_kernel(G, over, monkeypatch):
+    """Nested planes in the 128-row LDS-DMA kernel (chosen by itself from 256
+    rows per expert for gate/up, 512 for down): 16-row chunks of every width,
+    one expert per workgroup."""
+    monkeypatch.setenv("MOE_QGEMM_PATH", "dma")
+    cfg = gen.config("mixtral_mwq", **over)
+    buf = _layer_parity(G, cfg)
+    G.check_ulp(G.bf16_to_np(buf.out), oracle.moe_forward(gen.generate(cfg), cfg)["out"], str(over))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, "cycle"])
+def test_layer_mwq_prefill_widths(G, bits, monkeypatch):
+    """The 128-row kernel with one width everywhere, or widths cycling per pair
+    (chunks of every width in each workgroup, partial chunks at each end)."""
+    monkeypatch.setenv("MOE_QGEMM_PATH", "dma")
+    cfg = gen.config("mixtral_mwq", T=150, E=3, k=2, H=512, I=1024, seed=85)
+    d = gen.generate(cfg)
+    if bits == "cycle":
+        d["pair_bits"][:] = (4 - np.arange(d["pair_bits"].size) % 3).reshape(d["pair_bits"].shape)
+    else:
+        d["pair_bits"][:] = bits
+    ref = oracle.moe_forward(d, cfg)
+    buf = G.run_layer(d, cfg)
+    assert np.array_equal(buf.perm.seg_offsets.cpu().numpy(), ref["seg_offsets"])
+    out = G.bf16_to_np(buf.out)
+    G.check_close(out, ref["out"], f"mwq prefill widths {bits}")
+    G.check_ulp(out, ref["out"], f"mwq prefill widths {bits}")
+
+
 @pytest.mark.parametrize("bits", ["drawn", 2, 3, 4, "cycle"])
 def test_layer_mwq_decode_widths(G, bits, monkeypatch):
     """16-row tiles that take all widths of an expert at once: about 23 rows
     per expert, so tiles cross the b = 4 / 3 / 2 sub-segment boundaries; some
     widths absent; the one-width-per-tile kernel gives the same bits.  Besides
     the layer bar, every output is within one bf16 ulp of the exact value (plus
-    1e-3 RMS for values near zero)."""
+    5e-3 RMS, see check_ulp)."""
     cfg = gen.config("mixtral_mwq_decode", T=35, H=256, I=512, E=3, k=2, seed=47)
     d = gen.generate(cfg)
     if bits == "cycle":
