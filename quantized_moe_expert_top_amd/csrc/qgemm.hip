@@ -4,13 +4,18 @@
 // Row tiles of a segment are located on the device from seg_offsets (the host
 // never reads counts back), and every kernel streams the tiled weight layout
 // (16 channels x 128 inputs per tile block, see repack.hip) with
-// v_mfma_f32_16x16x32_bf16.  Three kernels:
+// v_mfma_f32_16x16x32_bf16.  The kernels:
 //   qgemm_d_kernel  few rows per segment (decode): 16-row tiles, 4 wavefronts
 //                   x 2 channel tiles each, activations shared through LDS,
-//                   weights and activations prefetched in register rings.
-//   qgemm_p_kernel  many rows per segment (prefill): 64-row tiles, each
-//                   dequantised weight fragment reused for 32 rows.
-//   qgemm_delta_kernel  2-bit delta + salient channels + shared bf16 base.
+//                   weights and activations prefetched in register rings;
+//                   nested MWQ takes all widths of an expert per tile; long K
+//                   with few work items splits K (splitk_reduce_kernel).
+//   qgemm_p_kernel  many rows per segment: 64-row tiles, each dequantised
+//                   weight fragment reused for 64 rows.
+//   qgemm_p2_kernel INT4 (and nested MWQ at large batches) with many rows:
+//                   128-row x 256-channel tiles fed by LDS-DMA only.
+//   qgemm_delta_kernel / qgemm_p2d_kernel  2-bit delta + salient channels +
+//                   shared bf16 base (32-row tiles / 128-row LDS-DMA tiles).
 //
 // Dequantisation is exact and costs under one VALU operation per pair of
 // weights: a code c is dropped into the low mantissa bits of the bf16 number
@@ -21,8 +26,8 @@
 // the per-channel step) multiplies that in fp32 once per group.
 //   INT4 (ExactMoE W4A16):       w = s[n][k/G] * (c - z)
 //   MWQ  (D2MoE MWQ equations):  c_b = 4*q2 + 2*d3*[b>=3] + d4*[b==4]; the
-//                                planes a segment's bit-width does not need are
-//                                never loaded
+//                                decode kernel never loads the planes its
+//                                tile's widths do not need
 //   DELTA2 (ME-Switch):          d = step[n] * (c - z) off the salient
 //                                channels (their codes were zeroed by the
 //                                repack); salient channels are one more MFMA
