@@ -19,6 +19,11 @@ five summarised systems; no page fixes a seed, so the seeds are ours):
   mixtral_mwq     512 tok, H 4096, I 14336, 8 experts, top-2, nested INT2+d3+d4
                   planes g128, per-pair bit-width from {2:0.40, 3:0.35, 4:0.25}
   mixtral_mwq_decode  the same layer at a decode batch of 16 tokens
+  olmoe_mixed_decode  the olmoe_decode layer with a static bit-width per expert
+                  (EdgeMoE expert-wise bit-width adaptation): the experts most
+                  often routed to (Zipf rank) keep 4 bits, the next 3, the rest 2,
+                  in the proportions 0.25 / 0.35 / 0.40; codes packed at their
+                  own width, zero point per expert, group scales U(lo,hi) x 2^(4-b)
   meswitch_delta  256 requests x 16 tok, linear 4096 -> 14336, 16 experts,
                   shared bf16 base N(0,0.02), 2-bit delta codes with per-output
                   channel fp16 step U(0.0005,0.002), 41 salient input channels
@@ -34,7 +39,7 @@ import numpy as np
 __all__ = [
     "MoeConfig", "DeltaConfig", "CONFIGS", "config", "rng_for",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "zipf_probs",
-    "gen_moe_int4", "gen_moe_mwq", "gen_delta_linear",
+    "gen_moe_int4", "gen_moe_mwq", "gen_moe_mixed", "gen_delta_linear",
 ]
 
 # tensor tags: one independent stream per (seed, tag)
@@ -42,7 +47,7 @@ _TAG = {
     "x": 1, "logits": 2, "gu_codes": 3, "gu_scales": 4, "dn_codes": 5,
     "dn_scales": 6, "bits": 7, "base": 8, "d2_codes": 9, "d2_step": 10,
     "sal_idx": 11, "sal_val": 12, "requests": 13, "gu_q2": 14, "gu_d3": 15,
-    "gu_d4": 16, "dn_q2": 17, "dn_d3": 18, "dn_d4": 19,
+    "gu_d4": 16, "dn_q2": 17, "dn_d3": 18, "dn_d4": 19, "expert_bits": 20, "expert_zero": 21,
 }
 
 
@@ -59,12 +64,12 @@ class MoeConfig:
     E: int                 # experts
     k: int                 # experts per token
     G: int                 # quantisation group size along K
-    fmt: str               # "int4" | "mwq"
+    fmt: str               # "int4" | "mwq" | "mixed"
     scale_lo: float
     scale_hi: float
     zipf: Optional[float]  # popularity exponent added to the logits, or None
     seed: int
-    bit_probs: tuple = ()  # mwq: probabilities of bit-widths (2, 3, 4)
+    bit_probs: tuple = ()  # mwq: probabilities of bit-widths (2, 3, 4); mixed: shares of experts at 2, 3, 4 bits
 
     @property
     def pairs(self) -> int:
@@ -104,6 +109,8 @@ CONFIGS = {
                              bit_probs=(0.40, 0.35, 0.25)),
     "mixtral_mwq_decode": MoeConfig("mixtral_mwq_decode", 16, 4096, 14336, 8, 2, 128, "mwq", 0.002, 0.01, None,
                                     406, bit_probs=(0.40, 0.35, 0.25)),
+    "olmoe_mixed_decode": MoeConfig("olmoe_mixed_decode", 32, 2048, 1024, 64, 8, 128, "mixed", 0.002, 0.01, 1.1,
+                                    707, bit_probs=(0.40, 0.35, 0.25)),
     "meswitch_delta": DeltaConfig("meswitch_delta", 256, 16, 4096, 14336, 16, 41, 0.02, 0.002,
                                   0.0005, 0.002, 1.0, 505),
 }
@@ -210,6 +217,61 @@ def gen_moe_mwq(cfg: MoeConfig) -> dict:
     }
 
 
+def expert_widths(cfg: MoeConfig) -> np.ndarray:
+    """Static bit-width per expert (int32 [E], values 2, 3, 4).
+
+    With a popularity bias the experts are ranked by it (expert 0 is the most
+    popular): the top share bit_probs[2] keeps 4 bits, the next bit_probs[1]
+    3 bits, the rest 2.  Without one the widths are a seeded permutation of
+    the same counts.
+    """
+    E = cfg.E
+    p = np.asarray(cfg.bit_probs, dtype=np.float64)
+    p = p / p.sum()
+    n4 = int(round(p[2] * E))
+    n3 = int(round(p[1] * E))
+    n3 = min(n3, E - n4)
+    ranked = np.array([4] * n4 + [3] * n3 + [2] * (E - n4 - n3), dtype=np.int32)
+    if cfg.zipf is None:
+        ranked = ranked[rng_for(cfg.seed, "expert_bits").permutation(E)]
+    return ranked
+
+
+def _bitstream(rng, E, N, K, bits) -> np.ndarray:
+    # expert e: N rows of K codes of bits[e] bits, LSB first; uniform bits give uniform codes
+    return np.concatenate([_bytes(rng, (N * K * int(b) // 8,)) for b in bits]) if E else np.zeros(0, np.uint8)
+
+
+def gen_moe_mixed(cfg: MoeConfig) -> dict:
+    """MoE layer with a static bit-width b_e in {2, 3, 4} per expert, canonical layout.
+
+    expert_bits int32 [E]; expert_zero int32 [E], z_e in {2^(b_e-1) - 1, 2^(b_e-1)}
+    gu_codes uint8 flat: expert e's [2I][H] codes of b_e bits, each row a
+             little-endian bit stream (code k at bits k*b_e .. k*b_e + b_e - 1),
+             experts back to back
+    gu_scales fp16 bits [E][2I][H/G], drawn U(lo, hi) * 2^(4 - b_e)
+    dn_codes / dn_scales likewise for [E][H][I]
+    """
+    assert cfg.fmt == "mixed"
+    T, H, I, E, G = cfg.T, cfg.H, cfg.I, cfg.E, cfg.G
+    s = cfg.seed
+    bits = expert_widths(cfg)
+    zero = (2 ** (bits - 1) - rng_for(s, "expert_zero").integers(0, 2, size=E)).astype(np.int32)
+    mult = (2.0 ** (4 - bits)).astype(np.float64)[:, None, None]
+    return {
+        "x": _normal_bf16(rng_for(s, "x"), (T, H)),
+        "logits": _logits(cfg),
+        "expert_bits": bits,
+        "expert_zero": zero,
+        "gu_codes": _bitstream(rng_for(s, "gu_codes"), E, 2 * I, H, bits),
+        "gu_scales": _f16_bits(rng_for(s, "gu_scales").uniform(cfg.scale_lo, cfg.scale_hi, size=(E, 2 * I, H // G))
+                               * mult),
+        "dn_codes": _bitstream(rng_for(s, "dn_codes"), E, H, I, bits),
+        "dn_scales": _f16_bits(rng_for(s, "dn_scales").uniform(cfg.scale_lo, cfg.scale_hi, size=(E, H, I // G))
+                               * mult),
+    }
+
+
 def gen_delta_linear(cfg: DeltaConfig) -> dict:
     """Shared-base + per-expert 2-bit delta linear layer, canonical layout.
 
@@ -242,6 +304,8 @@ def gen_delta_linear(cfg: DeltaConfig) -> dict:
 def generate(cfg) -> dict:
     if isinstance(cfg, DeltaConfig):
         return gen_delta_linear(cfg)
+    if cfg.fmt == "mixed":
+        return gen_moe_mixed(cfg)
     return gen_moe_int4(cfg) if cfg.fmt == "int4" else gen_moe_mwq(cfg)
 
 

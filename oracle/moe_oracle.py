@@ -35,6 +35,10 @@ specification, not by code):
   2*(k&3)+1 .. 2*(k&3)); d3 / d4 pack eight 1-bit fields (bit k & 7).
 * DELTA2: d = salient_val if k is salient else step[n] * (c - 2), c in [0, 3],
   packed like q2.
+* Static bit-width per expert (EdgeMoE, expert-wise bit-width adaptation):
+  expert e stores b_e-bit codes, b_e in {2, 3, 4}, with its own zero point:
+  w = scale[n][k // G] * (c - z_e).  Each row of an expert is a little-endian
+  bit stream (code k in bits k*b .. k*b + b - 1); experts are back to back.
 * SwiGLU expert: h = silu(x Wg^T) * (x Wu^T), y = bf16(h) Wd^T, with gate
   rows 0..I-1 and up rows I..2I-1 of the gate_up matrix.  The rounding of h
   to bf16 is the "A16" of W4A16 (ExactMoE) and the 16-bit GEMM of the D2MoE
@@ -126,6 +130,30 @@ def dequant_mwq(q2p, d3p, d4p, scales, G: int, b: int, zero_point: int = 8) -> n
     s = f16_to_f64(scales)
     assert s.shape[-1] * G == c.shape[-1]
     return np.repeat(s, G, axis=-1) * (c - zero_point).astype(F64)
+
+
+def unpack_bits(stream, n_codes: int, b: int) -> np.ndarray:
+    """A little-endian bit stream -> n_codes unsigned codes of b bits each
+    (code k is bits k*b .. k*b + b - 1, bit j of byte i being stream bit 8i + j)."""
+    bitv = np.unpackbits(np.asarray(stream, dtype=np.uint8), bitorder="little")[: n_codes * b].astype(np.int64)
+    return (bitv.reshape(n_codes, b) << np.arange(b, dtype=np.int64)).sum(axis=1)
+
+
+def dequant_per_expert(stream, scales, N: int, K: int, G: int, b: int, zero_point: int) -> np.ndarray:
+    """Expert matrix [N][K] stored at its own bit-width b (EdgeMoE expert-wise
+    bit-width adaptation), exact in float64: w = scale[n][k // G] * (c - z)."""
+    if b not in (2, 3, 4):
+        raise ValueError("bit-width must be 2, 3 or 4")
+    c = unpack_bits(stream, N * K, b).reshape(N, K)
+    s = f16_to_f64(scales)
+    assert s.shape == (N, K // G)
+    return np.repeat(s, G, axis=-1) * (c - zero_point).astype(F64)
+
+
+def expert_stream_offsets(bits, N: int, K: int) -> np.ndarray:
+    """Byte offset of each expert's codes in the flat per-expert stream (E + 1 entries)."""
+    sizes = np.asarray(bits, dtype=np.int64) * N * K // 8
+    return np.concatenate([[0], np.cumsum(sizes)])
 
 
 def dequant_delta2(codes, step, salient_idx, salient_val) -> np.ndarray:
@@ -239,10 +267,20 @@ def _expert_weights_mwq(data, e, G, b):
     return wgu, wd
 
 
+def _expert_weights_mixed(data, e, cfg):
+    b, z = int(data["expert_bits"][e]), int(data["expert_zero"][e])
+    I, H, G = cfg.I, cfg.H, cfg.G
+    og = expert_stream_offsets(data["expert_bits"], 2 * I, H)
+    od = expert_stream_offsets(data["expert_bits"], H, I)
+    wgu = dequant_per_expert(data["gu_codes"][og[e]:og[e + 1]], data["gu_scales"][e], 2 * I, H, G, b, z)
+    wd = dequant_per_expert(data["dn_codes"][od[e]:od[e + 1]], data["dn_scales"][e], H, I, G, b, z)
+    return wgu, wd
+
+
 def moe_forward(data: dict, cfg, tokens=None) -> dict:
     """Full routed-expert layer: route -> group -> per-segment expert FFN -> combine.
 
-    data: a generated workload (INT4 or MWQ).  tokens: optional subset of
+    data: a generated workload (INT4, MWQ or per-expert widths).  tokens: optional subset of
     token indices; routing and grouping always cover all tokens, the expert
     FFN and the combine only the pairs of the chosen tokens (rows of h_perm /
     y_perm for other pairs stay NaN).
@@ -268,6 +306,8 @@ def moe_forward(data: dict, cfg, tokens=None) -> dict:
         e = seg // S
         if mwq:
             wgu, wd = _expert_weights_mwq(data, e, G, 4 - seg % S)
+        elif cfg.fmt == "mixed":
+            wgu, wd = _expert_weights_mixed(data, e, cfg)
         else:
             wgu, wd = _expert_weights_int4(data, e, G)
         toks = sorted_pair[rows] // k

@@ -440,3 +440,99 @@ def test_round_bf16_pins():
     assert np.array_equal(oracle.round_bf16(v.astype(np.float64)), gen.bf16_bits_to_f32(bits).astype(np.float64))
     for x in v[:200]:
         assert oracle.round_bf16(float(x)) == py_bf16(float(x))
+
+
+# ------------------------------------------------- static bit-width per expert
+def _py_bitstream(codes, b):
+    """Pure-Python little-endian packing of b-bit codes (code k at bits k*b ..)."""
+    acc, nbits, out = 0, 0, []
+    for c in codes:
+        acc |= int(c) << nbits
+        nbits += b
+        while nbits >= 8:
+            out.append(acc & 0xFF)
+            acc >>= 8
+            nbits -= 8
+    assert nbits == 0
+    return np.array(out, dtype=np.uint8)
+
+
+@pytest.mark.parametrize("b", [2, 3, 4])
+def test_unpack_bits_against_python_packing(b):
+    rng = random.Random(30 + b)
+    codes = [rng.randrange(1 << b) for _ in range(8 * 24)]
+    got = oracle.unpack_bits(_py_bitstream(codes, b), len(codes), b)
+    assert got.tolist() == codes
+
+
+def test_per_expert_width_reduces_to_int4_and_2bit_layouts():
+    """At 4 bits the little-endian stream is the INT4 nibble layout (even k in
+    the low nibble), at 2 bits the q2 layout: the per-expert dequantisation
+    then equals those formats' (independent decoders)."""
+    rng = np.random.default_rng(12)
+    N, K, G = 6, 32, 8
+    s = gen._f16_bits(rng.uniform(0.01, 0.05, size=(N, K // G)))
+    st4 = rng.integers(0, 256, size=N * K // 2, dtype=np.uint8)
+    w4 = oracle.dequant_per_expert(st4, s, N, K, G, 4, 8)
+    assert np.array_equal(w4, oracle.dequant_int4(st4.reshape(N, K // 2), s, G, 8))
+    st2 = rng.integers(0, 256, size=N * K // 4, dtype=np.uint8)
+    w2 = oracle.dequant_per_expert(st2, s, N, K, G, 2, 1)
+    ref2 = np.repeat(oracle.f16_to_f64(s), G, axis=-1) * (oracle.unpack_u2(st2.reshape(N, K // 4)) - 1)
+    assert np.array_equal(w2, ref2)
+
+
+def test_per_expert_3bit_one_hot_probe():
+    """A 3-bit stream with one nonzero code: only that weight moves off -z * scale."""
+    N, K, G, z = 2, 16, 8, 4
+    codes = [0] * (N * K)
+    codes[K + 11] = 6
+    st = _py_bitstream(codes, 3)
+    s = gen._f16_bits(np.array([[0.5, 0.25], [0.125, 2.0]]))
+    w = oracle.dequant_per_expert(st, s, N, K, G, 3, z)
+    want = np.repeat(oracle.f16_to_f64(s), G, axis=-1) * -z
+    want[1, 11] = 2.0 * (6 - z)
+    assert np.array_equal(w, want)
+
+
+def test_mixed_expert_widths_recipe():
+    cfg = gen.config("olmoe_mixed_decode")
+    d = gen.generate(cfg)
+    bits, zero = d["expert_bits"], d["expert_zero"]
+    assert np.bincount(bits, minlength=5)[2:].tolist() == [26, 22, 16]
+    assert (bits[:16] == 4).all() and (bits[-26:] == 2).all()  # popular experts keep more bits
+    assert ((zero == 2 ** (bits - 1)) | (zero == 2 ** (bits - 1) - 1)).all()
+    assert d["gu_codes"].size == oracle.expert_stream_offsets(bits, 2 * cfg.I, cfg.H)[-1]
+    assert d["dn_codes"].size == oracle.expert_stream_offsets(bits, cfg.H, cfg.I)[-1]
+
+
+def test_moe_forward_matches_dense_bruteforce_mixed():
+    """Per-expert widths: the grouped oracle equals a pure-Python dense evaluation
+    that decodes each expert's bit stream itself."""
+    cfg = gen.config("olmoe_mixed_decode", T=5, H=16, I=8, E=4, k=2, G=8, zipf=None)
+    d = gen.generate(cfg)
+    res = oracle.moe_forward(d, cfg)
+
+    def mat(prefix, e, n_rows, kdim):
+        b, z = int(d["expert_bits"][e]), int(d["expert_zero"][e])
+        start = sum(int(d["expert_bits"][j]) * n_rows * kdim // 8 for j in range(e))
+        raw = d[prefix + "codes"][start:start + b * n_rows * kdim // 8]
+        bitl = [(int(raw[i // 8]) >> (i % 8)) & 1 for i in range(8 * raw.size)]
+        rows = []
+        for n in range(n_rows):
+            row = []
+            for kk in range(kdim):
+                pos = (n * kdim + kk) * b
+                c = sum(bitl[pos + j] << j for j in range(b))
+                row.append(f16_val(int(d[prefix + "scales"][e][n][kk // cfg.G])) * (c - z))
+            rows.append(row)
+        return rows
+    for t in range(cfg.T):
+        xt = [bf16_val(int(v)) for v in d["x"][t]]
+        row = [float(v) for v in d["logits"][t]]
+        order = sorted(range(cfg.E), key=lambda e: (-row[e], e))[:cfg.k]
+        ex = [math.exp(row[e] - row[order[0]]) for e in order]
+        acc = [0.0] * cfg.H
+        for j, e in enumerate(order):
+            y = py_ffn(xt, mat("gu_", e, 2 * cfg.I, cfg.H), mat("dn_", e, cfg.H, cfg.I), cfg.I)
+            acc = [a + ex[j] / sum(ex) * v for a, v in zip(acc, y)]
+        assert rel_err(res["out"][t], acc) < 1e-12
