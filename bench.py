@@ -110,6 +110,9 @@ def main():
             return (q.moe_repack_weights(src),)
         if cfg.fmt == "int4":
             mk = lambda p: q.int4_experts(to_dev(data[p + "codes"]), to_dev(data[p + "scales"]), cfg.G)  # noqa
+        elif cfg.fmt == "mixed":
+            mk = lambda p: q.per_expert_experts(to_dev(data[p + "codes"]), to_dev(data[p + "scales"]),  # noqa
+                                                data["expert_bits"], data["expert_zero"], cfg.G)
         else:
             mk = lambda p: q.mwq_experts(to_dev(data[p + "q2"]), to_dev(data[p + "d3"]),  # noqa
                                          to_dev(data[p + "d4"]), to_dev(data[p + "scales"]), cfg.G)
@@ -205,9 +208,14 @@ def main():
         touched = int((counts > 0).sum())
         rows = T * k
         per_e = weight_bytes_per_expert(cfg, "gate_up")
-        if cfg.fmt == "mwq":
+        if cfg.fmt in ("mwq", "mixed"):
             per_e = None
-        if per_e is None:
+        if cfg.fmt == "mixed":
+            # each touched expert's codes at its own width + scales
+            N, K = 2 * cfg.I, cfg.H
+            wb = sum(N * K * int(data["expert_bits"][e]) // 8 + N * (K // cfg.G) * 2
+                     for e in range(cfg.E) if counts[e] > 0)
+        elif per_e is None:
             # nested planes: q2 + scales always, d3 / d4 only for experts with b >= 3 / b == 4 rows
             segs = np.diff(buf.perm.seg_offsets.cpu().numpy()).reshape(cfg.E, 3)  # b = 4, 3, 2
             N, K = 2 * cfg.I, cfg.H
@@ -225,7 +233,7 @@ def main():
         dom_name = "qgemm gate_up + SwiGLU"
     gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
     tflops = dom_flops / (dom_ms * 1e-3) / 1e12
-    hbm_bound = cfg.name in ("olmoe_decode", "mixtral_mwq_decode", "tiny")
+    hbm_bound = cfg.name in ("olmoe_decode", "mixtral_mwq_decode", "olmoe_mixed_decode", "tiny")
     roofline = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                  "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
                 if hbm_bound else
@@ -286,7 +294,7 @@ def cpu_baseline(cfg, data, target_s):
     T = cfg.T
     # sample: whole batches for small workloads, else a token subset
     sample_tokens = None
-    if cfg.name not in ("olmoe_decode", "mixtral_mwq_decode", "tiny"):
+    if cfg.name not in ("olmoe_decode", "mixtral_mwq_decode", "olmoe_mixed_decode", "tiny"):
         sample_tokens = np.arange(0, T, max(1, T // 16))[:16]
     done = 0
     t0 = time.perf_counter()

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef int32_t moe_status;
 #define MOE_OK 0
@@ -151,6 +151,17 @@ moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t 
  *                    [E][N][K/4] (canonical: field k&3 at bits 2*(k&3)),
  *                    plane3 = d3, plane4 = d4, u8 [E][N][K/8] (bit k&7);
  *                    scales fp16 [E][N][K/G].
+ * MOE_W_INT_PER_EXPERT  static bit-width per expert (EdgeMoE page, expert-wise
+ *                    bit-width adaptation): expert e stores b_e-bit codes,
+ *                    b_e in {2, 3, 4}, with its own zero point z_e in
+ *                    [0, 2^b_e - 1]: w = s[n][k/G] * (c - z_e).  expert_bits
+ *                    and expert_zero (host int32 [E], read on every call)
+ *                    give b_e and z_e; zero_point is ignored; E <= 256.
+ *                    codes u8, experts back to back, expert e's [N][K] codes
+ *                    as one little-endian bit stream per row (code k at bits
+ *                    k*b_e .. k*b_e + b_e - 1): N*K*b_e/8 bytes per expert;
+ *                    scales fp16 [E][N][K/G].  No 8-bit width: 8-bit codes do
+ *                    not fit the exact 16-bit dequantisation of the kernels.
  * MOE_W_DELTA2_SALIENT  ME-Switch delta: d[n][k] = salient value if k is a
  *                    salient input channel of expert e, else
  *                    step[n] * (c - z) with c in [0,3] (z = 2 normally).
@@ -167,11 +178,15 @@ moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t 
  * canonical layout and may be shared between the two descriptors.  Tiled
  * MWQ keeps all three planes in `codes` (ENK/2 bytes: per tile block 512 B of
  * q2, then 256 B of d3, then 256 B of d4, so a block is one contiguous
- * kilobyte); its plane3 / plane4 are unused (NULL).
+ * kilobyte); its plane3 / plane4 are unused (NULL).  Tiled per-expert widths
+ * hold each code shifted to 4 bits (c << (4 - b_e)) as the same three planes,
+ * only the first b_e of them stored: a tile block is 256 * b_e bytes, and each
+ * expert keeps its canonical byte count and offset.
  */
 #define MOE_W_INT4_GROUP 1
 #define MOE_W_MWQ_2_3_4 2
 #define MOE_W_DELTA2_SALIENT 3
+#define MOE_W_INT_PER_EXPERT 4
 
 #define MOE_LAYOUT_CANONICAL 0
 #define MOE_LAYOUT_TILED 1
@@ -199,6 +214,8 @@ typedef struct moe_wdesc {
   const int32_t* salient_idx;  /* DELTA2 [E][n_salient] */
   const uint16_t* salient_val; /* DELTA2 bf16 */
   const uint16_t* base;        /* DELTA2 shared bf16 base [N][K], or NULL */
+  const int32_t* expert_bits;  /* INT_PER_EXPERT: host int32 [E], each 2, 3 or 4; else NULL */
+  const int32_t* expert_zero;  /* INT_PER_EXPERT: host int32 [E], zero point of each expert; else NULL */
 } moe_wdesc;
 
 #define MOE_FIELD_CODES 0

@@ -16,8 +16,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_qexpert.so")
 
-MOE_ABI_VERSION = 1
-MOE_W_INT4_GROUP, MOE_W_MWQ_2_3_4, MOE_W_DELTA2_SALIENT = 1, 2, 3
+MOE_ABI_VERSION = 2
+MOE_W_INT4_GROUP, MOE_W_MWQ_2_3_4, MOE_W_DELTA2_SALIENT, MOE_W_INT_PER_EXPERT = 1, 2, 3, 4
 MOE_LAYOUT_CANONICAL, MOE_LAYOUT_TILED = 0, 1
 MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_NONE_F32 = 0, 1, 2
 MOE_DTYPE_BF16, MOE_DTYPE_F32 = 0, 1
@@ -46,6 +46,7 @@ class WDesc(ctypes.Structure):
         ("codes", ctypes.c_void_p), ("plane3", ctypes.c_void_p), ("plane4", ctypes.c_void_p),
         ("scales", ctypes.c_void_p), ("salient_idx", ctypes.c_void_p), ("salient_val", ctypes.c_void_p),
         ("base", ctypes.c_void_p),
+        ("expert_bits", ctypes.POINTER(ctypes.c_int32)), ("expert_zero", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -182,9 +183,10 @@ def moe_route_permute(logits: torch.Tensor, k: int, pair_bits: torch.Tensor = No
 
 @dataclass
 class QuantizedExperts:
-    """A weight set in one layout; keeps its tensors alive with the descriptor."""
+    """A weight set in one layout; keeps its tensors (and host tables) alive with the descriptor."""
     desc: WDesc
     tensors: dict = field(default_factory=dict)
+    host: dict = field(default_factory=dict)
 
     @property
     def N(self):
@@ -196,14 +198,21 @@ class QuantizedExperts:
 
 
 def make_desc(fmt: int, layout: int, E: int, N: int, K: int, group_size: int, zero_point: int,
-              n_salient: int = 0, **tensors) -> QuantizedExperts:
+              n_salient: int = 0, expert_bits=None, expert_zero=None, **tensors) -> QuantizedExperts:
+    """expert_bits / expert_zero: per-expert widths and zero points (host sequences of E ints)."""
     d = WDesc()
     d.abi_version, d.format, d.layout = MOE_ABI_VERSION, fmt, layout
     d.E, d.N, d.K, d.group_size, d.zero_point, d.n_salient = E, N, K, group_size, zero_point, n_salient
     for name in ("codes", "plane3", "plane4", "scales", "salient_idx", "salient_val", "base"):
         t = tensors.get(name)
         setattr(d, name, _ptr(t) if t is not None else None)
-    return QuantizedExperts(d, {k: v for k, v in tensors.items() if v is not None})
+    host = {}
+    if expert_bits is not None:
+        host["expert_bits"] = (ctypes.c_int32 * E)(*[int(v) for v in expert_bits])
+        host["expert_zero"] = (ctypes.c_int32 * E)(*[int(v) for v in expert_zero])
+        d.expert_bits = ctypes.cast(host["expert_bits"], ctypes.POINTER(ctypes.c_int32))
+        d.expert_zero = ctypes.cast(host["expert_zero"], ctypes.POINTER(ctypes.c_int32))
+    return QuantizedExperts(d, {k: v for k, v in tensors.items() if v is not None}, host)
 
 
 def moe_weight_field_bytes(q: QuantizedExperts, fld: int) -> int:
@@ -214,7 +223,10 @@ def moe_repack_weights(src: QuantizedExperts, stream=None) -> QuantizedExperts:
     """Canonical -> tiled copy of a weight set (offline; allocates the tiled buffers)."""
     s = src.desc
     dev = next(iter(src.tensors.values())).device
-    probe = make_desc(s.format, MOE_LAYOUT_TILED, s.E, s.N, s.K, s.group_size, s.zero_point, s.n_salient)
+    tables = {}
+    if src.host:
+        tables = {"expert_bits": list(src.host["expert_bits"]), "expert_zero": list(src.host["expert_zero"])}
+    probe = make_desc(s.format, MOE_LAYOUT_TILED, s.E, s.N, s.K, s.group_size, s.zero_point, s.n_salient, **tables)
     t = {}
     for name, fld in (("codes", MOE_FIELD_CODES), ("plane3", MOE_FIELD_PLANE3), ("plane4", MOE_FIELD_PLANE4),
                       ("salient_val", MOE_FIELD_SALIENT_VAL)):
@@ -226,7 +238,7 @@ def moe_repack_weights(src: QuantizedExperts, stream=None) -> QuantizedExperts:
     for name in ("scales", "salient_idx"):
         if name in src.tensors:
             t[name] = src.tensors[name]
-    dst = make_desc(s.format, MOE_LAYOUT_TILED, s.E, s.N, s.K, s.group_size, s.zero_point, s.n_salient, **t)
+    dst = make_desc(s.format, MOE_LAYOUT_TILED, s.E, s.N, s.K, s.group_size, s.zero_point, s.n_salient, **tables, **t)
     _check(lib().moe_repack_weights(ctypes.byref(s), ctypes.byref(dst.desc), _stream(stream)), "moe_repack_weights")
     return dst
 
@@ -276,6 +288,15 @@ def mwq_experts(q2, d3, d4, scales, group_size: int, zero_point: int = 8) -> Qua
     E, N, Kq = q2.shape
     return make_desc(MOE_W_MWQ_2_3_4, MOE_LAYOUT_CANONICAL, E, N, 4 * Kq, group_size, zero_point,
                      codes=q2, plane3=d3, plane4=d4, scales=scales)
+
+
+def per_expert_experts(codes, scales, expert_bits, expert_zero, group_size: int) -> QuantizedExperts:
+    """Static width per expert: codes u8 flat (expert e's N x K codes of
+    expert_bits[e] bits, a little-endian bit stream per row, experts back to
+    back), scales fp16 [E][N][K/G], expert_bits / expert_zero host sequences."""
+    E, N, KG = scales.shape
+    return make_desc(MOE_W_INT_PER_EXPERT, MOE_LAYOUT_CANONICAL, E, N, KG * group_size, group_size, 0,
+                     expert_bits=expert_bits, expert_zero=expert_zero, codes=codes, scales=scales)
 
 
 def delta2_experts(codes, step, salient_idx, salient_val, base=None, zero_point: int = 2) -> QuantizedExperts:

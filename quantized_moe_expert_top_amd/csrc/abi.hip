@@ -33,7 +33,7 @@ moe_status check_desc(const moe_wdesc* w, int layout, bool need_buffers) {
   if (!w) return fail(MOE_ERR_NULL_ARG, "weight descriptor is NULL");
   if (w->abi_version != MOE_ABI_VERSION)
     return fail(MOE_ERR_BAD_FORMAT, "descriptor abi_version %d, library %d", w->abi_version, MOE_ABI_VERSION);
-  if (w->format < MOE_W_INT4_GROUP || w->format > MOE_W_DELTA2_SALIENT)
+  if (w->format < MOE_W_INT4_GROUP || w->format > MOE_W_INT_PER_EXPERT)
     return fail(MOE_ERR_BAD_FORMAT, "unknown weight format %d", w->format);
   if (w->layout != layout)
     return fail(MOE_ERR_BAD_FORMAT, "layout %d where %d is required%s", w->layout, layout,
@@ -52,7 +52,18 @@ moe_status check_desc(const moe_wdesc* w, int layout, bool need_buffers) {
     const int G = w->group_size;
     if (!(G == 32 || G == 64 || G == 128))
       return fail(MOE_ERR_UNSUPPORTED, "group_size %d (32, 64 or 128 supported)", G);
-    if (w->zero_point < 0 || w->zero_point > 15) return fail(MOE_ERR_BAD_SHAPE, "zero_point %d", w->zero_point);
+    if (w->format != MOE_W_INT_PER_EXPERT && (w->zero_point < 0 || w->zero_point > 15))
+      return fail(MOE_ERR_BAD_SHAPE, "zero_point %d", w->zero_point);
+  }
+  if (w->format == MOE_W_INT_PER_EXPERT) {  // the tables are needed for sizes as well
+    if (w->E > moe::kMaxMixedExperts)
+      return fail(MOE_ERR_UNSUPPORTED, "E=%d with per-expert widths (at most %d)", w->E, moe::kMaxMixedExperts);
+    if (!w->expert_bits || !w->expert_zero) return fail(MOE_ERR_NULL_ARG, "expert_bits / expert_zero is NULL");
+    for (int e = 0; e < w->E; ++e) {
+      const int b = w->expert_bits[e], z = w->expert_zero[e];
+      if (b < 2 || b > 4) return fail(MOE_ERR_UNSUPPORTED, "expert %d: %d bits (2, 3 or 4 supported)", e, b);
+      if (z < 0 || z >= (1 << b)) return fail(MOE_ERR_BAD_SHAPE, "expert %d: zero point %d for %d bits", e, z, b);
+    }
   }
   if (!need_buffers) return MOE_OK;
   if (!w->codes || !w->scales) return fail(MOE_ERR_NULL_ARG, "codes or scales is NULL");
@@ -82,6 +93,8 @@ moe::QWeights to_q(const moe_wdesc* w) {
   q.G = w->format == MOE_W_DELTA2_SALIENT ? w->K : w->group_size;
   q.z = w->zero_point;
   q.n_sal = w->format == MOE_W_DELTA2_SALIENT ? w->n_salient : 0;
+  q.xbits = w->format == MOE_W_INT_PER_EXPERT ? w->expert_bits : nullptr;
+  q.xzero = w->format == MOE_W_INT_PER_EXPERT ? w->expert_zero : nullptr;
   q.codes = w->codes;
   q.p3 = w->plane3;
   q.p4 = w->plane4;
@@ -218,6 +231,11 @@ size_t moe_weight_field_bytes(const moe_wdesc* w, int32_t field) {
   const bool tiled = w->layout == MOE_LAYOUT_TILED;
   switch (field) {
     case MOE_FIELD_CODES:  // tiled MWQ: the three planes of a tile block side by side
+      if (w->format == MOE_W_INT_PER_EXPERT) {
+        size_t n = 0;
+        for (int e = 0; e < w->E; ++e) n += (size_t)w->N * w->K * w->expert_bits[e] / 8;
+        return n;
+      }
       return (w->format == MOE_W_INT4_GROUP || (tiled && w->format == MOE_W_MWQ_2_3_4)) ? ENK / 2 : ENK / 4;
     case MOE_FIELD_PLANE3:
     case MOE_FIELD_PLANE4:
@@ -245,6 +263,10 @@ moe_status moe_repack_weights(const moe_wdesc* src, const moe_wdesc* dst, void* 
   if (src->format != dst->format || src->E != dst->E || src->N != dst->N || src->K != dst->K ||
       src->group_size != dst->group_size || src->zero_point != dst->zero_point || src->n_salient != dst->n_salient)
     return fail(MOE_ERR_BAD_SHAPE, "source and destination descriptors disagree");
+  if (src->format == MOE_W_INT_PER_EXPERT)
+    for (int e = 0; e < src->E; ++e)
+      if (src->expert_bits[e] != dst->expert_bits[e] || src->expert_zero[e] != dst->expert_zero[e])
+        return fail(MOE_ERR_BAD_SHAPE, "expert %d: source and destination widths or zero points disagree", e);
   if (src->format == MOE_W_DELTA2_SALIENT && ((src->base == nullptr) != (dst->base == nullptr)))
     return fail(MOE_ERR_NULL_ARG, "base given on one side only");
   if (src->codes == dst->codes) return fail(MOE_ERR_BAD_SHAPE, "repack cannot run in place");

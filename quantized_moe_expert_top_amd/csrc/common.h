@@ -136,10 +136,22 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, const 
 hipError_t launch_combine(const void* y, bool y_f32, const int32_t* pos, const float* w, int T, int k, int H,
                           uint16_t* out, hipStream_t s);
 
+// Static per-expert widths (format 4): the kernels get each expert's width,
+// zero point and first tile block (in units of 256 bytes; a tile block of a
+// b-bit expert is 256 * b bytes) by value, in the launch arguments.
+constexpr int kMaxMixedExperts = 256;
+struct XTab {
+  uint8_t bits[kMaxMixedExperts];
+  uint8_t zero[kMaxMixedExperts];
+  uint32_t off[kMaxMixedExperts];
+};
+
 // Weight descriptor as the kernels see it (tiled layout only).
 struct QWeights {
-  int fmt;  // 1 INT4, 2 MWQ, 3 DELTA2
+  int fmt;  // 1 INT4, 2 MWQ, 3 DELTA2, 4 per-expert widths
   int E, N, K, G, z, n_sal;
+  const int32_t* xbits;  // per-expert widths / zero points (host arrays, format 4)
+  const int32_t* xzero;
   const uint8_t* codes;
   const uint8_t* p3;
   const uint8_t* p4;

@@ -265,10 +265,17 @@ struct BRegs {
 // adds the n_ks partials in order.  It gives a long-K GEMM with few channel
 // groups and row tiles (the down projection of a decode batch) enough
 // wavefronts to keep loads in flight.
+//
+// FMT 5 (static width per expert, from `tab`): the codes, shifted to 4 bits,
+// are stored as the nested planes, only the first b of them per tile block
+// (256 * b bytes); the correction uses z << (4 - b) and the group scale is
+// multiplied by 2^(b - 4), both exact.
 template <int FMT, int EPI, int GPB>
-__global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, int n_rt, int n_ks, int kb_per) {
+__global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, int n_rt, int n_ks, int kb_per,
+                                                           XTab tab) {
   constexpr bool MW = FMT != 1;                // nested bit planes
   constexpr bool FU = FMT == 4;                // all widths of an expert per tile
+  constexpr bool FX = FMT == 5;                // one width per expert
   constexpr int SPG = 4 / GPB;                 // MFMA steps per scale group
   constexpr int PF = 3, R = 4;                 // prefetch distance, ring size
   __shared__ u32x4 lds_a[3][4][64];            // [slot][step][lane], 12 KB
@@ -291,6 +298,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
   // FMT 4: rows [.., o1) have b = 4, [o1, o2) b = 3, [o2, ..) b = 2
   const int o1 = FU ? uniform(p.seg_offsets[seg * SS + 1]) : 0;
   const int o2 = FU ? uniform(p.seg_offsets[seg * SS + 2]) : 0;
+  if (FX) c.bits = uniform((int)tab.bits[c.e]);
   const bool need3 = FU ? c.row0 < o2 : c.bits >= 3;
   const bool need4 = FU ? c.row0 < o1 : c.bits == 4;
   const int lrow = c.row0 + (lane & 15);
@@ -305,22 +313,26 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
   // activations: this thread carries (step wv, lane) of each K block
   const rsrc_t ar = make_rsrc(p.A, p.A_bytes);
   const uint32_t aoff = (uint32_t)((src_row(p, c, lane & 15) * p.K + 32 * wv + 8 * (lane >> 4)) * 2 + kb_lo * 256);
-  constexpr uint32_t CB = 1024;  // tile block: INT4 codes, or the q2 / d3 / d4 planes at 0 / 512 / 768
+  // tile block: INT4 codes, or the q2 / d3 / d4 planes at 0 / 512 / 768 (FMT 5: 256 * b bytes)
+  const uint32_t CB = FX ? uniform(256 * c.bits) : 1024u;
+  const uint8_t* codes_e = FX ? p.codes + (size_t)tab.off[c.e] * 256 : p.codes;  // FMT 5: this expert's blocks
   rsrc_t br[2], r3[2], r4[2], sr[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const size_t tile = (size_t)c.e * NT + (wvalid ? (u ? ct1 : ct0) : 0);
-    const size_t tb = tile * KBt + kb_lo;      // first tile block of the split
-    br[u] = make_rsrc(p.codes + tb * CB, wvalid ? KB * CB : 0);
-    r3[u] = make_rsrc(MW ? p.codes + tb * CB + 512 : nullptr, MW && wvalid && need3 ? KB * CB - 512 : 0);
-    r4[u] = make_rsrc(MW ? p.codes + tb * CB + 768 : nullptr, MW && wvalid && need4 ? KB * CB - 768 : 0);
+    const size_t tb = (FX ? tile - (size_t)c.e * NT : tile) * KBt + kb_lo;  // first tile block of the split
+    br[u] = make_rsrc(codes_e + tb * CB, wvalid ? KB * CB : 0);
+    r3[u] = make_rsrc(MW ? codes_e + tb * CB + 512 : nullptr, MW && wvalid && need3 ? KB * CB - 512 : 0);
+    r4[u] = make_rsrc(MW ? codes_e + tb * CB + 768 : nullptr, MW && wvalid && need4 ? KB * CB - 768 : 0);
     // scales [channel][group]: rows of KBt * GPB entries, this split's columns from kb_lo * GPB
     sr[u] = make_rsrc(p.scales + (tile * 16) * (size_t)(KBt * GPB) + (size_t)kb_lo * GPB,
                       wvalid ? (16 * KBt * GPB - kb_lo * GPB) * 2 : 0);
   }
   const uint32_t soff = (uint32_t)((lane & 15) * KBt * GPB * 2);
-  const uint32_t negc = (0xC300u | (uint32_t)p.z) * 0x00010001u;
+  const uint32_t zl = FX ? uniform((int)tab.zero[c.e] << (4 - c.bits)) : (uint32_t)p.z;
+  const uint32_t negc = (0xC300u | zl) * 0x00010001u;
   const bf16x8 neg = as_bf16x8(u32x4{negc, negc, negc, negc});
+  const float smul = FX ? __builtin_ldexpf(1.0f, c.bits - 4) : 1.0f;  // 4-bit-shifted codes: exact
 
   f32x4 acc[2] = {f32x4{}, f32x4{}};
   u32x4 ra[R];
@@ -362,14 +374,14 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
             tm[u] = mfma16(as_bf16x8(and4(araw, m2)), as_bf16x8(and4(b4, 0xFFFCFFFCu)), tm[u]);          \
           } else {                                                                                       \
             const bf16x8 bv = (FMT == 1) ? deq_u4(rb[J].c[u], t)                                         \
-                                         : deq_mwq(rb[J].q[u], rb[J].d3[u], rb[J].d4[u], t, c.bits);     \
+                                         : deq_mwq(rb[J].q[u], rb[J].d3[u], rb[J].d4[u], t, FX ? 4 : c.bits); \
             tm[u] = mfma16(av, bv, tm[u]);                                                               \
           }                                                                                              \
         }                                                                                                \
       }                                                                                                  \
       const int g = t0 / SPG;                                                                            \
       _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                                    \
-        const float sv = f16_to_f32((uint16_t)rsc[J][u][g]);                                             \
+        const float sv = f16_to_f32((uint16_t)rsc[J][u][g]) * smul;                                      \
         _Pragma("unroll") for (int r = 0; r < 4; ++r) acc[u][r] = __builtin_fmaf(sv, tm[u][r], acc[u][r]); \
       }                                                                                                  \
     }                                                                                                    \
@@ -1523,7 +1535,7 @@ int decode_row_tiles(int fmt, int path, int M_total, int E) {
 }
 
 template <int FMT, int EPI>
-void launch_d(const KArgs& ka, int n_cg, int n_rt, hipStream_t s) {
+void launch_d(const KArgs& ka, int n_cg, int n_rt, const XTab& tab, hipStream_t s) {
   const int KBt = ka.K / 128;
   const int n_ks = (EPI == 1 || !ka.part) ? 1 : decode_splits(n_cg * n_rt, ka.K);
   const int kb_per = (KBt + n_ks - 1) / n_ks;
@@ -1531,13 +1543,16 @@ void launch_d(const KArgs& ka, int n_cg, int n_rt, hipStream_t s) {
   const dim3 grid((unsigned)(((items + 7) / 8) * 8));  // multiple of 8: one equal share per XCD
   switch (ka.G) {
     case 128:
-      hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 1>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt, n_ks, kb_per);
+      hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 1>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt, n_ks, kb_per,
+                         tab);
       break;
     case 64:
-      hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 2>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt, n_ks, kb_per);
+      hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 2>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt, n_ks, kb_per,
+                         tab);
       break;
     default:
-      hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 4>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt, n_ks, kb_per);
+      hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 4>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt, n_ks, kb_per,
+                         tab);
       break;
   }
   if (n_ks > 1) {
@@ -1606,7 +1621,8 @@ void launch_p2d(const KArgs& ka, const float* rowsum, int M_total, hipStream_t s
 }
 
 template <int EPI>
-void launch_epi(const KArgs& ka, int fmt, int path, int M_total, int A_rows, void* ws, hipStream_t s) {
+void launch_epi(const KArgs& ka, int fmt, int path, int M_total, int A_rows, void* ws, const XTab& tab,
+                hipStream_t s) {
   if (path == 3 && EPI != 1) {
     float* rs = static_cast<float*>(ws);
     hipLaunchKernelGGL(rowsum_full_kernel, dim3((unsigned)((A_rows + 3) / 4)), dim3(256), 0, s, ka.A, A_rows, ka.K,
@@ -1656,9 +1672,10 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, int A_rows, voi
   KArgs kd = ka;
   if (EPI != 1) kd.part = static_cast<float*>(ws);
   const int n_rt = decode_row_tiles(fmt, path, M_total, ka.nseg / ka.S);
-  if (fmt == 1) launch_d<1, EPI>(kd, gx, n_rt, s);
-  else if (path == 1) launch_d<2, EPI>(kd, gx, n_rt, s);  // one width per tile
-  else launch_d<4, EPI>(kd, gx, n_rt, s);                 // all widths per tile
+  if (fmt == 1) launch_d<1, EPI>(kd, gx, n_rt, tab, s);
+  else if (fmt == 4) launch_d<5, EPI>(kd, gx, n_rt, tab, s);  // a width per expert
+  else if (path == 1) launch_d<2, EPI>(kd, gx, n_rt, tab, s);  // one width per tile
+  else launch_d<4, EPI>(kd, gx, n_rt, tab, s);                 // all widths per tile
 }
 
 // Kernel from the mean rows per segment (the host never sees the device
@@ -1675,6 +1692,7 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, int A_rows, voi
 // MOE_QGEMM_PATH=small|split|64|64n|128|dma forces a path.  The workspace
 // query covers both epilogues (the larger need).
 int pick_path(int M_total, int nseg, int fmt, int epi) {
+  if (fmt == 4) return 0;  // a width per expert: 16-row tiles at every batch size
   if (const char* f = getenv("MOE_QGEMM_PATH")) {
     if (fmt == 3) return !strcmp(f, "dma") ? 3 : 0;
     if (!strcmp(f, "small")) return 0;
@@ -1737,9 +1755,22 @@ hipError_t launch_qgemm(const QGemmArgs& a, hipStream_t s) {
   ka.n_out = swiglu ? w.N / 2 : w.N;
   (void)swiglu;
   const int path = pick_path(a.M_total, a.nseg, w.fmt, a.epilogue);
-  if (a.epilogue == 1) launch_epi<1>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, s);
-  else if (a.epilogue == 2) launch_epi<2>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, s);
-  else launch_epi<0>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, s);
+  // per-expert widths: width, zero point and first 256-byte unit of each expert's tile blocks
+  static const XTab kNoTab{};
+  XTab tab{};
+  if (w.fmt == 4) {
+    uint32_t off = 0;
+    for (int e = 0; e < w.E; ++e) {
+      tab.bits[e] = (uint8_t)w.xbits[e];
+      tab.zero[e] = (uint8_t)w.xzero[e];
+      tab.off[e] = off;
+      off += (uint32_t)((w.N / 16) * (w.K / 128) * w.xbits[e]);
+    }
+  }
+  const XTab& t = w.fmt == 4 ? tab : kNoTab;
+  if (a.epilogue == 1) launch_epi<1>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, t, s);
+  else if (a.epilogue == 2) launch_epi<2>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, t, s);
+  else launch_epi<0>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, t, s);
   return hipGetLastError();
 }
 

@@ -159,6 +159,52 @@ __global__ __launch_bounds__(kThreads) void repack_salient_kernel(const uint16_t
   dst[d] = o;
 }
 
+// Per-expert width b: one expert's N x K codes (little-endian b-bit stream per
+// row) -> its tiled blocks of 256 * b bytes: each code shifted to 4 bits,
+// c4 = c << (4 - b), as the nested planes q2 = c4 >> 2 (2-bit layout), d3 =
+// bit 1 and d4 = bit 0 (1-bit layouts), of which only the first b are stored.
+__global__ __launch_bounds__(kThreads) void repack_mixed_kernel(const uint8_t* __restrict__ src, int N, int K,
+                                                                int b, uint32_t* __restrict__ dst, size_t ndw) {
+  const size_t d = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (d >= ndw) return;
+  const int bdw = 64 * b;  // dwords per tile block
+  const size_t blk = d / bdw;
+  const int w = (int)(d % bdw);
+  const int KB = K / 128;
+  const int kb = (int)(blk % KB), ct = (int)(blk / KB);
+  const size_t row_bits = (size_t)K * b;
+  auto code4 = [&](int ch, int k) -> uint32_t {
+    const size_t pos = (size_t)ch * row_bits + (size_t)k * b;  // bit position in the expert's stream
+    uint32_t v = src[pos >> 3];
+    if ((int)(pos & 7) + b > 8) v |= (uint32_t)src[(pos >> 3) + 1] << 8;
+    return ((v >> (pos & 7)) & ((1u << b) - 1)) << (4 - b);
+  };
+  uint32_t o = 0;
+  if (w < 128) {  // q2: lane l = w / 2, steps 2 (w & 1) and 2 (w & 1) + 1
+    const int l = w >> 1, ch = ct * 16 + (l & 15);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = 2 * (w & 1) + tt;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int P = 4 * tt + (i >> 1);
+        o |= (code4(ch, kb * 128 + 32 * t + 8 * (l >> 4) + i) >> 2) << (16 * (i & 1) + 2 * P);
+      }
+    }
+  } else {  // d3 (w < 192) or d4: lane l = w % 64, all four steps
+    const int l = (w - 128) & 63, ch = ct * 16 + (l & 15);
+    const int sh = w < 192 ? 1 : 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int P = 4 * t + (i >> 1);
+        o |= ((code4(ch, kb * 128 + 32 * t + 8 * (l >> 4) + i) >> sh) & 1u) << (16 * (i & 1) + P);
+      }
+  }
+  dst[d] = o;
+}
+
 inline unsigned grid_for(size_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
 }  // namespace
 
@@ -171,6 +217,18 @@ hipError_t launch_repack(const QWeights& src, const QWeights& dst, hipStream_t s
   const size_t ENK = (size_t)src.E * src.N * src.K;
   if (ENK == 0) return hipSuccess;
   uint32_t* codes = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(dst.codes));
+  if (src.fmt == 4) {  // per expert: canonical and tiled bytes and offsets agree
+    size_t off = 0;
+    for (int e = 0; e < src.E; ++e) {
+      const int b = src.xbits[e];
+      const size_t nbytes = (size_t)src.N * src.K * b / 8;
+      const size_t ndw = nbytes / 4;
+      hipLaunchKernelGGL(repack_mixed_kernel, dim3(grid_for(ndw)), dim3(kThreads), 0, s, src.codes + off, src.N,
+                         src.K, b, reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(dst.codes) + off), ndw);
+      off += nbytes;
+    }
+    return hipGetLastError();
+  }
   if (src.fmt == 1) {
     const size_t ndw = ENK / 8;
     hipLaunchKernelGGL(repack_u4_kernel, dim3(grid_for(ndw)), dim3(kThreads), 0, s, src.codes, src.N, src.K, codes,

@@ -38,9 +38,14 @@ def experts_mwq(d, prefix, G):
     return q.mwq_experts(t(d[prefix + "q2"]), t(d[prefix + "d3"]), t(d[prefix + "d4"]), t(d[prefix + "scales"]), G)
 
 
+def experts_mixed(d, prefix, G):
+    return q.per_expert_experts(t(d[prefix + "codes"]), t(d[prefix + "scales"]), d["expert_bits"],
+                                d["expert_zero"], G)
+
+
 def tiled_layer(d, cfg):
     """Repacked (tiled) gate_up and down weight sets of a generated MoE layer."""
-    mk = experts_int4 if cfg.fmt == "int4" else experts_mwq
+    mk = {"int4": experts_int4, "mwq": experts_mwq, "mixed": experts_mixed}[cfg.fmt]
     gu = q.moe_repack_weights(mk(d, "gu_", cfg.G))
     dn = q.moe_repack_weights(mk(d, "dn_", cfg.G))
     return gu, dn

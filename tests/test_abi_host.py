@@ -107,6 +107,10 @@ def desc(fmt=q.MOE_W_INT4_GROUP, layout=q.MOE_LAYOUT_TILED, E=8, N=256, K=512, G
     d.salient_idx = ptrs.get("salient_idx", 0x50000)
     d.salient_val = ptrs.get("salient_val", 0x60000)
     d.base = ptrs.get("base", None)
+    if "bits" in ptrs:  # per-expert widths: host tables, kept alive on the descriptor object
+        d._tables = ((ctypes.c_int32 * E)(*ptrs["bits"]), (ctypes.c_int32 * E)(*ptrs["zero"]))
+        d.expert_bits = ctypes.cast(d._tables[0], ctypes.POINTER(ctypes.c_int32))
+        d.expert_zero = ctypes.cast(d._tables[1], ctypes.POINTER(ctypes.c_int32))
     return d
 
 
@@ -209,3 +213,24 @@ def test_binding_refuses_missing_library(tmp_path):
     with pytest.raises(ImportError):
         q.load_library(str(tmp_path / "missing.so"))
 
+
+
+def test_per_expert_width_validation_and_sizes(lib):
+    """Static bit-width per expert: tables required and checked; codes hold
+    N*K*b_e/8 bytes per expert in either layout; no planes."""
+    P = q.MOE_W_INT_PER_EXPERT
+    fb = lambda d, f: lib.moe_weight_field_bytes(ctypes.byref(d), f)  # noqa: E731
+    bits, zero = [4, 2, 3, 2], [8, 1, 3, 2]
+    for layout in (q.MOE_LAYOUT_CANONICAL, q.MOE_LAYOUT_TILED):
+        d = desc(fmt=P, layout=layout, E=4, N=256, K=512, bits=bits, zero=zero)
+        assert fb(d, q.MOE_FIELD_CODES) == 256 * 512 * sum(bits) // 8
+        assert fb(d, q.MOE_FIELD_PLANE3) == fb(d, q.MOE_FIELD_PLANE4) == 0
+        assert fb(d, q.MOE_FIELD_SCALES) == 4 * 256 * (512 // 128) * 2
+    assert fb(desc(fmt=P, E=4), q.MOE_FIELD_CODES) == 0                     # tables missing
+    assert gemm(lib, desc(fmt=P, E=4)) == NULL_ARG
+    assert gemm(lib, desc(fmt=P, E=4, bits=[4, 8, 2, 2], zero=[0, 0, 0, 0])) == UNSUPPORTED   # no 8-bit width
+    assert gemm(lib, desc(fmt=P, E=4, bits=[4, 2, 2, 2], zero=[0, 4, 0, 0])) == BAD_SHAPE     # z >= 2^b
+    assert gemm(lib, desc(fmt=P, E=300, bits=[2] * 300, zero=[1] * 300)) == UNSUPPORTED       # E > 256
+    src = desc(fmt=P, layout=q.MOE_LAYOUT_CANONICAL, E=4, bits=bits, zero=zero)
+    dst = desc(fmt=P, E=4, codes=0x70000, bits=bits, zero=[8, 1, 3, 1])
+    assert lib.moe_repack_weights(ctypes.byref(src), ctypes.byref(dst), None) == BAD_SHAPE   # tables disagree

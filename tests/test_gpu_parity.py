@@ -293,6 +293,28 @@ def test_decode_split_k(G, name, over):
     assert torch.equal(y16, buf.y_perm.to(torch.bfloat16))
 
 
+# ------------------------------------------- static bit-width per expert
+def test_layer_mixed_decode_full(G):
+    """OLMoE decode batch with 4 / 3 / 2 bits by expert popularity (EdgeMoE
+    expert-wise bit-width adaptation), every token."""
+    _layer_parity(G, gen.config("olmoe_mixed_decode"))
+
+
+@pytest.mark.parametrize("over", [
+    dict(T=64, E=8, k=2, H=256, I=512, G=64, zipf=None, seed=91),        # widths in a seeded order
+    dict(T=33, E=6, k=3, H=384, I=256, G=32, zipf=None, seed=92),        # 4 groups per K block, ragged
+    dict(T=40, E=4, k=4, H=256, I=256, G=128, zipf=None, seed=93),       # k = E
+    dict(T=8, E=3, k=1, H=256, I=2048, G=128, zipf=None, seed=94),       # down K 2048: split K
+    dict(T=50, E=5, k=2, H=256, I=512, G=128, bit_probs=(1, 0, 0), seed=95),  # every expert 2 bits
+    dict(T=50, E=5, k=2, H=256, I=512, G=128, bit_probs=(0, 1, 0), seed=96),  # every expert 3 bits
+    dict(T=50, E=5, k=2, H=256, I=512, G=128, bit_probs=(0, 0, 1), seed=97),  # every expert 4 bits
+])
+def test_layer_mixed_widths(G, over):
+    cfg = gen.config("olmoe_mixed_decode", **over)
+    buf = _layer_parity(G, cfg)
+    G.check_ulp(G.bf16_to_np(buf.out), oracle.moe_forward(gen.generate(cfg), cfg)["out"], str(over))
+
+
 # ------------------------------------------------------------------- delta
 def _delta_parity(G, cfg, tokens=None):
     d = gen.generate(cfg)
