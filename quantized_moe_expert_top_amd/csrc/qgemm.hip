@@ -34,6 +34,7 @@
 //                                K chunk with bf16 values; the shared base is a
 //                                plain bf16 MFMA on the same A operand
 #include <stdlib.h>
+#include <type_traits>
 #include <string.h>
 
 #include "common.h"
@@ -270,9 +271,21 @@ struct BRegs {
 // are stored as the nested planes, only the first b of them per tile block
 // (256 * b bytes); the correction uses z << (4 - b) and the group scale is
 // multiplied by 2^(b - 4), both exact.
+// The per-expert table travels only with FMT 5: 1.5 KB of launch arguments
+// would slow every launch of the other formats.
+struct NoTab {};
+template <int FMT>
+using TabOf = typename std::conditional<FMT == 5, XTab, NoTab>::type;
+__device__ __forceinline__ int tab_bits(const XTab& t, int e) { return t.bits[e]; }
+__device__ __forceinline__ int tab_zero(const XTab& t, int e) { return t.zero[e]; }
+__device__ __forceinline__ size_t tab_off(const XTab& t, int e) { return t.off[e]; }
+__device__ __forceinline__ int tab_bits(const NoTab&, int) { return 4; }
+__device__ __forceinline__ int tab_zero(const NoTab&, int) { return 0; }
+__device__ __forceinline__ size_t tab_off(const NoTab&, int) { return 0; }
+
 template <int FMT, int EPI, int GPB>
 __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, int n_rt, int n_ks, int kb_per,
-                                                           XTab tab) {
+                                                           TabOf<FMT> tab) {
   constexpr bool MW = FMT != 1;                // nested bit planes
   constexpr bool FU = FMT == 4;                // all widths of an expert per tile
   constexpr bool FX = FMT == 5;                // one width per expert
@@ -298,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
   // FMT 4: rows [.., o1) have b = 4, [o1, o2) b = 3, [o2, ..) b = 2
   const int o1 = FU ? uniform(p.seg_offsets[seg * SS + 1]) : 0;
   const int o2 = FU ? uniform(p.seg_offsets[seg * SS + 2]) : 0;
-  if (FX) c.bits = uniform((int)tab.bits[c.e]);
+  if (FX) c.bits = uniform(tab_bits(tab, c.e));
   const bool need3 = FU ? c.row0 < o2 : c.bits >= 3;
   const bool need4 = FU ? c.row0 < o1 : c.bits == 4;
   const int lrow = c.row0 + (lane & 15);
@@ -315,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
   const uint32_t aoff = (uint32_t)((src_row(p, c, lane & 15) * p.K + 32 * wv + 8 * (lane >> 4)) * 2 + kb_lo * 256);
   // tile block: INT4 codes, or the q2 / d3 / d4 planes at 0 / 512 / 768 (FMT 5: 256 * b bytes)
   const uint32_t CB = FX ? uniform(256 * c.bits) : 1024u;
-  const uint8_t* codes_e = FX ? p.codes + (size_t)tab.off[c.e] * 256 : p.codes;  // FMT 5: this expert's blocks
+  const uint8_t* codes_e = FX ? p.codes + tab_off(tab, c.e) * 256 : p.codes;  // FMT 5: this expert's blocks
   rsrc_t br[2], r3[2], r4[2], sr[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -329,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
                       wvalid ? (16 * KBt * GPB - kb_lo * GPB) * 2 : 0);
   }
   const uint32_t soff = (uint32_t)((lane & 15) * KBt * GPB * 2);
-  const uint32_t zl = FX ? uniform((int)tab.zero[c.e] << (4 - c.bits)) : (uint32_t)p.z;
+  const uint32_t zl = FX ? uniform(tab_zero(tab, c.e) << (4 - c.bits)) : (uint32_t)p.z;
   const uint32_t negc = (0xC300u | zl) * 0x00010001u;
   const bf16x8 neg = as_bf16x8(u32x4{negc, negc, negc, negc});
   const float smul = FX ? __builtin_ldexpf(1.0f, c.bits - 4) : 1.0f;  // 4-bit-shifted codes: exact
@@ -1536,6 +1549,8 @@ int decode_row_tiles(int fmt, int path, int M_total, int E) {
 
 template <int FMT, int EPI>
 void launch_d(const KArgs& ka, int n_cg, int n_rt, const XTab& tab, hipStream_t s) {
+  TabOf<FMT> targ{};
+  if constexpr (FMT == 5) targ = tab;
   const int KBt = ka.K / 128;
   const int n_ks = (EPI == 1 || !ka.part) ? 1 : decode_splits(n_cg * n_rt, ka.K);
   const int kb_per = (KBt + n_ks - 1) / n_ks;
@@ -1544,15 +1559,15 @@ void launch_d(const KArgs& ka, int n_cg, int n_rt, const XTab& tab, hipStream_t 
   switch (ka.G) {
     case 128:
       hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 1>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt, n_ks, kb_per,
-                         tab);
+                         targ);
       break;
     case 64:
       hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 2>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt, n_ks, kb_per,
-                         tab);
+                         targ);
       break;
     default:
       hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 4>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt, n_ks, kb_per,
-                         tab);
+                         targ);
       break;
   }
   if (n_ks > 1) {
