@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="weight copies rotated (0: enough to exceed 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU oracle sample")
+    ap.add_argument("--offload-slots", type=int, default=0,
+                    help="INT4 layers: keep the experts in pinned host memory with this many GPU slots "
+                         "(a separate measurement; routing changes every step)")
     ap.add_argument("--hbm-probe", action="store_true",
                     help="only time a plain 512 MiB device copy (achievable HBM rate; counter calibration)")
     return ap.parse_args()
@@ -86,6 +89,61 @@ def weight_bytes_per_expert(cfg, matrix):
     return N * K // 2 + N * (K // G) * 2
 
 
+def offload_bench(args):
+    """Experts host-resident, `--offload-slots` GPU slots, a new routing every step
+    (16 seeded logit batches of the workload's distribution, in turn): tokens/s with the
+    copies overlapped in hottest-first order and without overlap, hit rate, host-to-device
+    bytes per step.  Its own JSON line; not the layer's headline metric."""
+    import torch
+    import quantized_moe_expert_top_amd as q
+    from quantized_moe_expert_top_amd.offload import OffloadedMoeLayer
+    cfg = gen.config(args.config)
+    if cfg.fmt != "int4":
+        print(json.dumps({"error": "--offload-slots takes an INT4 workload"}))
+        sys.exit(2)
+    data = gen.generate(cfg)
+    gu = q.moe_repack_weights(q.int4_experts(to_dev(data["gu_codes"]), to_dev(data["gu_scales"]), cfg.G))
+    dn = q.moe_repack_weights(q.int4_experts(to_dev(data["dn_codes"]), to_dev(data["dn_scales"]), cfg.G))
+    x = to_dev(data["x"])
+    batches = [to_dev(gen.generate(gen.config(args.config, seed=cfg.seed + 1000 + i))["logits"]) for i in range(16)]
+    res = {}
+    for overlap in (True, False):
+        layer = OffloadedMoeLayer(gu, dn, args.offload_slots)
+        for i in range(args.warmup):
+            layer.forward(x, batches[i % 16], cfg.k, overlap=overlap)
+        torch.cuda.synchronize()
+        hits = experts = copied = 0
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            _, st = layer.forward(x, batches[(args.warmup + i) % 16], cfg.k, overlap=overlap)
+            hits, experts, copied = hits + st.hits, experts + st.experts, copied + st.bytes_copied
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        res[overlap] = dict(ms=dt / args.steps * 1e3, tps=cfg.T * args.steps / dt, hit=hits / max(experts, 1),
+                            mb=copied / args.steps / 1e6, gbs=copied / dt / 1e9)
+    # the same routings with every expert resident, for context
+    for i in range(3):
+        q.moe_layer_forward(x, batches[i], cfg.k, gu, dn)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        q.moe_layer_forward(x, batches[i % 16], cfg.k, gu, dn)
+    torch.cuda.synchronize()
+    resident_ms = (time.perf_counter() - t0) / args.steps * 1e3
+    o, n = res[True], res[False]
+    print(json.dumps({
+        "metric": "routed-expert layer tokens/s with experts in host memory", "value": round(o["tps"], 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(o["ms"], 4), "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}_offload", "slots": args.offload_slots, "experts": cfg.E,
+                   "tokens": cfg.T, "top_k": cfg.k, "routings": 16},
+        "hit_rate": round(o["hit"], 3), "copied_mb_per_step": round(o["mb"], 2),
+        "h2d_gbs": round(o["gbs"], 2),
+        "no_overlap": {"ms_per_step": round(n["ms"], 4), "tokens_s": round(n["tps"], 1)},
+        "all_resident_ms_per_step": round(resident_ms, 4),
+    }))
+
+
 def main():
     args = parse()
     if args.hbm_probe:
@@ -94,6 +152,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.offload_slots:
+        offload_bench(args)
+        return
     import torch
     import quantized_moe_expert_top_amd as q
 

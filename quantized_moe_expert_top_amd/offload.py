@@ -1,11 +1,13 @@
 """Host-resident experts with a GPU slot cache (expert offload on one GPU).
 
 The routed experts' tiled INT4 weights live in pinned host memory; the GPU
-holds `n_slots` expert slots.  Each layer step routes and groups on the GPU,
-reads the per-expert counts back, and then walks the touched experts hottest
-first: an expert already in a slot is computed at once, a missing one is
-copied into a free or least recently used slot on a copy stream while the
-experts before it are computed, and its GEMMs wait only for its own copy.
+holds `n_slots` expert slots.  Each layer step routes on the GPU and reads the
+expert ids back; the host gives every touched expert a slot (hits keep
+theirs, misses take a free or the least recently used slot) and queues the
+misses' copies hottest first on a copy stream.  The pairs are grouped by
+(phase, slot): phase 0 holds the experts already resident, phase 1 the ones
+being copied, so one grouped GEMM over the slots computes every resident
+expert while the copies run, and a second one the copied experts after them.
 
 Pages: D2MoE (bit-width-aware I/O-compute pipeline: Load E2 in parallel with
 Compute E1; HEBF, the hottest expert first), ExactMoE (GPU-resident slot cache
@@ -13,9 +15,10 @@ with host-resident experts), EdgeMoE (expert buffer for experts kept in
 external storage).  With INT4 weights there is no bit order to follow inside
 an expert.
 
-Host logic only: every arithmetic step runs in the library's kernels (the
-grouped GEMM on a one-expert view of a slot, then the combine over all
-pairs); copies are stream-ordered host-to-device copies from pinned memory.
+Host logic only: every arithmetic step runs in the library's kernels
+(routing, grouping, the grouped GEMMs on the slot buffer, the combine); the
+host remaps expert ids to grouping keys and issues stream-ordered copies from
+pinned memory.
 """
 from __future__ import annotations
 
@@ -23,8 +26,10 @@ import dataclasses
 
 import torch
 
+import numpy as np
+
 from . import (MOE_EPI_NONE_F32, MOE_EPI_SWIGLU, MOE_LAYOUT_TILED, MOE_W_INT4_GROUP, QuantizedExperts,
-               make_desc, moe_grouped_qgemm, moe_route_permute, moe_unpermute_combine)
+               make_desc, moe_grouped_qgemm, moe_permute, moe_route_topk, moe_unpermute_combine)
 
 
 @dataclasses.dataclass
@@ -50,9 +55,9 @@ class _HostExperts:
         self.host_scales.copy_(scales)
         self.slot_codes = torch.empty((n_slots, codes.shape[1]), dtype=codes.dtype, device=device)
         self.slot_scales = torch.empty((n_slots, scales.shape[1]), dtype=scales.dtype, device=device)
-        # a one-expert descriptor per slot: the grouped GEMM runs on it unchanged
-        self.views = [make_desc(MOE_W_INT4_GROUP, MOE_LAYOUT_TILED, 1, self.N, self.K, self.G, self.z,
-                                codes=self.slot_codes[s], scales=self.slot_scales[s]) for s in range(n_slots)]
+        # the slots as an S-expert weight set: the grouped GEMM runs on it unchanged
+        self.view = make_desc(MOE_W_INT4_GROUP, MOE_LAYOUT_TILED, n_slots, self.N, self.K, self.G, self.z,
+                              codes=self.slot_codes, scales=self.slot_scales)
         self.expert_bytes = codes.shape[1] * codes.element_size() + scales.shape[1] * scales.element_size()
 
     def copy_in(self, e: int, s: int):
@@ -103,43 +108,48 @@ class OffloadedMoeLayer:
         expert before computing any (the load-then-compute baseline)."""
         T = x.shape[0]
         P = T * k
-        ids, w, perm = moe_route_permute(logits, k)
-        counts = perm.counts.cpu()  # the host schedules the copies from the counts
+        S = self.S
+        ids, w = moe_route_topk(logits, k)
+        ids_h = ids.cpu().numpy()  # the host schedules the copies from the routing
+        counts = np.bincount(ids_h.ravel(), minlength=self.E)
         hot = sorted((e for e in range(self.E) if counts[e] > 0), key=lambda e: (-int(counts[e]), e))
-        if len(hot) > self.S:
-            raise ValueError(f"{len(hot)} experts touched, {self.S} slots")
+        if len(hot) > S:
+            raise ValueError(f"{len(hot)} experts touched, {S} slots")
         self.step += 1
         misses = self._assign(hot)
         stats = OffloadStats(len(hot), len(hot) - len(misses), len(misses) * (self.gu.expert_bytes +
                                                                              self.dn.expert_bytes))
+        # grouping key of a pair: its expert's slot, plus S if that expert is being copied
+        key_of = np.zeros(self.E, dtype=np.int32)
+        for e in hot:
+            key_of[e] = self.slot_of[e]
+        for e in misses:
+            key_of[e] += S
+        keys = torch.from_numpy(key_of[ids_h]).to(x.device)
+        perm = moe_permute(keys, 2 * S)
         compute = torch.cuda.current_stream()
         # the copies may overwrite slots that earlier work still reads
         self.copy_stream.wait_stream(compute)
-        ready = {}
-        with torch.cuda.stream(self.copy_stream):
-            for e in misses:
-                s = self.slot_of[e]
-                self.gu.copy_in(e, s)
-                self.dn.copy_in(e, s)
-                ev = torch.cuda.Event()
-                ev.record(self.copy_stream)
-                ready[e] = ev
-        if not overlap and misses:
-            compute.wait_event(ready[misses[-1]])
-        # expert e's rows are [first[e], first[e] + counts[e]) of the grouped order; each
-        # expert's GEMMs run on views that start at its first row, with its own segment [0, c)
-        first = [0] * (self.E + 1)
-        for e in range(self.E):
-            first[e + 1] = first[e] + int(counts[e])
-        segs = torch.tensor([[0, int(counts[e])] for e in hot], dtype=torch.int32).to(x.device, non_blocking=True)
+        done = None
+        if misses:
+            with torch.cuda.stream(self.copy_stream):
+                for e in misses:  # hottest first
+                    s = self.slot_of[e]
+                    self.gu.copy_in(e, s)
+                    self.dn.copy_in(e, s)
+                done = torch.cuda.Event()
+                done.record(self.copy_stream)
+            if not overlap:
+                compute.wait_event(done)
         h = torch.empty((P, self.I), dtype=torch.bfloat16, device=x.device)
         y = torch.empty((P, self.H), dtype=torch.float32, device=x.device)
-        for j, e in enumerate(hot):
-            if overlap and e in ready:
-                compute.wait_event(ready[e])
-            s, r0, c = self.slot_of[e], first[e], int(counts[e])
-            moe_grouped_qgemm(self.gu.views[s], x, segs[j], c, MOE_EPI_SWIGLU, gather_pair=perm.sorted_pair[r0:],
-                              k=k, out=h[r0:])
-            moe_grouped_qgemm(self.dn.views[s], h[r0:r0 + c], segs[j], c, MOE_EPI_NONE_F32, out=y[r0:])
+        for phase in (0, 1):
+            if phase == 1:
+                if not misses:
+                    break
+                compute.wait_event(done)
+            seg = perm.seg_offsets[phase * S:phase * S + S + 1]  # rows of this phase's slots
+            moe_grouped_qgemm(self.gu.view, x, seg, P, MOE_EPI_SWIGLU, gather_pair=perm.sorted_pair, k=k, out=h)
+            moe_grouped_qgemm(self.dn.view, h, seg, P, MOE_EPI_NONE_F32, out=y)
         out = moe_unpermute_combine(y, perm.pair_pos, w, T, k)
         return out, stats
