@@ -106,21 +106,26 @@ def offload_bench(args):
     dn = q.moe_repack_weights(q.int4_experts(to_dev(data["dn_codes"]), to_dev(data["dn_scales"]), cfg.G))
     x = to_dev(data["x"])
     batches = [to_dev(gen.generate(gen.config(args.config, seed=cfg.seed + 1000 + i))["logits"]) for i in range(16)]
+    # the routing of every batch, known ahead (a pre-gating router), for the lookahead variant
+    ahead = [q.moe_route_topk(lg, cfg.k)[0].cpu().numpy() for lg in batches]
     res = {}
-    for overlap in (True, False):
+    for mode in ("overlap", "serial", "lookahead"):
         layer = OffloadedMoeLayer(gu, dn, args.offload_slots)
-        for i in range(args.warmup):
-            layer.forward(x, batches[i % 16], cfg.k, overlap=overlap)
-        torch.cuda.synchronize()
         hits = experts = copied = 0
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            _, st = layer.forward(x, batches[(args.warmup + i) % 16], cfg.k, overlap=overlap)
+        t0 = 0.0
+        for i in range(args.warmup + args.steps):
+            if i == args.warmup:
+                torch.cuda.synchronize()
+                hits = experts = copied = 0
+                t0 = time.perf_counter()
+            _, st = layer.forward(x, batches[i % 16], cfg.k, overlap=mode != "serial")
             hits, experts, copied = hits + st.hits, experts + st.experts, copied + st.bytes_copied
+            if mode == "lookahead":
+                copied += layer.prefetch(ahead[(i + 1) % 16])
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
-        res[overlap] = dict(ms=dt / args.steps * 1e3, tps=cfg.T * args.steps / dt, hit=hits / max(experts, 1),
-                            mb=copied / args.steps / 1e6, gbs=copied / dt / 1e9)
+        res[mode] = dict(ms=dt / args.steps * 1e3, tps=cfg.T * args.steps / dt, hit=hits / max(experts, 1),
+                         mb=copied / args.steps / 1e6, gbs=copied / dt / 1e9)
     # the same routings with every expert resident, for context
     for i in range(3):
         q.moe_layer_forward(x, batches[i], cfg.k, gu, dn)
@@ -130,7 +135,7 @@ def offload_bench(args):
         q.moe_layer_forward(x, batches[i % 16], cfg.k, gu, dn)
     torch.cuda.synchronize()
     resident_ms = (time.perf_counter() - t0) / args.steps * 1e3
-    o, n = res[True], res[False]
+    o, n, la = res["overlap"], res["serial"], res["lookahead"]
     print(json.dumps({
         "metric": "routed-expert layer tokens/s with experts in host memory", "value": round(o["tps"], 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -140,6 +145,8 @@ def offload_bench(args):
         "hit_rate": round(o["hit"], 3), "copied_mb_per_step": round(o["mb"], 2),
         "h2d_gbs": round(o["gbs"], 2),
         "no_overlap": {"ms_per_step": round(n["ms"], 4), "tokens_s": round(n["tps"], 1)},
+        "lookahead": {"ms_per_step": round(la["ms"], 4), "tokens_s": round(la["tps"], 1),
+                      "hit_rate": round(la["hit"], 3), "copied_mb_per_step": round(la["mb"], 2)},
         "all_resident_ms_per_step": round(resident_ms, 4),
     }))
 

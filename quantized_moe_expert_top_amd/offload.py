@@ -79,13 +79,14 @@ class OffloadedMoeLayer:
         self.slot_of: dict[int, int] = {}
         self.expert_in = [-1] * n_slots
         self.last_use = [0] * n_slots
+        self.pending: dict[int, torch.cuda.Event] = {}  # slot -> copy issued ahead of its step
         self.step = 0
         self.copy_stream = torch.cuda.Stream(device=device)  # default priority
 
-    def _assign(self, hot):
+    def _assign(self, hot, keep=()):
         """Slots for this step's experts (hottest first): hits keep theirs; misses take
-        a free slot, else the least recently used one not needed in this step."""
-        needed = set(hot)
+        a free slot, else the least recently used one holding none of `hot` or `keep`."""
+        needed = set(hot) | set(keep)
         misses = []
         for e in hot:
             s = self.slot_of.get(e)
@@ -95,6 +96,8 @@ class OffloadedMoeLayer:
                     s = free[0]
                 else:
                     cand = [j for j in range(self.S) if self.expert_in[j] not in needed]
+                    if not cand:
+                        return None
                     s = min(cand, key=lambda j: self.last_use[j])
                     del self.slot_of[self.expert_in[s]]
                 self.slot_of[e] = s
@@ -117,6 +120,8 @@ class OffloadedMoeLayer:
             raise ValueError(f"{len(hot)} experts touched, {S} slots")
         self.step += 1
         misses = self._assign(hot)
+        if misses is None:
+            raise ValueError("no slot left")
         stats = OffloadStats(len(hot), len(hot) - len(misses), len(misses) * (self.gu.expert_bytes +
                                                                              self.dn.expert_bytes))
         # grouping key of a pair: its expert's slot, plus S if that expert is being copied
@@ -141,6 +146,11 @@ class OffloadedMoeLayer:
                 done.record(self.copy_stream)
             if not overlap:
                 compute.wait_event(done)
+        for e in hot:  # resident experts whose copy was issued ahead
+            ev = self.pending.pop(self.slot_of[e], None)
+            if ev is not None and e not in misses:
+                compute.wait_event(ev)
+        self._current = set(hot)
         h = torch.empty((P, self.I), dtype=torch.bfloat16, device=x.device)
         y = torch.empty((P, self.H), dtype=torch.float32, device=x.device)
         for phase in (0, 1):
@@ -153,3 +163,32 @@ class OffloadedMoeLayer:
             moe_grouped_qgemm(self.dn.view, h, seg, P, MOE_EPI_NONE_F32, out=y)
         out = moe_unpermute_combine(y, perm.pair_pos, w, T, k)
         return out, stats
+
+    def prefetch(self, next_ids) -> int:
+        """Lookahead with routing known ahead (Read-ME page: a pre-gating router
+        routes before the layer runs): copy the experts of the next batch
+        (expert ids, host array [T][k]) that are not resident, hottest first, into
+        slots the current step does not use, on the copy stream, so that they
+        overlap this step's GEMMs.  Call after forward().  Returns bytes queued."""
+        ids_h = np.asarray(next_ids)
+        counts = np.bincount(ids_h.ravel(), minlength=self.E)
+        hot = sorted((e for e in range(self.E) if counts[e] > 0), key=lambda e: (-int(counts[e]), e))
+        current = getattr(self, "_current", set())
+        todo = [e for e in hot if e not in self.slot_of]
+        queued = 0
+        # the copy stream already waited for every step before this one; the
+        # current step's slots are never chosen
+        with torch.cuda.stream(self.copy_stream):
+            for e in todo:
+                got = self._assign([e], keep=current | set(hot))
+                if got is None:
+                    break
+                s = self.slot_of[e]
+                self.last_use[s] = self.step  # the next step uses it
+                self.gu.copy_in(e, s)
+                self.dn.copy_in(e, s)
+                ev = torch.cuda.Event()
+                ev.record(self.copy_stream)
+                self.pending[s] = ev
+                queued += self.gu.expert_bytes + self.dn.expert_bytes
+        return queued
