@@ -361,8 +361,8 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
         rb[SLOT].c[u] = buf_x4(br[u], 16 * lane, kbi * CB);                              \
       } else {                                                                           \
         rb[SLOT].q[u] = buf_x2(br[u], 8 * lane, kbi * CB);                               \
-        rb[SLOT].d3[u] = buf_x1(r3[u], 4 * lane, kbi * CB);                              \
-        rb[SLOT].d4[u] = buf_x1(r4[u], 4 * lane, kbi * CB);                              \
+        rb[SLOT].d3[u] = L3 ? buf_x1(r3[u], 4 * lane, kbi * CB) : 0u;                    \
+        rb[SLOT].d4[u] = L4 ? buf_x1(r4[u], 4 * lane, kbi * CB) : 0u;                    \
       }                                                                                  \
       _Pragma("unroll") for (int g = 0; g < GPB; ++g)                                    \
           rsc[SLOT][u][g] = buf_u16(sr[u], soff, (kbi * GPB + g) * 2);                   \
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
             tm[u] = mfma16(as_bf16x8(and4(araw, m2)), as_bf16x8(and4(b4, 0xFFFCFFFCu)), tm[u]);          \
           } else {                                                                                       \
             const bf16x8 bv = (FMT == 1) ? deq_u4(rb[J].c[u], t)                                         \
-                                         : deq_mwq(rb[J].q[u], rb[J].d3[u], rb[J].d4[u], t, FX ? 4 : c.bits); \
+                                         : deq_mwq(rb[J].q[u], rb[J].d3[u], rb[J].d4[u], t, BW ? BW : 4); \
             tm[u] = mfma16(av, bv, tm[u]);                                                               \
           }                                                                                              \
         }                                                                                                \
@@ -417,23 +417,37 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
     QD_COMPUTE(J, i);                                                  \
   }
 
-  // prologue: activations and weights of K blocks 0..PF-1 in flight, block 0 staged
+  // The K loop, once per code width known at compile time (BW = 2, 3, 4: a
+  // width per tile, FMT 2 and 5; 0 otherwise): a narrower tile neither loads
+  // nor decodes the planes it does not have.
+  auto k_loop = [&](auto bw_tag) {
+    constexpr int BW = decltype(bw_tag)::value;
+    constexpr bool L3 = BW != 2, L4 = BW == 0 || BW == 4;  // d3 / d4 planes loaded
+    // prologue: activations and weights of K blocks 0..PF-1 in flight, block 0 staged
 #pragma unroll
-  for (int j = 0; j < PF; ++j)
-    if (j < KB) QD_ISSUE(j, j);
-  lds_a[0][wv][lane] = ra[0];
-  int kb0 = 0;
-  for (; kb0 + R + PF <= KB; kb0 += R) {
-    QD_STEP_U(0)
-    QD_STEP_U(1)
-    QD_STEP_U(2)
-    QD_STEP_U(3)
-  }
-  for (; kb0 < KB; kb0 += R) {
-    QD_STEP(0)
-    QD_STEP(1)
-    QD_STEP(2)
-    QD_STEP(3)
+    for (int j = 0; j < PF; ++j)
+      if (j < KB) QD_ISSUE(j, j);
+    lds_a[0][wv][lane] = ra[0];
+    int kb0 = 0;
+    for (; kb0 + R + PF <= KB; kb0 += R) {
+      QD_STEP_U(0)
+      QD_STEP_U(1)
+      QD_STEP_U(2)
+      QD_STEP_U(3)
+    }
+    for (; kb0 < KB; kb0 += R) {
+      QD_STEP(0)
+      QD_STEP(1)
+      QD_STEP(2)
+      QD_STEP(3)
+    }
+  };
+  if constexpr (FMT == 2 || FX) {
+    if (c.bits == 2) k_loop(std::integral_constant<int, 2>{});
+    else if (c.bits == 3) k_loop(std::integral_constant<int, 3>{});
+    else k_loop(std::integral_constant<int, 4>{});
+  } else {
+    k_loop(std::integral_constant<int, 0>{});
   }
 #undef QD_ISSUE
 #undef QD_COMPUTE
