@@ -1296,9 +1296,11 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
 // One workgroup of 8 wavefronts per (128-row tile, 128-channel block);
 // wavefront (wm, wn) owns 64 rows x 2 channel tiles, and each activation
 // fragment read from LDS feeds 4 MFMAs: the bf16 base product and the 2-bit
-// delta product of both tiles.  Per K block, two LDS stages hold the 128
-// activation rows, the bf16 base fragments and the 2-bit codes of the 8
-// tiles (68 KB), loaded by LDS-DMA one block ahead.  The delta has one step
+// delta product of both tiles.  The K loop runs over half K blocks (64
+// channels): four LDS stages of 34 KB each hold a half block's 128 activation
+// rows, the bf16 base fragments and the 2-bit codes of the 8 tiles, loaded by
+// LDS-DMA three half blocks ahead (two full-block stages, one block ahead,
+// left the wavefronts waiting on memory about half the time).  The delta has one step
 // per output channel, so its chain runs over all of K: it starts from the
 // row's -(128 + z) * sum_k a_k (one row sum over all of K, from
 // rowsum_full_kernel) and the step multiplies once at the end.  The salient
@@ -1322,16 +1324,16 @@ __global__ __launch_bounds__(256) void rowsum_full_kernel(const uint16_t* __rest
 }
 
 struct __attribute__((aligned(16))) P2DStage {
-  u32x4 a[8][4][64];  // activations [row tile][MFMA step][lane], 32 KB
-  u32x4 b[8][4][64];  // base [tile][MFMA step][lane], 32 KB
-  uint32_t d[8][2][64];  // 2-bit codes [tile][dword][lane], 4 KB
+  u32x4 a[8][2][64];  // activations of half a K block [row tile][MFMA step][lane], 16 KB
+  u32x4 b[8][2][64];  // base [tile][MFMA step][lane], 16 KB
+  uint32_t d[8][64];  // 2-bit codes [tile][lane] (one dword: two MFMA steps), 2 KB
 };
 
 template <int EPI>
 __global__ __launch_bounds__(kP2Threads) void qgemm_p2d_kernel(KArgs p, const float* __restrict__ rowsum, int n_nblk,
                                                                int n_mt, int GM) {
-  constexpr int RT = 4, UT = 2, V = 10;  // V: vector-memory instructions per K block and wavefront
-  __shared__ P2DStage st0, st1;
+  constexpr int RT = 4, UT = 2, V = 5;  // V: vector-memory instructions per half K block and wavefront
+  __shared__ P2DStage st0, st1, st2, st3;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = uniform(tid >> 6), wm = wv >> 2, wn = wv & 3;
 
@@ -1400,28 +1402,29 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2d_kernel(KArgs p, const fl
     }
   }
 
-#define PD_ISSUE(ST, KBI)                                                                                  \
+// half block J: K block J / 2, MFMA steps 2 (J % 2) and 2 (J % 2) + 1
+#define PD_ISSUE(ST, J)                                                                                    \
   {                                                                                                        \
-    const int kbi = (KBI);                                                                                 \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q)                                                          \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, &ST.a[wv][q][0], 16, a_off, kbi * 256 + 64 * q, 0, 0);  \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q)                                                          \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(bsr, &ST.b[wv][q][0], 16, 16 * lane, kbi * 4096 + 1024 * q, 0, 0); \
-    _Pragma("unroll") for (int h = 0; h < 2; ++h)                                                          \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(csr, &ST.d[wv][h][0], 4, 8 * lane, kbi * 512 + 4 * h, 0, 0); \
+    const int kbi = (J) >> 1, hh = (J) & 1;                                                                \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q)                                                          \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, &ST.a[wv][q][0], 16, a_off, kbi * 256 + 64 * (2 * hh + q), 0, 0); \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q)                                                          \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(bsr, &ST.b[wv][q][0], 16, 16 * lane, kbi * 4096 + 1024 * (2 * hh + q), 0, 0); \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(csr, &ST.d[wv][0], 4, 8 * lane, kbi * 512 + 4 * hh, 0, 0);     \
   }
-#define PD_COMPUTE(ST)                                                                                     \
+#define PD_COMPUTE(ST, J)                                                                                  \
   {                                                                                                        \
     u32x2 cd[UT];                                                                                          \
-    _Pragma("unroll") for (int u = 0; u < UT; ++u) cd[u] = u32x2{ST.d[2 * wn + u][0][lane], ST.d[2 * wn + u][1][lane]}; \
-    _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                                        \
+    _Pragma("unroll") for (int u = 0; u < UT; ++u) { const uint32_t w_ = ST.d[2 * wn + u][lane]; cd[u] = u32x2{w_, w_}; } \
+    _Pragma("unroll") for (int tt = 0; tt < 2; ++tt) {                                                     \
+      const int t = 2 * ((J) & 1) + tt;                                                                    \
       bf16x8 bb[UT], bd[UT];                                                                               \
       _Pragma("unroll") for (int u = 0; u < UT; ++u) {                                                     \
-        bb[u] = as_bf16x8(ST.b[2 * wn + u][t][lane]);                                                      \
+        bb[u] = as_bf16x8(ST.b[2 * wn + u][tt][lane]);                                                     \
         bd[u] = deq_u2(cd[u], t);                                                                          \
       }                                                                                                    \
       _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                                  \
-        const bf16x8 av = as_bf16x8(ST.a[4 * wm + rt][t][lane]);                                           \
+        const bf16x8 av = as_bf16x8(ST.a[4 * wm + rt][tt][lane]);                                          \
         _Pragma("unroll") for (int u = 0; u < UT; ++u) {                                                   \
           accb[rt][u] = mfma16(av, bb[u], accb[rt][u]);                                                    \
           accd[rt][u] = mfma16(av, bd[u], accd[rt][u]);                                                    \
@@ -1432,33 +1435,48 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2d_kernel(KArgs p, const fl
   // block i in stage i % 2: wait for this wavefront's loads of block i, the
   // barrier publishes them and retires the other stage, then block i + 1 is
   // issued into it and block i multiplied; the steady state has no branch
-#define PD_STEP_U(CS, IS, I)            \
+  // half block j in stage j % 4, three in flight: before j, wait for this
+  // wavefront's loads of j (those of j + 1 and j + 2 may stay in flight); the
+  // barrier publishes them and retires stage (j - 1) % 4, into which j + 3 goes
+#define PD_STEP_U(CS, IS, J)            \
   {                                     \
     __builtin_amdgcn_sched_barrier(0);  \
-    vm_wait<0>();                       \
+    vm_wait<2 * V>();                   \
     __builtin_amdgcn_s_barrier();       \
-    PD_ISSUE(IS, (I) + 1);              \
-    PD_COMPUTE(CS);                     \
+    PD_ISSUE(IS, (J) + 3);              \
+    PD_COMPUTE(CS, J);                  \
   }
+#define PD_STEP(CS, IS, J)                                   \
+  if ((J) < NH) {                                            \
+    __builtin_amdgcn_sched_barrier(0);                       \
+    if ((J) + 2 < NH) vm_wait<2 * V>();                      \
+    else if ((J) + 1 < NH) vm_wait<V>();                     \
+    else vm_wait<0>();                                       \
+    __builtin_amdgcn_s_barrier();                            \
+    if ((J) + 3 < NH) PD_ISSUE(IS, (J) + 3);                 \
+    PD_COMPUTE(CS, J);                                       \
+  }
+  const int NH = 2 * KB;  // half blocks
   PD_ISSUE(st0, 0);
-  int kb0 = 0;
-  for (; kb0 + 3 <= KB; kb0 += 2) {
-    PD_STEP_U(st0, st1, kb0)
-    PD_STEP_U(st1, st0, kb0 + 1)
+  PD_ISSUE(st1, 1);
+  // unconditional, so the loop's wait counts hold from its first step; with one K
+  // block this half block lies past the end: the buffer resources bound its loads
+  // and no step reads that stage
+  PD_ISSUE(st2, 2);
+  int j0 = 0;
+  for (; j0 + 7 <= NH; j0 += 4) {
+    PD_STEP_U(st0, st3, j0)
+    PD_STEP_U(st1, st0, j0 + 1)
+    PD_STEP_U(st2, st1, j0 + 2)
+    PD_STEP_U(st3, st2, j0 + 3)
   }
-  for (; kb0 < KB; kb0 += 2) {
-    __builtin_amdgcn_sched_barrier(0);
-    vm_wait<0>();
-    __builtin_amdgcn_s_barrier();
-    if (kb0 + 1 < KB) PD_ISSUE(st1, kb0 + 1);
-    PD_COMPUTE(st0);
-    if (kb0 + 1 < KB) {
-      vm_wait<0>();
-      __builtin_amdgcn_s_barrier();
-      if (kb0 + 2 < KB) PD_ISSUE(st0, kb0 + 2);
-      PD_COMPUTE(st1);
-    }
+  for (; j0 < NH; j0 += 4) {
+    PD_STEP(st0, st3, j0)
+    PD_STEP(st1, st0, j0 + 1)
+    PD_STEP(st2, st1, j0 + 2)
+    PD_STEP(st3, st2, j0 + 3)
   }
+#undef PD_STEP
 #undef PD_STEP_U
 #undef PD_COMPUTE
 #undef PD_ISSUE

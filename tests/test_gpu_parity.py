@@ -85,7 +85,8 @@ def test_permute_flags_invalid_ids(G):
     assert p.counts.cpu().numpy().sum() == 5
 
 
-@pytest.mark.parametrize("T,E,k,mwq", [(1, 8, 2, False), (32, 64, 8, False), (64, 64, 8, True), (64, 64, 64, False),
+@pytest.mark.parametrize("T,E,k,mwq", [(1, 8, 2, False), (16, 8, 2, True), (32, 64, 8, False), (64, 64, 8, True),
+                                        (64, 64, 64, False),
                                         (65, 64, 4, True), (512, 8, 8, False), (513, 8, 8, False),
                                         (300, 128, 4, True)])
 def test_route_permute_matches_oracle(G, T, E, k, mwq):
