@@ -337,6 +337,8 @@ def test_delta_small_full(G):
     dict(requests=12, tokens_per_request=5, K=512, N=256, E=4, n_salient=7, seed=9),
     dict(requests=40, tokens_per_request=7, K=384, N=160, E=3, n_salient=40, seed=19),  # 3 K blocks, partial block, 2 salient steps
     dict(requests=20, tokens_per_request=16, K=256, N=128, E=2, n_salient=1, seed=29),
+    dict(requests=10, tokens_per_request=13, K=128, N=128, E=2, n_salient=3, seed=39),  # one K block: prologue past the end
+    dict(requests=9, tokens_per_request=16, K=1152, N=128, E=2, n_salient=5, seed=49),  # three steady passes, then two tail passes
 ])
 def test_delta_dma_kernel(G, over, monkeypatch):
     """The 128-row LDS-DMA delta kernel forced on small layers (it is chosen by
