@@ -143,6 +143,21 @@ def test_layer_decode_full(G):
     _layer_parity(G, gen.config("olmoe_decode"))
 
 
+def test_layer_empty_batch(G):
+    """No tokens: every call takes the empty problem, and the grouping still writes
+    zero counts and offsets."""
+    cfg = gen.config("tiny")
+    d = gen.generate(cfg)
+    gu, dn = G.tiled_layer(d, cfg)
+    x = torch.empty((0, cfg.H), dtype=torch.bfloat16, device="cuda:0")
+    logits = torch.empty((0, cfg.E), dtype=torch.float32, device="cuda:0")
+    buf = G.q.moe_layer_forward(x, logits, cfg.k, gu, dn)
+    torch.cuda.synchronize()
+    assert tuple(buf.out.shape) == (0, cfg.H)
+    assert not buf.perm.counts.cpu().numpy().any()
+    assert not buf.perm.seg_offsets.cpu().numpy().any()
+
+
 @pytest.mark.parametrize("T", [1, 33, 97])
 def test_layer_ragged_small(G, T):
     _layer_parity(G, gen.config("tiny", T=T, seed=7 + T))
