@@ -17,8 +17,8 @@
 //   qgemm_delta_kernel / qgemm_p2d_kernel  2-bit delta + salient channels +
 //                   shared bf16 base (32-row tiles / 128-row LDS-DMA tiles).
 //
-// Dequantisation is exact and costs under one VALU operation per pair of
-// weights: a code c is dropped into the low mantissa bits of the bf16 number
+// Dequantisation is exact and cheap (INT4: seven VALU operations per eight
+// weights): a code c is dropped into the low mantissa bits of the bf16 number
 // 128 (bits 0x4300), giving exactly 128 + c.  The MFMA accumulates
 // sum_k a_k * (128 + c_k) in fp32, a second MFMA chain with the constant
 // -(128 + z) adds sum_k a_k * (-(128 + z)), so the sum of the two is exactly
