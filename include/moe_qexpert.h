@@ -44,8 +44,10 @@
  *   - Arguments are validated on the host before anything is launched; on any
  *     error nothing is launched and the status says why
  *     (moe_last_error_detail() adds a sentence, per calling thread).
- *     A launch failure returns MOE_ERR_HIP.  Faults inside kernels surface at
- *     the caller's next synchronisation.
+ *     A launch failure returns MOE_ERR_HIP.  An error that an earlier HIP call
+ *     of the caller left pending is cleared before the launch (it is not this
+ *     call's error).  Faults inside kernels surface at the caller's next
+ *     synchronisation.
  *   - Identical inputs give bitwise identical outputs (no floating-point
  *     atomics; every reduction has a fixed order).
  *   - No exception or process exit crosses this interface.  The only library
@@ -61,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef int32_t moe_status;
 #define MOE_OK 0
@@ -191,6 +193,19 @@ moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t 
 #define MOE_LAYOUT_CANONICAL 0
 #define MOE_LAYOUT_TILED 1
 
+/* Kernel choice of moe_grouped_qgemm (tuning and tests; AUTO everywhere else).
+   Every choice computes the same result; the LDS-DMA and 128-row kernels add
+   row sums in a different order, so their bits may differ from the others'. */
+#define MOE_KERNEL_AUTO 0            /* chosen from the mean rows per segment */
+#define MOE_KERNEL_SMALL 1           /* 16-row tiles (decode batches); nested MWQ: all widths of an
+                                        expert in one tile; DELTA2: 32-row tiles */
+#define MOE_KERNEL_SMALL_PER_WIDTH 2 /* nested MWQ only: 16-row tiles of one width each */
+#define MOE_KERNEL_TILE64_WIDE 3     /* INT4, MWQ: 64-row tiles, 128 SwiGLU / 256 plain channels */
+#define MOE_KERNEL_TILE64 4          /* INT4, MWQ: 64-row tiles, 64 SwiGLU / 128 plain channels */
+#define MOE_KERNEL_TILE128 5         /* INT4, MWQ: 128-row tiles fed through registers */
+#define MOE_KERNEL_LDS_DMA 6         /* INT4, MWQ, DELTA2 with a base and a plain epilogue: 128-row
+                                        tiles fed by LDS-DMA (activation row sums in the workspace) */
+
 #define MOE_EPI_NONE 0      /* out bf16 [M_total][N] */
 #define MOE_EPI_SWIGLU 1    /* N = 2*I; rows [0,I) gate, [I,2I) up; out = bf16(silu(gate) * up), width I */
 #define MOE_EPI_NONE_F32 2  /* out fp32 [M_total][N], not rounded (expert outputs feeding the combine) */
@@ -259,25 +274,33 @@ moe_status moe_repack_weights(const moe_wdesc* src, const moe_wdesc* dst, void* 
  *
  *   w           tiled descriptor (host pointer; its buffers are device memory)
  *   A           bf16 [A_rows][K], 16-byte aligned, K % 128 == 0
- *   seg_offsets i32 [E*S + 1] from moe_permute (device); rows beyond
- *               seg_offsets[E*S] are not written
+ *   seg_offsets i32 [E*S + 1] from moe_permute (device), or any slice of
+ *               E*S + 1 consecutive entries of a longer ascending table (a
+ *               subset of segments); only rows in [seg_offsets[0],
+ *               seg_offsets[E*S]) are written
  *   M_total     host upper bound of rows (T*k); grid sizing never reads the
  *               device counts back
+ *   kernel      MOE_KERNEL_AUTO, or a MOE_KERNEL_* choice; a choice that does
+ *               not run the format -> MOE_ERR_UNSUPPORTED
  *   out         bf16 or fp32 (see epilogue) [M_total][N or N/2], 16-byte aligned
  *   workspace   moe_grouped_qgemm_workspace_size(...) bytes, device memory,
  *               16-byte aligned; the 128-row prefill kernels keep per-row
  *               sums of A there (INT4: A_rows x K/G fp32; DELTA2 with base:
  *               A_rows fp32), rewritten on every call; size 0 (NULL allowed)
- *               for every other launch.  Calls that share one workspace must
- *               be ordered on one stream.  Too small -> MOE_ERR_WORKSPACE_TOO_SMALL,
+ *               for every other launch.  Decode-sized plain-epilogue calls
+ *               with long K split K and keep fp32 partial sums there
+ *               (n_splits x M_total x N).  Nothing in it needs to start at
+ *               zero.  The size depends on the kernel choice.  Calls that
+ *               share one workspace must be ordered on one stream.  Too small -> MOE_ERR_WORKSPACE_TOO_SMALL,
  *               misaligned -> MOE_ERR_MISALIGNED
  * Supported: N % 32 == 0, K % 128 == 0, G in {32, 64, 128} for INT4 and MWQ.
  */
-size_t moe_grouped_qgemm_workspace_size(const moe_wdesc* w, int32_t A_rows, int32_t M_total);
+size_t moe_grouped_qgemm_workspace_size(const moe_wdesc* w, int32_t A_rows, int32_t M_total, int32_t kernel);
 moe_status moe_grouped_qgemm(const moe_wdesc* w, const uint16_t* A, int32_t A_rows,
                              const int32_t* gather_pair, int32_t k,
                              const int32_t* seg_offsets, int32_t M_total, int32_t epilogue,
-                             void* out, void* workspace, size_t workspace_bytes, void* stream);
+                             int32_t kernel, void* out, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* ----------------------------------------------------------------- combine
  * out[t] = sum_{j<k} w[t][j] * y_perm[pair_pos[t*k + j]], accumulated in fp32
@@ -286,11 +309,15 @@ moe_status moe_grouped_qgemm(const moe_wdesc* w, const uint16_t* A, int32_t A_ro
  *   y_perm   [T*k][H] (grouped order) of y_dtype (MOE_DTYPE_BF16 or
  *            MOE_DTYPE_F32), 16-byte aligned, H % 8 == 0
  *   pair_pos i32 [T*k]
+ *   n_valid  device i32 [1], or NULL: the number of rows the GEMMs wrote
+ *            (seg_offsets[E*S] of the grouping).  A pair whose pair_pos is at
+ *            or past it (an id or bit-width the grouping flagged as invalid)
+ *            adds nothing and its row is not read.  NULL: every row is valid.
  *   topk_w   f32 [T*k], or NULL for weight 1 (k = 1 delta layer)
  *   out      bf16 [T][H], 16-byte aligned
  */
 moe_status moe_unpermute_combine(const void* y_perm, int32_t y_dtype, const int32_t* pair_pos,
-                                 const float* topk_w, int32_t T, int32_t k, int32_t H,
+                                 const int32_t* n_valid, const float* topk_w, int32_t T, int32_t k, int32_t H,
                                  uint16_t* out, void* stream);
 
 #ifdef __cplusplus

@@ -3,7 +3,8 @@
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this module.  The GPU library never calls it, and it shares no code,
 tables or helpers with the GPU library: it unpacks every storage format with
-its own code and works in float64 throughout.
+its own code and works in float64 throughout (one diagnostic variant rounds
+the SwiGLU activation to bf16; see below).
 
 What is computed (the plain definition; the method changes only how expert
 weights are stored and moved, not what the layer computes):
@@ -39,12 +40,13 @@ specification, not by code):
   expert e stores b_e-bit codes, b_e in {2, 3, 4}, with its own zero point:
   w = scale[n][k // G] * (c - z_e).  Each row of an expert is a little-endian
   bit stream (code k in bits k*b .. k*b + b - 1); experts are back to back.
-* SwiGLU expert: h = silu(x Wg^T) * (x Wu^T), y = bf16(h) Wd^T, with gate
-  rows 0..I-1 and up rows I..2I-1 of the gate_up matrix.  The rounding of h
-  to bf16 is the "A16" of W4A16 (ExactMoE) and the 16-bit GEMM of the D2MoE
-  pipeline equation: the activation entering each expert GEMM is a 16-bit
-  value.  Everything else stays float64 (gate/up products, SiLU, the expert
-  output y and the combine).
+* SwiGLU expert: h = silu(x Wg^T) * (x Wu^T), y = h Wd^T, with gate rows
+  0..I-1 and up rows I..2I-1 of the gate_up matrix.  Everything is float64:
+  the gate/up products, SiLU, h, the expert output y and the combine.  As a
+  second, diagnostic result (`out_h16`) the same layer is also evaluated with
+  h rounded once to bf16 before the down product: the 16-bit activation that
+  W4A16 (ExactMoE) and the D2MoE pipeline equation (dequantise, then a 16-bit
+  GEMM) feed into the next expert GEMM.  The parity bar applies to `out`.
 * MWQ segment order inside an expert: b = 4, 3, 2 (sub-key 4 - b).
 """
 from __future__ import annotations
@@ -69,28 +71,28 @@ def f16_to_f64(bits) -> np.ndarray:
 def unpack_u4(packed) -> np.ndarray:
     """[..., K/2] bytes -> [..., K] codes in [0, 15]; even k is the low nibble."""
     p = np.asarray(packed, dtype=np.uint8)
-    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.int64)
-    out[..., 0::2] = p & 0xF
-    out[..., 1::2] = p >> 4
-    return out
+    out = np.empty(p.shape[:-1] + (p.shape[-1], 2), dtype=np.uint8)
+    out[..., 0] = p & 0xF
+    out[..., 1] = p >> 4
+    return out.reshape(p.shape[:-1] + (p.shape[-1] * 2,))
 
 
 def unpack_u2(packed) -> np.ndarray:
     """[..., K/4] bytes -> [..., K] 2-bit fields; field k&3 sits at bits 2*(k&3)."""
-    p = np.asarray(packed, dtype=np.uint8).astype(np.int64)
-    out = np.empty(p.shape[:-1] + (p.shape[-1] * 4,), dtype=np.int64)
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1], 4), dtype=np.uint8)
     for j in range(4):
-        out[..., j::4] = (p >> (2 * j)) & 3
-    return out
+        out[..., j] = (p >> (2 * j)) & 3
+    return out.reshape(p.shape[:-1] + (p.shape[-1] * 4,))
 
 
 def unpack_u1(packed) -> np.ndarray:
     """[..., K/8] bytes -> [..., K] bits; bit k&7 of byte k>>3."""
-    p = np.asarray(packed, dtype=np.uint8).astype(np.int64)
-    out = np.empty(p.shape[:-1] + (p.shape[-1] * 8,), dtype=np.int64)
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1], 8), dtype=np.uint8)
     for j in range(8):
-        out[..., j::8] = (p >> j) & 1
-    return out
+        out[..., j] = (p >> j) & 1
+    return out.reshape(p.shape[:-1] + (p.shape[-1] * 8,))
 
 
 # --------------------------------------------------------------- dequantisation
@@ -104,7 +106,7 @@ def dequant_int4(codes, scales, G: int, zero_point: int = 8) -> np.ndarray:
     K = c.shape[-1]
     s = f16_to_f64(scales)
     assert s.shape[-1] * G == K
-    return np.repeat(s, G, axis=-1) * (c - zero_point).astype(F64)
+    return np.repeat(s, G, axis=-1) * (c.astype(F64) - zero_point)
 
 
 def mwq_code(q2, d3, d4, b: int) -> np.ndarray:
@@ -126,10 +128,15 @@ def mwq_code(q2, d3, d4, b: int) -> np.ndarray:
 
 def dequant_mwq(q2p, d3p, d4p, scales, G: int, b: int, zero_point: int = 8) -> np.ndarray:
     """Nested-plane expert matrix [N][K] at bit-width b, exact in float64."""
-    c = mwq_code(unpack_u2(q2p), unpack_u1(d3p), unpack_u1(d4p), b)
+    return dequant_mwq_planes(unpack_u2(q2p), unpack_u1(d3p), unpack_u1(d4p), scales, G, b, zero_point)
+
+
+def dequant_mwq_planes(q2, d3, d4, scales, G: int, b: int, zero_point: int = 8) -> np.ndarray:
+    """As dequant_mwq, from planes already unpacked to one field per weight."""
+    c = mwq_code(q2, d3, d4, b)
     s = f16_to_f64(scales)
     assert s.shape[-1] * G == c.shape[-1]
-    return np.repeat(s, G, axis=-1) * (c - zero_point).astype(F64)
+    return np.repeat(s, G, axis=-1) * (c.astype(F64) - zero_point)
 
 
 def unpack_bits(stream, n_codes: int, b: int) -> np.ndarray:
@@ -147,7 +154,7 @@ def dequant_per_expert(stream, scales, N: int, K: int, G: int, b: int, zero_poin
     c = unpack_bits(stream, N * K, b).reshape(N, K)
     s = f16_to_f64(scales)
     assert s.shape == (N, K // G)
-    return np.repeat(s, G, axis=-1) * (c - zero_point).astype(F64)
+    return np.repeat(s, G, axis=-1) * (c.astype(F64) - zero_point)
 
 
 def expert_stream_offsets(bits, N: int, K: int) -> np.ndarray:
@@ -160,7 +167,7 @@ def dequant_delta2(codes, step, salient_idx, salient_val) -> np.ndarray:
     """ME-Switch delta [N][K]: salient input channels keep their bf16 value,
     every other channel is step[n] * (c - 2) with a 2-bit code c."""
     c = unpack_u2(codes)
-    d = f16_to_f64(step)[:, None] * (c - 2).astype(F64)
+    d = f16_to_f64(step)[:, None] * (c.astype(F64) - 2.0)
     idx = np.asarray(salient_idx, dtype=np.int64)
     d[:, idx] = bf16_to_f64(salient_val).T
     return d
@@ -229,18 +236,21 @@ def silu(g):
     return g / (1.0 + np.exp(-g))
 
 
-def swiglu_expert(xrows, w_gate_up, w_down):
-    """SwiGLU FFN of one expert on rows of 16-bit activations.
+def swiglu_expert(xrows, w_gate_up, w_down, h_bf16: bool = False):
+    """SwiGLU FFN of one expert on rows of activations, in float64.
 
     w_gate_up [2I][H]: rows 0..I-1 gate, I..2I-1 up; w_down [H][I].
-    The intermediate activation h is a bf16 value (W4A16: 16-bit activations
-    into every expert GEMM); products and sums are float64.
+    h = silu(x Wg^T) * (x Wu^T), y = h Wd^T.  With h_bf16 the activation h
+    is rounded once to bf16 before the down product (the 16-bit activation of
+    W4A16; a diagnostic model, not the definition).
     Returns (h [m][I], y [m][H]).
     """
     I = w_gate_up.shape[0] // 2
     g = xrows @ w_gate_up[:I].T
     u = xrows @ w_gate_up[I:].T
-    h = round_bf16(silu(g) * u)
+    h = silu(g) * u
+    if h_bf16:
+        h = round_bf16(h)
     return h, h @ w_down.T
 
 
@@ -261,9 +271,15 @@ def _expert_weights_int4(data, e, G):
     return wgu, wd
 
 
-def _expert_weights_mwq(data, e, G, b):
-    wgu = dequant_mwq(data["gu_q2"][e], data["gu_d3"][e], data["gu_d4"][e], data["gu_scales"][e], G, b)
-    wd = dequant_mwq(data["dn_q2"][e], data["dn_d3"][e], data["dn_d4"][e], data["dn_scales"][e], G, b)
+def _expert_planes_mwq(data, e):
+    """The nested planes of expert e, unpacked once for all of its bit-widths."""
+    return {m: (unpack_u2(data[m + "q2"][e]), unpack_u1(data[m + "d3"][e]), unpack_u1(data[m + "d4"][e]))
+            for m in ("gu_", "dn_")}
+
+
+def _expert_weights_mwq(data, planes, e, G, b):
+    wgu = dequant_mwq_planes(*planes["gu_"], data["gu_scales"][e], G, b)
+    wd = dequant_mwq_planes(*planes["dn_"], data["dn_scales"][e], G, b)
     return wgu, wd
 
 
@@ -284,6 +300,9 @@ def moe_forward(data: dict, cfg, tokens=None) -> dict:
     token indices; routing and grouping always cover all tokens, the expert
     FFN and the combine only the pairs of the chosen tokens (rows of h_perm /
     y_perm for other pairs stay NaN).
+    Returns the float64 layer (`h_perm`, `y_perm`, `out`) and, as a
+    diagnostic, `out_h16` / `y_perm_h16`: the same layer with the SwiGLU
+    activation rounded once to bf16 before the down product.
     """
     T, E, k, G = cfg.T, cfg.E, cfg.k, cfg.G
     x = bf16_to_f64(data["x"])
@@ -297,33 +316,40 @@ def moe_forward(data: dict, cfg, tokens=None) -> dict:
     I, H = cfg.I, cfg.H
     h_perm = np.full((P, I), np.nan)
     y_perm = np.full((P, H), np.nan)
-    for seg in range(E * S):
-        lo, hi = seg_offsets[seg], seg_offsets[seg + 1]
-        rows = np.arange(lo, hi)
-        rows = rows[want[sorted_pair[lo:hi]]]
-        if rows.size == 0:
-            continue
-        e = seg // S
-        if mwq:
-            wgu, wd = _expert_weights_mwq(data, e, G, 4 - seg % S)
-        elif cfg.fmt == "mixed":
-            wgu, wd = _expert_weights_mixed(data, e, cfg)
-        else:
-            wgu, wd = _expert_weights_int4(data, e, G)
-        toks = sorted_pair[rows] // k
-        h, y = swiglu_expert(x[toks], wgu, wd)
-        h_perm[rows] = h
-        y_perm[rows] = y
+    y_perm16 = np.full((P, H), np.nan)
+    for e in range(E):
+        planes = None
+        for seg in range(e * S, (e + 1) * S):
+            lo, hi = seg_offsets[seg], seg_offsets[seg + 1]
+            rows = np.arange(lo, hi)
+            rows = rows[want[sorted_pair[lo:hi]]]
+            if rows.size == 0:
+                continue
+            if mwq:
+                planes = planes or _expert_planes_mwq(data, e)
+                wgu, wd = _expert_weights_mwq(data, planes, e, G, 4 - seg % S)
+            elif cfg.fmt == "mixed":
+                wgu, wd = _expert_weights_mixed(data, e, cfg)
+            else:
+                wgu, wd = _expert_weights_int4(data, e, G)
+            toks = sorted_pair[rows] // k
+            h, y = swiglu_expert(x[toks], wgu, wd)
+            h_perm[rows] = h
+            y_perm[rows] = y
+            y_perm16[rows] = round_bf16(h) @ wd.T
     sel = np.arange(T) if tokens is None else np.asarray(tokens)
     out = unpermute_combine(np.nan_to_num(y_perm), pair_pos, w, T, k)
+    out16 = unpermute_combine(np.nan_to_num(y_perm16), pair_pos, w, T, k)
     if tokens is not None:
         keep = np.zeros(T, dtype=bool)
         keep[sel] = True
         out[~keep] = np.nan
+        out16[~keep] = np.nan
     return {
         "ids": ids, "w": w, "counts": counts, "seg_offsets": seg_offsets,
         "sorted_pair": sorted_pair, "pair_pos": pair_pos,
         "h_perm": h_perm, "y_perm": y_perm, "out": out, "tokens": sel,
+        "y_perm_h16": y_perm16, "out_h16": out16,
     }
 
 

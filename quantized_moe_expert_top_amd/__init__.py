@@ -16,11 +16,13 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_qexpert.so")
 
-MOE_ABI_VERSION = 2
+MOE_ABI_VERSION = 3
 MOE_W_INT4_GROUP, MOE_W_MWQ_2_3_4, MOE_W_DELTA2_SALIENT, MOE_W_INT_PER_EXPERT = 1, 2, 3, 4
 MOE_LAYOUT_CANONICAL, MOE_LAYOUT_TILED = 0, 1
 MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_NONE_F32 = 0, 1, 2
 MOE_DTYPE_BF16, MOE_DTYPE_F32 = 0, 1
+(MOE_KERNEL_AUTO, MOE_KERNEL_SMALL, MOE_KERNEL_SMALL_PER_WIDTH, MOE_KERNEL_TILE64_WIDE, MOE_KERNEL_TILE64,
+ MOE_KERNEL_TILE128, MOE_KERNEL_LDS_DMA) = range(7)
 (MOE_FIELD_CODES, MOE_FIELD_PLANE3, MOE_FIELD_PLANE4, MOE_FIELD_SCALES,
  MOE_FIELD_SALIENT_IDX, MOE_FIELD_SALIENT_VAL, MOE_FIELD_BASE) = range(7)
 
@@ -66,9 +68,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_route_permute": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moe_weight_field_bytes": (sz, [ctypes.POINTER(WDesc), i32]),
         "moe_repack_weights": (i32, [ctypes.POINTER(WDesc), ctypes.POINTER(WDesc), vp]),
-        "moe_grouped_qgemm_workspace_size": (sz, [ctypes.POINTER(WDesc), i32, i32]),
-        "moe_grouped_qgemm": (i32, [ctypes.POINTER(WDesc), vp, i32, vp, i32, vp, i32, i32, vp, vp, sz, vp]),
-        "moe_unpermute_combine": (i32, [vp, i32, vp, vp, i32, i32, i32, vp, vp]),
+        "moe_grouped_qgemm_workspace_size": (sz, [ctypes.POINTER(WDesc), i32, i32, i32]),
+        "moe_grouped_qgemm": (i32, [ctypes.POINTER(WDesc), vp, i32, vp, i32, vp, i32, i32, i32, vp, vp, sz, vp]),
+        "moe_unpermute_combine": (i32, [vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -243,36 +245,50 @@ def moe_repack_weights(src: QuantizedExperts, stream=None) -> QuantizedExperts:
     return dst
 
 
+def moe_grouped_qgemm_workspace_size(w: QuantizedExperts, A_rows: int, M_total: int,
+                                     kernel: int = MOE_KERNEL_AUTO) -> int:
+    return lib().moe_grouped_qgemm_workspace_size(ctypes.byref(w.desc), A_rows, M_total, kernel)
+
+
 def moe_grouped_qgemm(w: QuantizedExperts, A: torch.Tensor, seg_offsets: torch.Tensor, M_total: int,
                       epilogue: int = MOE_EPI_NONE, gather_pair: torch.Tensor = None, k: int = 1,
-                      out: torch.Tensor = None, workspace: torch.Tensor = None, stream=None) -> torch.Tensor:
+                      out: torch.Tensor = None, workspace: torch.Tensor = None, stream=None,
+                      kernel: int = MOE_KERNEL_AUTO) -> torch.Tensor:
     _bf16(A)
     A_rows = A.shape[0]
     n_out = w.N // 2 if epilogue == MOE_EPI_SWIGLU else w.N
     if out is None:
         dt = torch.float32 if epilogue == MOE_EPI_NONE_F32 else torch.bfloat16
         out = torch.empty((M_total, n_out), dtype=dt, device=A.device)
-    ws_need = lib().moe_grouped_qgemm_workspace_size(ctypes.byref(w.desc), A_rows, M_total)
+    ws_need = moe_grouped_qgemm_workspace_size(w, A_rows, M_total, kernel)
     if workspace is None and ws_need:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=A.device)
     ws_bytes = workspace.numel() if workspace is not None else 0
     _check(lib().moe_grouped_qgemm(ctypes.byref(w.desc), _ptr(A), A_rows, _ptr(gather_pair), k, _ptr(seg_offsets),
-                                   M_total, epilogue, _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
+                                   M_total, epilogue, kernel, _ptr(out), _ptr(workspace), ws_bytes,
+                                   _stream(stream)),
            "moe_grouped_qgemm")
     return out
 
 
 def moe_unpermute_combine(y_perm: torch.Tensor, pair_pos: torch.Tensor, topk_w: Optional[torch.Tensor],
-                          T: int, k: int, out: torch.Tensor = None, stream=None) -> torch.Tensor:
-    """y_perm: fp32 or 16-bit (bf16 bit pattern) rows in grouped order."""
+                          T: int, k: int, out: torch.Tensor = None, stream=None,
+                          n_valid: torch.Tensor = None) -> torch.Tensor:
+    """y_perm: fp32 or 16-bit (bf16 bit pattern) rows in grouped order.  n_valid: optional
+    one-element int32 device tensor (e.g. seg_offsets[-1:]); pairs at or past it add nothing."""
     y_dtype = MOE_DTYPE_F32 if y_perm.dtype == torch.float32 else MOE_DTYPE_BF16
     if y_dtype == MOE_DTYPE_BF16:
         _bf16(y_perm)
     H = y_perm.shape[1]
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y_perm.device)
-    _check(lib().moe_unpermute_combine(_ptr(y_perm), y_dtype, _ptr(pair_pos), _ptr(topk_w), T, k, H, _ptr(out),
-                                       _stream(stream)), "moe_unpermute_combine")
+    nv = None
+    if n_valid is not None:
+        if n_valid.dtype != torch.int32 or n_valid.numel() < 1 or not n_valid.is_cuda:
+            raise ValueError("n_valid must be an int32 device tensor")
+        nv = n_valid.data_ptr()  # a one-element view of a longer table is fine
+    _check(lib().moe_unpermute_combine(_ptr(y_perm), y_dtype, _ptr(pair_pos), nv, _ptr(topk_w), T, k, H,
+                                       _ptr(out), _stream(stream)), "moe_unpermute_combine")
     return out
 
 
@@ -337,8 +353,9 @@ def alloc_layer(T: int, E: int, k: int, H: int, I: int, mwq: bool, device) -> La
 
 def moe_layer_forward(x: torch.Tensor, logits: torch.Tensor, k: int, gate_up: QuantizedExperts,
                       down: QuantizedExperts, pair_bits: torch.Tensor = None,
-                      buf: LayerBuffers = None, stream=None) -> LayerBuffers:
-    """Route -> group -> gate_up (+SwiGLU, bf16 h) -> down (fp32 expert outputs) -> combine, one stream."""
+                      buf: LayerBuffers = None, stream=None, kernel: int = MOE_KERNEL_AUTO) -> LayerBuffers:
+    """Route -> group -> gate_up (+SwiGLU, bf16 h) -> down (fp32 expert outputs) -> combine, one stream.
+    kernel: the grouped GEMMs' kernel choice (MOE_KERNEL_*; AUTO chooses from the shapes)."""
     T, H = x.shape
     E = logits.shape[1]
     I = gate_up.N // 2
@@ -346,7 +363,9 @@ def moe_layer_forward(x: torch.Tensor, logits: torch.Tensor, k: int, gate_up: Qu
         buf = alloc_layer(T, E, k, H, I, pair_bits is not None, x.device)
     moe_route_permute(logits, k, pair_bits=pair_bits, ids=buf.ids, w=buf.w, out=buf.perm, stream=stream)
     moe_grouped_qgemm(gate_up, x, buf.perm.seg_offsets, T * k, MOE_EPI_SWIGLU, gather_pair=buf.perm.sorted_pair,
-                      k=k, out=buf.h, stream=stream)
-    moe_grouped_qgemm(down, buf.h, buf.perm.seg_offsets, T * k, MOE_EPI_NONE_F32, out=buf.y_perm, stream=stream)
-    moe_unpermute_combine(buf.y_perm, buf.perm.pair_pos, buf.w, T, k, out=buf.out, stream=stream)
+                      k=k, out=buf.h, stream=stream, kernel=kernel)
+    moe_grouped_qgemm(down, buf.h, buf.perm.seg_offsets, T * k, MOE_EPI_NONE_F32, out=buf.y_perm, stream=stream,
+                      kernel=kernel)
+    moe_unpermute_combine(buf.y_perm, buf.perm.pair_pos, buf.w, T, k, out=buf.out, stream=stream,
+                          n_valid=buf.perm.seg_offsets[-1:])
     return buf

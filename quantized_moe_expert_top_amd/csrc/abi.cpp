@@ -1,12 +1,17 @@
 // C ABI entry points: host-side validation, then stream-ordered launches.
 // Every check happens before anything is launched; a failing call launches
 // nothing and leaves a one-sentence reason in a thread-local buffer.
+//
+// Plain C++ (no HIP headers): the device side is reached only through the
+// launchers and runtime queries of launch.h.  Before a launch, any error an
+// earlier HIP call of the caller left pending is taken and dropped, so that
+// MOE_ERR_HIP reports what this call's own launches returned.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
 #include "moe_qexpert.h"
-#include "common.h"
+#include "launch.h"
 
 namespace {
 thread_local char g_detail[512] = "";
@@ -22,10 +27,12 @@ moe_status ok() {
   g_detail[0] = '\0';
   return MOE_OK;
 }
-moe_status hip_status(hipError_t e, const char* what) {
-  if (e == hipSuccess) return ok();
-  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+moe_status hip_status(int e, const char* what) {
+  if (e == 0) return ok();
+  return fail(MOE_ERR_HIP, "%s: %s", what, moe::rt_error_string(e));
 }
+// Drops an error left pending by an earlier HIP call of the caller.
+void clear_pending() { (void)moe::rt_take_error(); }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Validates a weight descriptor; `tiled` selects which layout is expected.
@@ -105,19 +112,22 @@ moe::QWeights to_q(const moe_wdesc* w) {
   return q;
 }
 
-// gfx950 check, once per device, on the first launching call.
+// gfx950 check, once per device and thread, on the first launching call;
+// then any error left pending by the caller's earlier HIP calls is dropped.
 moe_status check_device() {
   int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  int e = moe::rt_current_device(&dev);
+  if (e != 0) return fail(MOE_ERR_HIP, "current device: %s", moe::rt_error_string(e));
   static thread_local int checked_dev = -1;
-  if (checked_dev == dev) return MOE_OK;
-  hipDeviceProp_t prop;
-  e = hipGetDeviceProperties(&prop, dev);
-  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
-  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
-    return fail(MOE_ERR_UNSUPPORTED, "device arch %s; this library is built for gfx950", prop.gcnArchName);
-  checked_dev = dev;
+  if (checked_dev != dev) {
+    char arch[64] = "";
+    e = moe::rt_device_arch(dev, arch, sizeof(arch));
+    if (e != 0) return fail(MOE_ERR_HIP, "device properties: %s", moe::rt_error_string(e));
+    if (strncmp(arch, "gfx950", 6) != 0)
+      return fail(MOE_ERR_UNSUPPORTED, "device arch %s; this library is built for gfx950", arch);
+    checked_dev = dev;
+  }
+  clear_pending();
   return MOE_OK;
 }
 }  // namespace
@@ -154,7 +164,7 @@ moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, 
     return fail(MOE_ERR_MISALIGNED, "route buffers must be 4-byte aligned");
   moe_status st = check_device();
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_route_topk(logits, T, E, k, topk_ids, topk_w, (hipStream_t)stream),
+  return hip_status(moe::launch_route_topk(logits, T, E, k, topk_ids, topk_w, stream),
                     "route_topk launch");
 }
 
@@ -188,7 +198,7 @@ moe_status moe_permute(const int32_t* topk_ids, const uint8_t* pair_bits, int32_
   if (st != MOE_OK) return st;
   moe::PermuteArgs a{topk_ids, pair_bits, T * k, k, E, S, expert_counts, seg_offsets, sorted_pair, pair_pos,
                      x, H, x_perm, workspace};
-  return hip_status(moe::launch_permute(a, (hipStream_t)stream), "permute launch");
+  return hip_status(moe::launch_permute(a, stream), "permute launch");
 }
 
 moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k, const uint8_t* pair_bits,
@@ -211,7 +221,7 @@ moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t 
     return fail(MOE_ERR_MISALIGNED, "route buffers must be 4-byte aligned");
   moe_status st = check_device();
   if (st != MOE_OK) return st;
-  const hipStream_t s = (hipStream_t)stream;
+  void* const s = stream;
   if (T > 0 && moe::route_permute_fusable(T, k, E))
     return hip_status(moe::launch_route_permute(logits, T, E, k, pair_bits, topk_ids, topk_w, expert_counts,
                                                 seg_offsets, sorted_pair, pair_pos, workspace, s),
@@ -272,22 +282,29 @@ moe_status moe_repack_weights(const moe_wdesc* src, const moe_wdesc* dst, void* 
   if (src->codes == dst->codes) return fail(MOE_ERR_BAD_SHAPE, "repack cannot run in place");
   st = check_device();
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_repack(to_q(src), to_q(dst), (hipStream_t)stream), "repack launch");
+  return hip_status(moe::launch_repack(to_q(src), to_q(dst), stream), "repack launch");
 }
 
-size_t moe_grouped_qgemm_workspace_size(const moe_wdesc* w, int32_t A_rows, int32_t M_total) {
+size_t moe_grouped_qgemm_workspace_size(const moe_wdesc* w, int32_t A_rows, int32_t M_total, int32_t kernel) {
   if (check_desc(w, MOE_LAYOUT_TILED, false) != MOE_OK) return 0;
-  return moe::qgemm_workspace_bytes(to_q(w), A_rows, M_total);
+  if (A_rows < 0 || M_total < 0 || !moe::qgemm_kernel_supported(w->format, kernel)) return 0;
+  return moe::qgemm_workspace_bytes(to_q(w), A_rows, M_total, kernel);
 }
 
 moe_status moe_grouped_qgemm(const moe_wdesc* w, const uint16_t* A, int32_t A_rows, const int32_t* gather_pair,
                              int32_t k, const int32_t* seg_offsets, int32_t M_total, int32_t epilogue,
-                             void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                             int32_t kernel, void* out, void* workspace, size_t workspace_bytes, void* stream) {
   moe_status st = check_desc(w, MOE_LAYOUT_TILED, true);
   if (st != MOE_OK) return st;
   if (M_total < 0 || A_rows < 0) return fail(MOE_ERR_BAD_SHAPE, "M_total=%d A_rows=%d", M_total, A_rows);
   if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SWIGLU && epilogue != MOE_EPI_NONE_F32)
     return fail(MOE_ERR_BAD_FORMAT, "unknown epilogue %d", epilogue);
+  if (kernel < MOE_KERNEL_AUTO || kernel > MOE_KERNEL_LDS_DMA)
+    return fail(MOE_ERR_BAD_FORMAT, "unknown kernel choice %d", kernel);
+  if (!moe::qgemm_kernel_supported(w->format, kernel))
+    return fail(MOE_ERR_UNSUPPORTED, "kernel choice %d does not run weight format %d", kernel, w->format);
+  if (w->format == MOE_W_DELTA2_SALIENT && kernel == MOE_KERNEL_LDS_DMA && (!w->base || epilogue == MOE_EPI_SWIGLU))
+    return fail(MOE_ERR_UNSUPPORTED, "the LDS-DMA delta kernel needs a shared base and a plain epilogue");
   if (gather_pair) {
     if (k < 1) return fail(MOE_ERR_BAD_SHAPE, "k=%d with gather_pair", k);
     if ((int64_t)A_rows * k < M_total) return fail(MOE_ERR_BAD_SHAPE, "A_rows*k < M_total");
@@ -298,22 +315,23 @@ moe_status moe_grouped_qgemm(const moe_wdesc* w, const uint16_t* A, int32_t A_ro
   if (!A || !seg_offsets || !out) return fail(MOE_ERR_NULL_ARG, "A, seg_offsets and out are required");
   if (!aligned(A, 16) || !aligned(out, 16)) return fail(MOE_ERR_MISALIGNED, "A and out must be 16-byte aligned");
   const moe::QWeights q = to_q(w);
-  const size_t need = moe::qgemm_workspace_bytes(q, A_rows, M_total);
+  const size_t need = moe::qgemm_workspace_bytes(q, A_rows, M_total, kernel);
   if (workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, %zu needed", workspace_bytes, need);
   if (need && !workspace) return fail(MOE_ERR_NULL_ARG, "workspace is NULL");
   if (need && !aligned(workspace, 16)) return fail(MOE_ERR_MISALIGNED, "workspace must be 16-byte aligned");
-  st = check_device();
-  if (st != MOE_OK) return st;
   if ((int64_t)A_rows * w->K * 2 >= ((int64_t)1 << 32))
     return fail(MOE_ERR_UNSUPPORTED, "activation matrix of %lld bytes (4 GiB or more)", (long long)A_rows * w->K * 2);
+  st = check_device();
+  if (st != MOE_OK) return st;
   moe::QGemmArgs a{q, A, A_rows, gather_pair, k, seg_offsets, w->E * (w->format == MOE_W_MWQ_2_3_4 ? 3 : 1), M_total,
-                   epilogue, out, workspace};
-  return hip_status(moe::launch_qgemm(a, (hipStream_t)stream), "grouped_qgemm launch");
+                   epilogue, kernel, out, workspace};
+  return hip_status(moe::launch_qgemm(a, stream), "grouped_qgemm launch");
 }
 
-moe_status moe_unpermute_combine(const void* y_perm, int32_t y_dtype, const int32_t* pair_pos, const float* topk_w,
-                                 int32_t T, int32_t k, int32_t H, uint16_t* out, void* stream) {
+moe_status moe_unpermute_combine(const void* y_perm, int32_t y_dtype, const int32_t* pair_pos,
+                                 const int32_t* n_valid, const float* topk_w, int32_t T, int32_t k, int32_t H,
+                                 uint16_t* out, void* stream) {
   if (y_dtype != MOE_DTYPE_BF16 && y_dtype != MOE_DTYPE_F32) return fail(MOE_ERR_BAD_FORMAT, "y_dtype %d", y_dtype);
   if (T < 0 || k < 1 || H < 8 || H % 8 != 0)
     return fail(MOE_ERR_BAD_SHAPE, "T=%d k=%d H=%d (H must be a positive multiple of 8)", T, k, H);
@@ -321,10 +339,11 @@ moe_status moe_unpermute_combine(const void* y_perm, int32_t y_dtype, const int3
   if (T == 0) return ok();
   if (!y_perm || !pair_pos || !out) return fail(MOE_ERR_NULL_ARG, "y_perm, pair_pos and out are required");
   if (!aligned(y_perm, 16) || !aligned(out, 16)) return fail(MOE_ERR_MISALIGNED, "y_perm and out must be 16-byte aligned");
+  if (n_valid && !aligned(n_valid, 4)) return fail(MOE_ERR_MISALIGNED, "n_valid must be 4-byte aligned");
   moe_status st = check_device();
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_combine(y_perm, y_dtype == MOE_DTYPE_F32, pair_pos, topk_w, T, k, H, out,
-                                        (hipStream_t)stream),
+  return hip_status(moe::launch_combine(y_perm, y_dtype == MOE_DTYPE_F32, pair_pos, n_valid, topk_w, T, k, H, out,
+                                        stream),
                     "combine launch");
 }
 

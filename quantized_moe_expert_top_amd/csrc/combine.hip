@@ -2,7 +2,9 @@
 //   out[t] = sum_{j<k} w[t][j] * y_perm[pair_pos[t*k+j]]
 // accumulated in fp32 in slot order and rounded once to bf16.  No atomics, so
 // the result is bitwise reproducible.  One workgroup per token; each lane
-// moves 8 bf16 (16 bytes) per row and slot.
+// moves 8 bf16 (16 bytes) per row and slot.  With `n_valid`, a pair whose
+// grouped row lies at or past *n_valid (a pair the grouping flagged as
+// invalid, whose row no GEMM wrote) adds nothing and its row is not read.
 #include "common.h"
 
 namespace moe {
@@ -16,11 +18,13 @@ constexpr int kThreads = 256;
 template <bool Y_F32>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restrict__ yv,
                                                            const int32_t* __restrict__ pos,
+                                                           const int32_t* __restrict__ n_valid,
                                                            const float* __restrict__ w, int k, int H,
                                                            uint16_t* __restrict__ out) {
   constexpr int B = 8;
   const int t = blockIdx.x;
   const int nvec = H >> 3;
+  const int nv = n_valid ? *n_valid : 0x7FFFFFFF;
   for (int c = threadIdx.x; c < nvec; c += kThreads) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < k; j0 += B) {
@@ -29,8 +33,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
 #pragma unroll
       for (int i = 0; i < B; ++i) {
         const int j = j0 + i;
-        if (j < k) {
-          const int p = pos[(size_t)t * k + j];
+        g[i] = 0.f;
+        v[i][0] = v[i][1] = f32x4{};
+        const int p = j < k ? pos[(size_t)t * k + j] : nv;
+        if (p < nv) {
           g[i] = w ? w[(size_t)t * k + j] : 1.0f;
           if (Y_F32) {
             const f32x4* row = reinterpret_cast<const f32x4*>(static_cast<const float*>(yv) + (size_t)p * H);
@@ -63,12 +69,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
 }
 }  // namespace
 
-hipError_t launch_combine(const void* y, bool y_f32, const int32_t* pos, const float* w, int T, int k, int H,
-                          uint16_t* out, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  if (y_f32) hipLaunchKernelGGL(combine_kernel<true>, dim3(T), dim3(kThreads), 0, s, y, pos, w, k, H, out);
-  else hipLaunchKernelGGL(combine_kernel<false>, dim3(T), dim3(kThreads), 0, s, y, pos, w, k, H, out);
-  return hipGetLastError();
+int launch_combine(const void* y, bool y_f32, const int32_t* pos, const int32_t* n_valid, const float* w, int T,
+                   int k, int H, uint16_t* out, void* stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) return 0;
+  if (y_f32) hipLaunchKernelGGL(combine_kernel<true>, dim3(T), dim3(kThreads), 0, s, y, pos, n_valid, w, k, H, out);
+  else hipLaunchKernelGGL(combine_kernel<false>, dim3(T), dim3(kThreads), 0, s, y, pos, n_valid, w, k, H, out);
+  return (int)hipGetLastError();
 }
 
 }  // namespace moe

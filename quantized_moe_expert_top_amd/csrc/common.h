@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
+
 namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -107,76 +109,13 @@ __device__ __forceinline__ void route_token_rank(float v, int E, int k, int32_t*
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Kernel-side launch helpers return hipGetLastError() after the launch.
-hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
-                             hipStream_t s);
-
-struct PermuteArgs {
-  const int32_t* ids;
-  const uint8_t* bits;
-  int P, k, E, S;
-  int32_t* counts;
-  int32_t* seg_offsets;
-  int32_t* sorted_pair;
-  int32_t* pair_pos;
-  const uint16_t* x;
-  int H;
-  uint16_t* x_perm;
-  void* ws;
-};
-size_t permute_workspace_bytes(int P, int E, int S);
-hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
-// Routing + grouping in one launch (E <= 64 experts, T*k <= 4096 pairs).
-bool route_permute_fusable(int T, int k, int E);
-hipError_t launch_route_permute(const float* logits, int T, int E, int k, const uint8_t* bits, int32_t* ids,
-                                float* w, int32_t* counts, int32_t* seg_offsets, int32_t* sorted_pair,
-                                int32_t* pair_pos, void* ws, hipStream_t s);
-
-
-hipError_t launch_combine(const void* y, bool y_f32, const int32_t* pos, const float* w, int T, int k, int H,
-                          uint16_t* out, hipStream_t s);
-
 // Static per-expert widths (format 4): the kernels get each expert's width,
 // zero point and first tile block (in units of 256 bytes; a tile block of a
 // b-bit expert is 256 * b bytes) by value, in the launch arguments.
-constexpr int kMaxMixedExperts = 256;
 struct XTab {
   uint8_t bits[kMaxMixedExperts];
   uint8_t zero[kMaxMixedExperts];
   uint32_t off[kMaxMixedExperts];
 };
-
-// Weight descriptor as the kernels see it (tiled layout only).
-struct QWeights {
-  int fmt;  // 1 INT4, 2 MWQ, 3 DELTA2, 4 per-expert widths
-  int E, N, K, G, z, n_sal;
-  const int32_t* xbits;  // per-expert widths / zero points (host arrays, format 4)
-  const int32_t* xzero;
-  const uint8_t* codes;
-  const uint8_t* p3;
-  const uint8_t* p4;
-  const uint16_t* scales;
-  const int32_t* sal_idx;
-  const uint16_t* sal_val;
-  const uint16_t* base;
-};
-struct QGemmArgs {
-  QWeights w;
-  const uint16_t* A;
-  int A_rows;
-  const int32_t* gather;
-  int k;
-  const int32_t* seg_offsets;
-  int nseg;
-  int M_total;
-  int epilogue;  // 0 bf16, 1 SwiGLU bf16, 2 fp32
-  void* out;
-  void* ws;
-};
-size_t qgemm_workspace_bytes(const QWeights& w, int A_rows, int M_total);
-hipError_t launch_qgemm(const QGemmArgs& a, hipStream_t s);
-
-hipError_t launch_repack(const QWeights& src, const QWeights& dst, hipStream_t s);
-size_t tiled_salient_bytes(int E, int N, int n_sal);
 
 }  // namespace moe

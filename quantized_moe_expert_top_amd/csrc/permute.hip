@@ -17,8 +17,8 @@ namespace moe {
 
 namespace {
 constexpr int kThreads = 256;
-constexpr int kChunk = 2048;          // pairs per workgroup in the multi-block path
-constexpr int kSmallMax = 4096;       // up to this many pairs: single workgroup
+constexpr int kChunk = kPermuteChunk;        // pairs per workgroup in the multi-block path
+constexpr int kSmallMax = kPermuteSmallMax;  // up to this many pairs: single workgroup
 constexpr int kMaxKeys = 3 * 1024 + 1;
 
 struct Keyer {
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void permute_small_kernel(Keyer kr, int P
 // its ids visible device-wide and counts itself in; the last workgroup to
 // arrive groups all pairs and resets the counter.  Outputs are identical to
 // moe_route_topk followed by moe_permute.
-constexpr int kRPMaxE = 64, kRPMaxKeys = 3 * kRPMaxE + 1;
+constexpr int kRPMaxE = kRoutePermuteMaxE, kRPMaxKeys = 3 * kRPMaxE + 1;
 __global__ __launch_bounds__(kThreads) void route_permute_kernel(const float* __restrict__ logits, int T, int E,
                                                                  int k, const uint8_t* bits, int32_t* ids, float* w,
                                                                  int32_t* counts, int32_t* seg_offsets,
@@ -296,23 +296,19 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(const uint16_t* _
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 }  // namespace
 
-bool route_permute_fusable(int T, int k, int E) { return E <= kRPMaxE && (int64_t)T * k <= kSmallMax; }
 
-hipError_t launch_route_permute(const float* logits, int T, int E, int k, const uint8_t* bits, int32_t* ids,
-                                float* w, int32_t* counts, int32_t* seg_offsets, int32_t* sorted_pair,
-                                int32_t* pair_pos, void* ws, hipStream_t s) {
+int launch_route_permute(const float* logits, int T, int E, int k, const uint8_t* bits, int32_t* ids, float* w,
+                         int32_t* counts, int32_t* seg_offsets, int32_t* sorted_pair, int32_t* pair_pos, void* ws,
+                         void* stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(route_permute_kernel, dim3((unsigned)((T + 3) / 4)), dim3(kThreads), 0, s, logits, T, E, k, bits,
                      ids, w, counts, seg_offsets, sorted_pair, pair_pos, static_cast<uint32_t*>(ws));
-  return hipGetLastError();
+  return (int)hipGetLastError();
 }
 
-size_t permute_workspace_bytes(int P, int E, int S) {
-  const size_t nk1 = (size_t)E * S + 1;
-  const size_t nb = P <= kSmallMax ? 0 : (size_t)(P + kChunk - 1) / kChunk;
-  return 256 + align256(nb * 4) + align256(nb * nk1 * 4);
-}
 
-hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
+int launch_permute(const PermuteArgs& a, void* stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   Keyer kr{a.ids, a.bits, a.E, a.S, a.E * a.S};
   uint8_t* ws = static_cast<uint8_t*>(a.ws);
   uint32_t* flag = reinterpret_cast<uint32_t*>(ws);
@@ -330,13 +326,13 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
                        a.sorted_pair, a.pair_pos);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess) return (int)e;
   if (a.x_perm && a.P > 0) {
     hipLaunchKernelGGL(gather_rows_kernel, dim3(a.P), dim3(kThreads), 0, s, a.x, a.H, a.k, a.sorted_pair, a.P,
                        a.x_perm);
     e = hipGetLastError();
   }
-  return e;
+  return (int)e;
 }
 
 }  // namespace moe

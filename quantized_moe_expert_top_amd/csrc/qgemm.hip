@@ -33,9 +33,7 @@
 //                                repack); salient channels are one more MFMA
 //                                K chunk with bf16 values; the shared base is a
 //                                plain bf16 MFMA on the same A operand
-#include <stdlib.h>
 #include <type_traits>
-#include <string.h>
 
 #include "common.h"
 
@@ -1538,15 +1536,16 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2d_kernel(KArgs p, const fl
 }
 
 // out[row] = sum over ks = 0..n_ks-1 of part[ks][row], in that order, for the
-// rows the segments hold (seg_offsets[nseg]); fp32 or bf16 out.  One thread
-// per 4 outputs.
+// rows the segments hold, [seg_offsets[0], seg_offsets[nseg]) (a caller may
+// pass a slice of a longer offset table whose first entry is not zero); fp32
+// or bf16 out.  One thread per 4 outputs; the grid covers M_total rows.
 template <int EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int n_ks, int M_total,
                                                             int N, const int32_t* __restrict__ seg_offsets, int nseg,
                                                             void* __restrict__ out) {
-  const size_t i4 = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t rows = (size_t)seg_offsets[nseg];
-  if (i4 * 4 >= rows * N) return;
+  const size_t first = (size_t)seg_offsets[0] * N / 4, last = (size_t)seg_offsets[nseg] * N / 4;
+  const size_t i4 = first + (size_t)blockIdx.x * 256 + threadIdx.x;  // N % 32 == 0: rows hold whole vectors
+  if (i4 >= last) return;
   const size_t plane = (size_t)M_total * N;
   f32x4 v = reinterpret_cast<const f32x4*>(part)[i4];
   for (int ks = 1; ks < n_ks; ++ks) v += reinterpret_cast<const f32x4*>(part + ks * plane)[i4];
@@ -1561,23 +1560,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
-// K splits of the decode kernel: one unless the (channel group, row tile)
-// items leave the chip short of workgroups (fewer than 3 per CU), then enough
-// to bring them to about 4 per CU, each split keeping at least 8 K blocks.
-int decode_splits(int n_items, int K) {
-  const int KBt = K / 128;
-  if (n_items >= 768 || KBt < 16) return 1;
-  int n = (1024 + n_items - 1) / n_items;
-  n = min(n, KBt / 8);
-  const int kb_per = (KBt + n - 1) / n;
-  return (KBt + kb_per - 1) / kb_per;  // every split non-empty
-}
 
-// Upper bound of the decode kernel's row tiles: one partial tile per tile
-// segment (an expert, or for MWQ on path 1 each width of an expert).
-int decode_row_tiles(int fmt, int path, int M_total, int E) {
-  return (M_total + 15) / 16 + ((fmt == 2 && path == 1) ? 3 * E : E);
-}
 
 template <int FMT, int EPI>
 void launch_d(const KArgs& ka, int n_cg, int n_rt, const XTab& tab, hipStream_t s) {
@@ -1687,14 +1670,8 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, int A_rows, voi
     return;
   }
   if (fmt != 3 && path != 0 && path != 1) {
-    // 64 rows per workgroup; 8 wavefront columns (wide channel blocks: the
-    // activations are read fewer times) when the activations outweigh the
-    // weights, else 4.  path 65 forces 4 columns, 128 two rows of 4.
-    if (path == 64) {
-      const double a_bytes = (double)M_total * ka.K * 2.0;
-      const double w_bytes = (double)(ka.nseg / ka.S) * ka.N * ka.K * (fmt == 1 ? 0.5 : 0.25);
-      if (a_bytes < w_bytes && !getenv("MOE_QGEMM_PATH")) path = 65;
-    }
+    // 64 rows per workgroup with 8 (path 64) or 4 (65) wavefront columns, or
+    // 128 rows as two rows of 4 (128)
     if (fmt == 1) {
       if (path == 64) launch_p<1, EPI, 1, 8>(ka, M_total, s);
       else if (path == 65) launch_p<1, EPI, 1, 4>(ka, M_total, s);
@@ -1725,55 +1702,12 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, int A_rows, voi
   else launch_d<4, EPI>(kd, gx, n_rt, tab, s);                 // all widths per tile
 }
 
-// Kernel from the mean rows per segment (the host never sees the device
-// counts): few rows per segment -> 16-row tiles (decode kernel); many -> the
-// 128-row LDS-DMA kernel for INT4, 64-row tiles otherwise (and for INT4
-// segments of under ~96 rows, where 128-row tiles would be mostly padding).
-// Nested MWQ -> the 128-row kernel over 16-row chunks of every width from
-// about 256 rows per expert for SwiGLU and 512 for the plain epilogues
-// (measured on the Mixtral-shaped layer: with fewer rows, 64-row tiles of one
-// width are as fast or faster, the 128-row kernel leaving many chunks of its
-// last workgroup per expert empty); few rows -> the 16-row tiles, which take
-// all widths of an expert together (one read of each bit plane) unless
-// MOE_QGEMM_PATH=split gives each width its own tiles.
-// MOE_QGEMM_PATH=small|split|64|64n|128|dma forces a path.  The workspace
-// query covers both epilogues (the larger need).
-int pick_path(int M_total, int nseg, int fmt, int epi) {
-  if (fmt == 4) return 0;  // a width per expert: 16-row tiles at every batch size
-  if (const char* f = getenv("MOE_QGEMM_PATH")) {
-    if (fmt == 3) return !strcmp(f, "dma") ? 3 : 0;
-    if (!strcmp(f, "small")) return 0;
-    if (!strcmp(f, "split")) return fmt == 2 ? 1 : 0;
-    if (!strcmp(f, "64")) return 64;
-    if (!strcmp(f, "64n")) return 65;
-    if (!strcmp(f, "128")) return 128;
-    if (!strcmp(f, "dma")) return 2;
-  }
-  const double avg = (double)M_total / (double)(nseg > 0 ? nseg : 1);
-  if (fmt == 3) return avg >= 96.0 ? 3 : 0;  // delta: 128-row LDS-DMA kernel, else 32-row tiles
-  // nested MWQ: the 128-row kernel takes all widths of an expert (16-row chunks per width)
-  if (fmt == 2 && 3.0 * avg >= (epi == 1 ? 256.0 : 512.0)) return 2;
-  if (avg < 24.0) return 0;
-  return (fmt == 1 && avg >= 96.0) ? 2 : 64;
-}
 }  // namespace
 
-size_t qgemm_workspace_bytes(const QWeights& w, int A_rows, int M_total) {
-  const int nseg = w.E * (w.fmt == 2 ? 3 : 1);
-  // the 128-row MWQ kernel runs from fewer rows with SwiGLU than with plain epilogues
-  const int path = (w.fmt == 2 && pick_path(M_total, nseg, w.fmt, 1) == 2) ? 2 : pick_path(M_total, nseg, w.fmt, 0);
-  if (path == 2) return ((size_t)A_rows * (w.K / w.G) * 4 + 255) & ~(size_t)255;  // row sums per group
-  if (path == 3) return ((size_t)A_rows * 4 + 255) & ~(size_t)255;                 // row sums over all of K
-  if (w.fmt != 3 && (path == 0 || path == 1)) {
-    // split-K partial sums of the plain epilogues (the SwiGLU one never splits)
-    const int n_ks = decode_splits(((w.N + 127) / 128) * decode_row_tiles(w.fmt, path, M_total, w.E), w.K);
-    if (n_ks > 1) return ((size_t)n_ks * M_total * w.N * 4 + 255) & ~(size_t)255;
-  }
-  return 0;
-}
 
-hipError_t launch_qgemm(const QGemmArgs& a, hipStream_t s) {
-  if (a.M_total == 0) return hipSuccess;
+int launch_qgemm(const QGemmArgs& a, void* stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.M_total == 0) return 0;
   const QWeights& w = a.w;
   KArgs ka;
   ka.codes = w.codes;
@@ -1801,7 +1735,7 @@ hipError_t launch_qgemm(const QGemmArgs& a, hipStream_t s) {
   const bool swiglu = a.epilogue == 1;
   ka.n_out = swiglu ? w.N / 2 : w.N;
   (void)swiglu;
-  const int path = pick_path(a.M_total, a.nseg, w.fmt, a.epilogue);
+  const int path = pick_path(w, a.M_total, a.nseg, a.epilogue, a.kernel);
   // per-expert widths: width, zero point and first 256-byte unit of each expert's tile blocks
   static const XTab kNoTab{};
   XTab tab{};
@@ -1818,7 +1752,7 @@ hipError_t launch_qgemm(const QGemmArgs& a, hipStream_t s) {
   if (a.epilogue == 1) launch_epi<1>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, t, s);
   else if (a.epilogue == 2) launch_epi<2>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, t, s);
   else launch_epi<0>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, t, s);
-  return hipGetLastError();
+  return (int)hipGetLastError();
 }
 
 }  // namespace moe

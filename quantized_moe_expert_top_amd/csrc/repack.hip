@@ -208,14 +208,11 @@ __global__ __launch_bounds__(kThreads) void repack_mixed_kernel(const uint8_t* _
 inline unsigned grid_for(size_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
 }  // namespace
 
-size_t tiled_salient_bytes(int E, int N, int n_sal) {
-  const size_t nsteps = (size_t)(n_sal + 31) / 32;
-  return (size_t)E * (N / 16) * nsteps * 1024;
-}
 
-hipError_t launch_repack(const QWeights& src, const QWeights& dst, hipStream_t s) {
+int launch_repack(const QWeights& src, const QWeights& dst, void* stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t ENK = (size_t)src.E * src.N * src.K;
-  if (ENK == 0) return hipSuccess;
+  if (ENK == 0) return 0;
   uint32_t* codes = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(dst.codes));
   if (src.fmt == 4) {  // per expert: canonical and tiled bytes and offsets agree
     size_t off = 0;
@@ -227,7 +224,7 @@ hipError_t launch_repack(const QWeights& src, const QWeights& dst, hipStream_t s
                          src.K, b, reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(dst.codes) + off), ndw);
       off += nbytes;
     }
-    return hipGetLastError();
+    return (int)hipGetLastError();
   }
   if (src.fmt == 1) {
     const size_t ndw = ENK / 8;
@@ -261,7 +258,7 @@ hipError_t launch_repack(const QWeights& src, const QWeights& dst, hipStream_t s
       }
     }
   }
-  return hipGetLastError();
+  return (int)hipGetLastError();
 }
 
 }  // namespace moe

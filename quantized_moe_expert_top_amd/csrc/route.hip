@@ -99,14 +99,15 @@ __global__ __launch_bounds__(256) void route_rank_kernel(const float* __restrict
 }
 }  // namespace
 
-hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
-  if (T == 0) return hipSuccess;
+int launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, void* stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) return 0;
   const int blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
   if (E <= 64)
     hipLaunchKernelGGL(route_rank_kernel, dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, logits, T, E, k, ids, w);
   else
     hipLaunchKernelGGL(route_topk_kernel, dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, logits, T, E, k, ids, w);
-  return hipGetLastError();
+  return (int)hipGetLastError();
 }
 
 }  // namespace moe

@@ -70,7 +70,7 @@ def test_permute_validation(lib):
     A = fake(0x1000)
     need = lib.moe_permute_workspace_size(8192, 8, 64, 1)
     assert need > 256
-    assert lib.moe_permute_workspace_size(32, 8, 64, 1) == 256 + 0 + 0 or lib.moe_permute_workspace_size(32, 8, 64, 1) >= 256
+    assert lib.moe_permute_workspace_size(32, 8, 64, 1) == 256   # one-workgroup path: the flag and counter words only
     assert lib.moe_permute_workspace_size(4, 1, 8, 2) == 0  # S must be 1 or 3
     args = lambda ws_bytes, ws=A: (A, None, 8192, 8, 64, A, A, A, A, None, 0, None, ws, ws_bytes, None)  # noqa: E731
     assert lib.moe_permute(*args(need - 1)) == WS_SMALL
@@ -114,9 +114,10 @@ def desc(fmt=q.MOE_W_INT4_GROUP, layout=q.MOE_LAYOUT_TILED, E=8, N=256, K=512, G
     return d
 
 
-def gemm(lib, d, A=0x1000, rows=64, gather=0x2000, k=2, seg=0x3000, M=128, epi=q.MOE_EPI_SWIGLU, out=0x4000):
+def gemm(lib, d, A=0x1000, rows=64, gather=0x2000, k=2, seg=0x3000, M=128, epi=q.MOE_EPI_SWIGLU, out=0x4000,
+         kernel=q.MOE_KERNEL_AUTO):
     return lib.moe_grouped_qgemm(ctypes.byref(d), fake(A) if A else None, rows, fake(gather) if gather else None, k,
-                                 fake(seg) if seg else None, M, epi, fake(out) if out else None, None, 0, None)
+                                 fake(seg) if seg else None, M, epi, kernel, fake(out) if out else None, None, 0, None)
 
 
 def test_grouped_qgemm_validation(lib):
@@ -143,29 +144,40 @@ def test_grouped_qgemm_validation(lib):
     assert gemm(lib, desc(), A=0) == NULL_ARG
     assert gemm(lib, desc(), out=0x4004) == MISALIGNED
     assert gemm(lib, desc(), M=0, A=0, seg=0, out=0) == OK           # empty problem
+    # kernel choices: unknown, or not for this format
+    assert gemm(lib, desc(), kernel=7) == BAD_FORMAT
+    assert gemm(lib, desc(), kernel=-1) == BAD_FORMAT
+    assert gemm(lib, desc(), kernel=q.MOE_KERNEL_SMALL_PER_WIDTH) == UNSUPPORTED            # nested MWQ only
+    delta = dict(fmt=q.MOE_W_DELTA2_SALIENT, z=2, ns=4)
+    assert gemm(lib, desc(**delta), kernel=q.MOE_KERNEL_TILE64) == UNSUPPORTED
+    assert gemm(lib, desc(**delta), kernel=q.MOE_KERNEL_LDS_DMA, epi=q.MOE_EPI_NONE) == UNSUPPORTED  # no base
+    assert gemm(lib, desc(**delta, base=0x80000), kernel=q.MOE_KERNEL_LDS_DMA) == UNSUPPORTED  # SwiGLU epilogue
+    mixed = desc(fmt=q.MOE_W_INT_PER_EXPERT, E=4, bits=[4, 2, 3, 2], zero=[8, 1, 3, 2])
+    assert gemm(lib, mixed, kernel=q.MOE_KERNEL_LDS_DMA) == UNSUPPORTED
+    assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(desc()), 64, 128, 9) == 0
 
 
 def test_grouped_qgemm_workspace(lib):
     # many rows per expert (INT4): the 128-row kernel keeps activation row sums in the workspace
     d = desc(E=8, N=256, K=512, G=128)
-    need = lib.moe_grouped_qgemm_workspace_size(ctypes.byref(d), 4096, 8192)
+    need = lib.moe_grouped_qgemm_workspace_size(ctypes.byref(d), 4096, 8192, 0)
     assert need == 4096 * (512 // 128) * 4
-    assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(d), 32, 64) == 0          # decode-sized: none
+    assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(d), 32, 64, 0) == 0          # decode-sized: none
     mwq = desc(fmt=q.MOE_W_MWQ_2_3_4, E=8, N=256, K=512, G=128)
     # nested MWQ: 1024 rows per expert take the 128-row kernel; 64 do not
-    assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(mwq), 4096, 8192) == 4096 * (512 // 128) * 4
-    assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(mwq), 256, 512) == 0
+    assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(mwq), 4096, 8192, 0) == 4096 * (512 // 128) * 4
+    assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(mwq), 256, 512, 0) == 0
     # long K, few channel groups and row tiles (a decode batch's down projection,
     # 32 rows, N 4096, K 14336): 32 x (2 + 8) work items -> 4 K splits of 28 blocks,
     # fp32 partial sums [4][32][4096]
     for fmt in (q.MOE_W_INT4_GROUP, q.MOE_W_MWQ_2_3_4):
         dn = desc(fmt=fmt, E=8, N=4096, K=14336, G=128)
-        assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(dn), 32, 32) == 4 * 32 * 4096 * 4
+        assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(dn), 32, 32, 0) == 4 * 32 * 4096 * 4
     # enough work items without a split (64 experts, N 2048, K 1024)
-    assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(desc(E=64, N=2048, K=1024, G=128)), 256, 256) == 0
+    assert lib.moe_grouped_qgemm_workspace_size(ctypes.byref(desc(E=64, N=2048, K=1024, G=128)), 256, 256, 0) == 0
     call = lambda ws, nbytes: lib.moe_grouped_qgemm(ctypes.byref(d), fake(0x1000), 4096, fake(0x2000), 2,  # noqa
-                                                    fake(0x3000), 8192, q.MOE_EPI_SWIGLU, fake(0x4000), ws, nbytes,
-                                                    None)
+                                                    fake(0x3000), 8192, q.MOE_EPI_SWIGLU, q.MOE_KERNEL_AUTO,
+                                                    fake(0x4000), ws, nbytes, None)
     assert call(None, 0) == WS_SMALL
     assert call(fake(0x5000), need - 1) == WS_SMALL
     assert call(None, need) == NULL_ARG
@@ -202,11 +214,12 @@ def test_repack_validation(lib):
 
 def test_combine_validation(lib):
     A = fake(0x1000)
-    assert lib.moe_unpermute_combine(A, 0, A, A, 4, 2, 12, A, None) == BAD_SHAPE
-    assert lib.moe_unpermute_combine(A, 3, A, A, 4, 2, 16, A, None) == BAD_FORMAT
-    assert lib.moe_unpermute_combine(None, 1, A, A, 4, 2, 16, A, None) == NULL_ARG
-    assert lib.moe_unpermute_combine(fake(0x1008), 0, A, A, 4, 2, 16, A, None) == MISALIGNED
-    assert lib.moe_unpermute_combine(None, 0, None, None, 0, 2, 16, None, None) == OK
+    assert lib.moe_unpermute_combine(A, 0, A, None, A, 4, 2, 12, A, None) == BAD_SHAPE
+    assert lib.moe_unpermute_combine(A, 3, A, None, A, 4, 2, 16, A, None) == BAD_FORMAT
+    assert lib.moe_unpermute_combine(None, 1, A, None, A, 4, 2, 16, A, None) == NULL_ARG
+    assert lib.moe_unpermute_combine(fake(0x1008), 0, A, None, A, 4, 2, 16, A, None) == MISALIGNED
+    assert lib.moe_unpermute_combine(A, 0, A, fake(0x2002), A, 4, 2, 16, A, None) == MISALIGNED   # n_valid
+    assert lib.moe_unpermute_combine(None, 0, None, None, None, 0, 2, 16, None, None) == OK
 
 
 def test_binding_refuses_missing_library(tmp_path):

@@ -83,4 +83,73 @@ def test_offload_lookahead_prefetch(G):
         ref_buf = G.q.moe_layer_forward(x, G.t(lg), cfg.k, gu, dn)
         torch.cuda.synchronize()
         assert torch.equal(out, ref_buf.out), f"step {i}"
+        ref = oracle.moe_forward(dict(d, logits=lg), cfg)
+        G.check_close(G.bf16_to_np(out), ref["out"], f"lookahead step {i}")
     assert queued > 0
+
+
+def _steps_logits(T, E, sets, seed):
+    """One logit batch per step: token t goes to expert sets[i][t % len(sets[i])]
+    (logit 10 against N(0,1) elsewhere), so each step touches a chosen set."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for s in sets:
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+        for t in range(T):
+            lg[t, s[t % len(s)]] = 10.0
+        out.append(lg)
+    return out
+
+
+def test_offload_split_k_down_keeps_earlier_rows(G):
+    """A down projection long enough in K to split (I = 2048) on a decode batch,
+    with hits and misses in the same step: the copied experts' GEMMs run on a
+    slice of the offset table whose first entry is not zero, and must leave the
+    resident experts' rows alone.  Every step equals the in-HBM layer bit for
+    bit and meets the bar against the oracle."""
+    from quantized_moe_expert_top_amd.offload import OffloadedMoeLayer
+    cfg = gen.config("tiny", T=8, E=6, k=1, H=256, I=2048, G=128, seed=124)
+    d = gen.generate(cfg)
+    gu, dn = G.tiled_layer(d, cfg)
+    ws = G.q.moe_grouped_qgemm_workspace_size(dn, cfg.T, cfg.T)
+    assert ws > 0, "this shape must split K"
+    layer = OffloadedMoeLayer(gu, dn, n_slots=4)
+    x = G.t(d["x"])
+    sets = [[0, 1, 2], [0, 1, 3], [2, 4, 5], [0, 3, 4], [1, 4]]
+    for i, lg in enumerate(_steps_logits(cfg.T, cfg.E, sets, 7)):
+        out, st = layer.forward(x, G.t(lg), cfg.k)
+        torch.cuda.synchronize()
+        if i > 0:
+            assert 0 < st.hits < st.experts, f"step {i}: want hits and misses"
+        ref_buf = G.q.moe_layer_forward(x, G.t(lg), cfg.k, gu, dn)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_buf.out), f"step {i}"
+        d2 = dict(d, logits=lg)
+        G.check_close(G.bf16_to_np(out), oracle.moe_forward(d2, cfg)["out"], f"split-K offload step {i}")
+
+
+def test_grouped_gemm_on_offset_slices(G):
+    """The grouped GEMM on two slices of one offset table (keys e and E + e):
+    each call writes only its own rows, including through split K, and the two
+    together give the one-call result bit for bit."""
+    cfg = gen.config("tiny", T=12, E=3, k=1, H=256, I=2048, G=128, seed=125)
+    d = gen.generate(cfg)
+    gu, dn = G.tiled_layer(d, cfg)
+    ids_np = oracle.route_topk(d["logits"], 1)[0].astype(np.int32)
+    half = (np.arange(cfg.T) % 2).reshape(-1, 1).astype(np.int32)
+    keys = G.t(ids_np + cfg.E * half)
+    perm2 = G.q.moe_permute(keys, 2 * cfg.E)
+    h = torch.randn((cfg.T, cfg.I), device="cuda:0").to(torch.bfloat16)
+    y = torch.full((cfg.T, cfg.H), float("nan"), device="cuda:0")
+    for part in (0, 1):
+        seg = perm2.seg_offsets[part * cfg.E:part * cfg.E + cfg.E + 1]
+        hp = h[perm2.sorted_pair.long()].contiguous()
+        G.q.moe_grouped_qgemm(dn, hp, seg, cfg.T, G.q.MOE_EPI_NONE_F32, out=y)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any()
+    # one call over expert-only keys on the same rows
+    perm1 = G.q.moe_permute(G.t(ids_np), cfg.E)
+    y1 = G.q.moe_grouped_qgemm(dn, h[perm1.sorted_pair.long()].contiguous(), perm1.seg_offsets, cfg.T,
+                               G.q.MOE_EPI_NONE_F32)
+    torch.cuda.synchronize()
+    assert torch.equal(y[perm2.pair_pos.long()], y1[perm1.pair_pos.long()])

@@ -2,7 +2,9 @@
 
 Bars: expert ids, counts, offsets and permutation indices bit-exact; gate
 weights within 1e-6 relative; bf16 outputs within relative L2 5e-3 and
-max-abs 2e-2 x RMS of the oracle output.
+max-abs 2e-2 x RMS of the oracle output, against the oracle's float64 layer
+(no intermediate rounding).  Several tests add an element-wise check against
+the oracle's bf16-activation variant (check_ulp).
 """
 import numpy as np
 import pytest
@@ -85,6 +87,29 @@ def test_permute_flags_invalid_ids(G):
     assert p.counts.cpu().numpy().sum() == 5
 
 
+def test_combine_skips_invalid_pairs(G):
+    """A pair whose id the grouping flagged (placed after every valid segment,
+    where no GEMM writes) adds nothing to its token's output when the combine
+    gets the number of valid rows; its row is never read (NaN there stays out)."""
+    ids = np.array([[0, 1], [2, 7], [1, 3]], np.int32)   # E = 4: pair 3 is invalid
+    p = G.q.moe_permute(G.t(ids), 4)
+    torch.cuda.synchronize()
+    nv = int(p.seg_offsets.cpu().numpy()[-1])
+    assert nv == 5
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal((6, 16)).astype(np.float32)
+    y[nv:] = np.nan
+    w = np.array([[0.5, 0.5], [0.25, 0.75], [0.6, 0.4]], np.float32)
+    out = G.q.moe_unpermute_combine(G.t(y), p.pair_pos, G.t(w), 3, 2, n_valid=p.seg_offsets[-1:])
+    torch.cuda.synchronize()
+    got = G.bf16_to_np(out)
+    pos = p.pair_pos.cpu().numpy()
+    y0 = np.where(np.arange(6)[:, None] < nv, y, 0.0).astype(np.float64)
+    ref = oracle.unpermute_combine(y0, pos, w.astype(np.float64), 3, 2)
+    assert np.isfinite(got).all()
+    assert np.all(np.abs(got - ref) <= G.bf16_ulp(ref))   # fp32 sums, one bf16 rounding
+
+
 @pytest.mark.parametrize("T,E,k,mwq", [(1, 8, 2, False), (16, 8, 2, True), (32, 64, 8, False), (64, 64, 8, True),
                                         (64, 64, 64, False),
                                         (65, 64, 4, True), (512, 8, 8, False), (513, 8, 8, False),
@@ -114,9 +139,9 @@ def test_route_permute_matches_oracle(G, T, E, k, mwq):
 
 
 # --------------------------------------------------------------- full layers
-def _layer_parity(G, cfg, tokens=None):
-    d = gen.generate(cfg)
-    buf = G.run_layer(d, cfg)
+def _layer_parity(G, cfg, tokens=None, kernel=0, d=None):
+    d = gen.generate(cfg) if d is None else d
+    buf = G.run_layer(d, cfg, kernel=kernel)
     ref = oracle.moe_forward(d, cfg, tokens=tokens)
     assert np.array_equal(buf.ids.cpu().numpy(), ref["ids"])
     np.testing.assert_allclose(buf.w.cpu().numpy().astype(np.float64), ref["w"], rtol=G.GATE_RTOL, atol=0)
@@ -126,13 +151,13 @@ def _layer_parity(G, cfg, tokens=None):
     assert np.array_equal(buf.perm.pair_pos.cpu().numpy(), ref["pair_pos"])
     sel = ref["tokens"]
     rows = ref["pair_pos"].reshape(cfg.T, cfg.k)[sel].ravel()
-    # intermediates: diagnostics with a looser bar (h is rounded to bf16 before the down GEMM)
+    # intermediates: diagnostics with a looser bar (the kernels round h to bf16)
     hm = oracle.compare(G.bf16_to_np(buf.h)[rows], ref["h_perm"][rows])
-    ym = oracle.compare(G.bf16_to_np(buf.y_perm)[rows], ref["y_perm"][rows])
+    ym = oracle.compare(G.bf16_to_np(buf.y_perm)[rows], ref["y_perm_h16"][rows])
     assert hm["rel_l2"] < 1e-2 and ym["rel_l2"] < 1e-2, (hm, ym)
     m = G.check_close(G.bf16_to_np(buf.out)[sel], ref["out"][sel], cfg.name)
     print(cfg.name, "h", hm, "y", ym, "out", m)
-    return buf
+    return buf, ref
 
 
 def test_layer_tiny_full(G):
@@ -171,22 +196,19 @@ def test_layer_g128_one_hot_expert(G):
     buf = G.run_layer(d, cfg)
     ref = oracle.moe_forward(d, cfg)
     G.check_close(G.bf16_to_np(buf.out), ref["out"], "one expert")
+    G.check_ulp(G.bf16_to_np(buf.out), ref["out_h16"], "one expert")
 
 
 def test_layer_k_equals_E(G):
     _layer_parity(G, gen.config("tiny", T=40, E=4, k=4, seed=5))
 
 
-def test_layer_prefill_sampled(G):
-    cfg = gen.config("olmoe_prefill")
-    tokens = np.random.default_rng(1).choice(cfg.T, size=48, replace=False)
-    _layer_parity(G, cfg, tokens=np.sort(tokens))
-
-
-def test_layer_prefill_zipf_sampled(G):
-    cfg = gen.config("olmoe_prefill_zipf")
-    tokens = np.random.default_rng(2).choice(cfg.T, size=48, replace=False)
-    _layer_parity(G, cfg, tokens=np.sort(tokens))
+@pytest.mark.parametrize("name", ["olmoe_prefill", "olmoe_prefill_zipf"])
+def test_layer_prefill_full(G, name):
+    """The prefill-shaped layer (8192 tokens, 64 experts, top-8), uniform and
+    Zipf-skewed routing, in the launch configuration the benchmark times:
+    every token against the oracle."""
+    _layer_parity(G, gen.config(name))
 
 
 @pytest.mark.parametrize("over", [
@@ -196,11 +218,18 @@ def test_layer_prefill_zipf_sampled(G):
     dict(T=64, E=2, k=1, H=128, I=128, G=128, seed=64),     # a single K block
     dict(T=150, E=5, k=2, H=1024, I=640, G=128, seed=65),   # 8 / 5 K blocks
 ])
-def test_layer_prefill_dma_kernel(G, over, monkeypatch):
+def test_layer_prefill_dma_kernel(G, over):
     """The 128-row LDS-DMA kernel forced on small layers (it is chosen by
     itself for INT4 segments of about 96 rows and more)."""
-    monkeypatch.setenv("MOE_QGEMM_PATH", "dma")
-    _layer_parity(G, gen.config("tiny", **over))
+    _layer_parity(G, gen.config("tiny", **over), kernel=G.q.MOE_KERNEL_LDS_DMA)
+
+
+@pytest.mark.parametrize("kernel", ["SMALL", "TILE64_WIDE", "TILE64", "TILE128"])
+def test_layer_int4_every_kernel(G, kernel):
+    """Every INT4 kernel choice on one ragged layer (about 75 rows per expert:
+    several row tiles of each size, a partial last tile per expert)."""
+    cfg = gen.config("tiny", T=150, E=8, k=4, H=512, I=384, G=64, seed=66)
+    _layer_parity(G, cfg, kernel=getattr(G.q, "MOE_KERNEL_" + kernel))
 
 
 def test_layer_mwq_small_full(G):
@@ -217,16 +246,17 @@ def test_layer_mwq_all_b4_equals_int4(G):
     G.check_close(G.bf16_to_np(buf.out), ref["out"], "mwq b=4")
 
 
-def test_layer_mwq_full_size_sampled(G):
-    cfg = gen.config("mixtral_mwq")
-    _layer_parity(G, cfg, tokens=np.array([0, 211, 377, 510]))
+def test_layer_mwq_full_size(G):
+    """The Mixtral-shaped nested-plane layer (512 tokens, 8 experts, top-2, H
+    4096, I 14336) in the benchmark's launch configuration: every token."""
+    _layer_parity(G, gen.config("mixtral_mwq"))
 
 
 def test_layer_mwq_decode_full(G):
     """Nested planes at a decode batch (16 tokens): most bit-width segments hold
     one or two rows, and a segment loads only the planes its width needs."""
-    _layer_parity(G, gen.config("mixtral_mwq_decode", H=1024, I=2048))       # every token
-    _layer_parity(G, gen.config("mixtral_mwq_decode"), tokens=np.array([3, 12]))  # full size, sampled
+    _layer_parity(G, gen.config("mixtral_mwq_decode", H=1024, I=2048))   # a smaller layer
+    _layer_parity(G, gen.config("mixtral_mwq_decode"))                    # full size, every token
 
 
 @pytest.mark.parametrize("over", [
@@ -235,21 +265,19 @@ def test_layer_mwq_decode_full(G):
     dict(T=150, E=8, k=4, H=512, I=256, G=128, seed=83),   # ~75 rows per expert, ragged chunks
     dict(T=64, E=2, k=2, H=128, I=128, G=128, seed=84),    # one K block: odd groups per channel, register scales
 ])
-def test_layer_mwq_prefill_dma_kernel(G, over, monkeypatch):
+def test_layer_mwq_prefill_dma_kernel(G, over):
     """Nested planes in the 128-row LDS-DMA kernel (chosen by itself from 256
     rows per expert for gate/up, 512 for down): 16-row chunks of every width,
     one expert per workgroup."""
-    monkeypatch.setenv("MOE_QGEMM_PATH", "dma")
     cfg = gen.config("mixtral_mwq", **over)
-    buf = _layer_parity(G, cfg)
-    G.check_ulp(G.bf16_to_np(buf.out), oracle.moe_forward(gen.generate(cfg), cfg)["out"], str(over))
+    buf, ref = _layer_parity(G, cfg, kernel=G.q.MOE_KERNEL_LDS_DMA)
+    G.check_ulp(G.bf16_to_np(buf.out), ref["out_h16"], str(over))
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, "cycle"])
-def test_layer_mwq_prefill_widths(G, bits, monkeypatch):
+def test_layer_mwq_prefill_widths(G, bits):
     """The 128-row kernel with one width everywhere, or widths cycling per pair
     (chunks of every width in each workgroup, partial chunks at each end)."""
-    monkeypatch.setenv("MOE_QGEMM_PATH", "dma")
     cfg = gen.config("mixtral_mwq", T=150, E=3, k=2, H=512, I=1024, seed=85)
     d = gen.generate(cfg)
     if bits == "cycle":
@@ -257,15 +285,15 @@ def test_layer_mwq_prefill_widths(G, bits, monkeypatch):
     else:
         d["pair_bits"][:] = bits
     ref = oracle.moe_forward(d, cfg)
-    buf = G.run_layer(d, cfg)
+    buf = G.run_layer(d, cfg, kernel=G.q.MOE_KERNEL_LDS_DMA)
     assert np.array_equal(buf.perm.seg_offsets.cpu().numpy(), ref["seg_offsets"])
     out = G.bf16_to_np(buf.out)
     G.check_close(out, ref["out"], f"mwq prefill widths {bits}")
-    G.check_ulp(out, ref["out"], f"mwq prefill widths {bits}")
+    G.check_ulp(out, ref["out_h16"], f"mwq prefill widths {bits}")
 
 
 @pytest.mark.parametrize("bits", ["drawn", 2, 3, 4, "cycle"])
-def test_layer_mwq_decode_widths(G, bits, monkeypatch):
+def test_layer_mwq_decode_widths(G, bits):
     """16-row tiles that take all widths of an expert at once: about 23 rows
     per expert, so tiles cross the b = 4 / 3 / 2 sub-segment boundaries; some
     widths absent; the one-width-per-tile kernel gives the same bits.  Besides
@@ -282,9 +310,8 @@ def test_layer_mwq_decode_widths(G, bits, monkeypatch):
     assert np.array_equal(buf.perm.seg_offsets.cpu().numpy(), ref["seg_offsets"])
     out_fused = G.bf16_to_np(buf.out)
     G.check_close(out_fused, ref["out"], f"mwq widths {bits}")
-    G.check_ulp(out_fused, ref["out"], f"mwq widths {bits}")
-    monkeypatch.setenv("MOE_QGEMM_PATH", "split")
-    out_split = G.bf16_to_np(G.run_layer(d, cfg).out)
+    G.check_ulp(out_fused, ref["out_h16"], f"mwq widths {bits}")
+    out_split = G.bf16_to_np(G.run_layer(d, cfg, kernel=G.q.MOE_KERNEL_SMALL_PER_WIDTH).out)
     assert np.array_equal(out_fused, out_split)
 
 
@@ -302,7 +329,7 @@ def test_decode_split_k(G, name, over):
     buf = G.run_layer(d, cfg, gu, dn)
     ref = oracle.moe_forward(d, cfg)
     assert np.array_equal(buf.perm.seg_offsets.cpu().numpy(), ref["seg_offsets"])
-    assert oracle.compare(buf.y_perm.cpu().numpy(), ref["y_perm"])["rel_l2"] < 1e-2
+    assert oracle.compare(buf.y_perm.cpu().numpy(), ref["y_perm_h16"])["rel_l2"] < 1e-2
     G.check_close(G.bf16_to_np(buf.out), ref["out"], name)
     y16 = G.q.moe_grouped_qgemm(dn, buf.h, buf.perm.seg_offsets, cfg.T * cfg.k, G.q.MOE_EPI_NONE)
     torch.cuda.synchronize()
@@ -327,14 +354,14 @@ def test_layer_mixed_decode_full(G):
 ])
 def test_layer_mixed_widths(G, over):
     cfg = gen.config("olmoe_mixed_decode", **over)
-    buf = _layer_parity(G, cfg)
-    G.check_ulp(G.bf16_to_np(buf.out), oracle.moe_forward(gen.generate(cfg), cfg)["out"], str(over))
+    buf, ref = _layer_parity(G, cfg)
+    G.check_ulp(G.bf16_to_np(buf.out), ref["out_h16"], str(over))
 
 
 # ------------------------------------------------------------------- delta
-def _delta_parity(G, cfg, tokens=None):
+def _delta_parity(G, cfg, tokens=None, kernel=0):
     d = gen.generate(cfg)
-    perm, y_perm, out = G.run_delta(d, cfg)
+    perm, y_perm, out = G.run_delta(d, cfg, kernel=kernel)
     ref = oracle.delta_linear(d, cfg, tokens=tokens)
     assert np.array_equal(perm.counts.cpu().numpy(), ref["counts"])
     assert np.array_equal(perm.sorted_pair.cpu().numpy(), ref["sorted_pair"])
@@ -355,16 +382,16 @@ def test_delta_small_full(G):
     dict(requests=10, tokens_per_request=13, K=128, N=128, E=2, n_salient=3, seed=39),  # one K block: prologue past the end
     dict(requests=9, tokens_per_request=16, K=1152, N=128, E=2, n_salient=5, seed=49),  # three steady passes, then two tail passes
 ])
-def test_delta_dma_kernel(G, over, monkeypatch):
+def test_delta_dma_kernel(G, over):
     """The 128-row LDS-DMA delta kernel forced on small layers (it is chosen by
     itself for about 96 rows per expert and more)."""
-    monkeypatch.setenv("MOE_QGEMM_PATH", "dma")
-    _delta_parity(G, gen.config("meswitch_delta", **over))
+    _delta_parity(G, gen.config("meswitch_delta", **over), kernel=G.q.MOE_KERNEL_LDS_DMA)
 
 
-def test_delta_full_size_sampled(G):
-    cfg = gen.config("meswitch_delta")
-    _delta_parity(G, cfg, tokens=np.array([0, 17, 1000, 2047, 3333, 4095]))
+def test_delta_full_size(G):
+    """The ME-Switch-shaped delta layer (4096 tokens, 16 experts, 4096 -> 14336)
+    in the benchmark's launch configuration: every token."""
+    _delta_parity(G, gen.config("meswitch_delta"))
 
 
 # ---------------------------------------------------------- combine, determinism

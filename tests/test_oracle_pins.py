@@ -63,13 +63,16 @@ def py_bf16(v):
     return math.ldexp(round(m * 256.0), e - 8)   # round(): half to even
 
 
-def py_ffn(x, wgu, wd, I):
-    """Textbook SwiGLU on Python lists: wgu[n][k] (2I x H), wd[m][n] (H x I);
-    the activation h entering the down projection is a 16-bit (bf16) value."""
+def py_ffn(x, wgu, wd, I, h16=False):
+    """Textbook SwiGLU on Python lists: wgu[n][k] (2I x H), wd[m][n] (H x I).
+    With h16 the activation h entering the down projection is first rounded to
+    bf16 (the oracle's diagnostic 16-bit-activation variant)."""
     H = len(x)
     g = [sum(x[kk] * wgu[n][kk] for kk in range(H)) for n in range(I)]
     u = [sum(x[kk] * wgu[I + n][kk] for kk in range(H)) for n in range(I)]
-    h = [py_bf16(py_silu(g[n]) * u[n]) for n in range(I)]
+    h = [py_silu(g[n]) * u[n] for n in range(I)]
+    if h16:
+        h = [py_bf16(v) for v in h]
     return [sum(h[n] * wd[m][n] for n in range(I)) for m in range(H)]
 
 
@@ -327,6 +330,36 @@ def test_delta_linear_reductions():
         assert y.tolist() == expect
 
 
+def test_delta_linear_matches_dense_bruteforce_several_experts():
+    """y[t] = x[t] (W_base + D_{e(t)})^T evaluated densely in pure Python, per
+    token with its own expert (ME-Switch: expert weight = shared base + its
+    delta), against the grouped oracle: three experts, tokens on each, base
+    and deltas non-zero."""
+    cfg = gen.config("meswitch_delta", requests=6, tokens_per_request=2, K=32, N=8, E=3, n_salient=2, seed=13)
+    d = gen.gen_delta_linear(cfg)
+    d["ids"] = np.array([0, 2, 1, 1, 2, 0, 0, 1, 2, 2, 1, 0], np.int32)
+    res = oracle.delta_linear(d, cfg)
+    x = [[bf16_val(int(v)) for v in row] for row in d["x"]]
+    base = [[bf16_val(int(v)) for v in row] for row in d["base"]]
+
+    def delta(e, n, kk):
+        sal = [int(v) for v in d["salient_idx"][e]]
+        if kk in sal:
+            return bf16_val(int(d["salient_val"][e][sal.index(kk)][n]))
+        c = (int(d["codes"][e][n][kk // 4]) >> (2 * (kk % 4))) & 3
+        return f16_val(int(d["step"][e][n])) * (c - 2)
+
+    for t in range(cfg.T):
+        e = int(d["ids"][t])
+        want = [sum(x[t][kk] * (base[n][kk] + delta(e, n, kk)) for kk in range(cfg.K)) for n in range(cfg.N)]
+        assert rel_err(res["out"][t], want) < 1e-12
+        # another expert's delta gives a visibly different row (the check can tell experts apart)
+        other = (e + 1) % cfg.E
+        alt = [sum(x[t][kk] * (base[n][kk] + delta(other, n, kk)) for kk in range(cfg.K)) for n in range(cfg.N)]
+        assert rel_err(alt, want) > 1e-4
+    assert sorted(set(d["ids"].tolist())) == [0, 1, 2]
+
+
 def test_unpack_2bit_against_python_packing():
     rnd = random.Random(2)
     fields = [rnd.randrange(4) for _ in range(64)]
@@ -357,13 +390,17 @@ def test_moe_forward_matches_dense_bruteforce_int4():
         order = sorted(range(cfg.E), key=lambda e: (-row[e], e))[:cfg.k]
         ex = [math.exp(row[e] - row[order[0]]) for e in order]
         gates = [v / sum(ex) for v in ex]
-        acc = [0.0] * cfg.H
+        acc, acc16 = [0.0] * cfg.H, [0.0] * cfg.H
         for j, e in enumerate(order):
             wgu = [_py_dequant_int4(d["gu_codes"][e][n], d["gu_scales"][e][n], cfg.G) for n in range(2 * cfg.I)]
             wd = [_py_dequant_int4(d["dn_codes"][e][m], d["dn_scales"][e][m], cfg.G) for m in range(cfg.H)]
             y = py_ffn(x[t], wgu, wd, cfg.I)
+            y16 = py_ffn(x[t], wgu, wd, cfg.I, h16=True)
             acc = [a + gates[j] * v for a, v in zip(acc, y)]
+            acc16 = [a + gates[j] * v for a, v in zip(acc16, y16)]
         assert rel_err(res["out"][t], acc) < 1e-12
+        assert rel_err(res["out_h16"][t], acc16) < 1e-12
+        assert rel_err(res["out_h16"][t], acc) > 1e-6   # the bf16 rounding of h is visible
 
 
 def test_moe_forward_k1_identical_experts_is_dense_ffn():
@@ -379,6 +416,7 @@ def test_moe_forward_k1_identical_experts_is_dense_ffn():
     for t in range(cfg.T):
         xt = [bf16_val(int(v)) for v in d["x"][t]]
         assert rel_err(res["out"][t], py_ffn(xt, wgu, wd, cfg.I)) < 1e-12
+        assert rel_err(res["out_h16"][t], py_ffn(xt, wgu, wd, cfg.I, h16=True)) < 1e-12
 
 
 def test_moe_forward_matches_dense_bruteforce_mwq():
@@ -390,7 +428,7 @@ def test_moe_forward_matches_dense_bruteforce_mwq():
         row = [float(v) for v in d["logits"][t]]
         order = sorted(range(cfg.E), key=lambda e: (-row[e], e))[:cfg.k]
         ex = [math.exp(row[e] - row[order[0]]) for e in order]
-        acc = [0.0] * cfg.H
+        acc, acc16 = [0.0] * cfg.H, [0.0] * cfg.H
         for j, e in enumerate(order):
             b = int(d["pair_bits"][t * cfg.k + j])
             mask = {4: 15, 3: 14, 2: 12}[b]
@@ -405,9 +443,13 @@ def test_moe_forward_matches_dense_bruteforce_mwq():
                     rows.append([f16_val(int(d[prefix + "scales"][e][n][i // cfg.G])) * ((full[i] & mask) - 8)
                                  for i in range(kdim)])
                 return rows
-            y = py_ffn(xt, mat("gu_", 2 * cfg.I, cfg.H), mat("dn_", cfg.H, cfg.I), cfg.I)
+            wgu, wd = mat("gu_", 2 * cfg.I, cfg.H), mat("dn_", cfg.H, cfg.I)
+            y = py_ffn(xt, wgu, wd, cfg.I)
+            y16 = py_ffn(xt, wgu, wd, cfg.I, h16=True)
             acc = [a + ex[j] / sum(ex) * v for a, v in zip(acc, y)]
+            acc16 = [a + ex[j] / sum(ex) * v for a, v in zip(acc16, y16)]
         assert rel_err(res["out"][t], acc) < 1e-12
+        assert rel_err(res["out_h16"][t], acc16) < 1e-12
 
 
 def test_moe_forward_token_subset_matches_full():
@@ -477,7 +519,7 @@ def test_per_expert_width_reduces_to_int4_and_2bit_layouts():
     assert np.array_equal(w4, oracle.dequant_int4(st4.reshape(N, K // 2), s, G, 8))
     st2 = rng.integers(0, 256, size=N * K // 4, dtype=np.uint8)
     w2 = oracle.dequant_per_expert(st2, s, N, K, G, 2, 1)
-    ref2 = np.repeat(oracle.f16_to_f64(s), G, axis=-1) * (oracle.unpack_u2(st2.reshape(N, K // 4)) - 1)
+    ref2 = np.repeat(oracle.f16_to_f64(s), G, axis=-1) * (oracle.unpack_u2(st2.reshape(N, K // 4)).astype(np.int64) - 1)
     assert np.array_equal(w2, ref2)
 
 
@@ -531,8 +573,12 @@ def test_moe_forward_matches_dense_bruteforce_mixed():
         row = [float(v) for v in d["logits"][t]]
         order = sorted(range(cfg.E), key=lambda e: (-row[e], e))[:cfg.k]
         ex = [math.exp(row[e] - row[order[0]]) for e in order]
-        acc = [0.0] * cfg.H
+        acc, acc16 = [0.0] * cfg.H, [0.0] * cfg.H
         for j, e in enumerate(order):
-            y = py_ffn(xt, mat("gu_", e, 2 * cfg.I, cfg.H), mat("dn_", e, cfg.H, cfg.I), cfg.I)
+            wgu, wd = mat("gu_", e, 2 * cfg.I, cfg.H), mat("dn_", e, cfg.H, cfg.I)
+            y = py_ffn(xt, wgu, wd, cfg.I)
+            y16 = py_ffn(xt, wgu, wd, cfg.I, h16=True)
             acc = [a + ex[j] / sum(ex) * v for a, v in zip(acc, y)]
+            acc16 = [a + ex[j] / sum(ex) * v for a, v in zip(acc16, y16)]
         assert rel_err(res["out"][t], acc) < 1e-12
+        assert rel_err(res["out_h16"][t], acc16) < 1e-12
