@@ -12,6 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_qexpert.so")
+PROBE_LIB = os.path.join(HERE, "libmoe_probe.so")  # measurement-only ceiling probes (bench.py)
 SOURCES = ["route.hip", "permute.hip", "qgemm.hip", "combine.hip", "repack.hip", "runtime.hip"]
 HOST_SOURCES = ["abi.cpp", "plan.cpp"]  # validation and launch planning: plain C++, no HIP headers
 
@@ -42,17 +43,18 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = HOST_SOURCES + SOURCES
+    srcs = HOST_SOURCES + SOURCES + ["probe.hip"]
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"built {LIB}")
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    for lib, parts in ((LIB, HOST_SOURCES + SOURCES), (PROBE_LIB, ["probe.hip"])):
+        tmp = lib + ".tmp"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[objs[p] for p in parts], "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, lib)
+        if verbose:
+            print(f"built {lib}")
     return LIB
 
 

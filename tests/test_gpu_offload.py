@@ -7,6 +7,7 @@ import torch
 
 import gen
 import oracle
+from oracle import cpp as REF  # the C++17 float64 oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +40,7 @@ def test_offload_steps_match_resident_layer(G, overlap):
         assert torch.equal(out, ref_buf.out), f"step {step}"
         d2 = dict(d)
         d2["logits"] = dl
-        ref = oracle.moe_forward(d2, cfg)
+        ref = REF.moe_forward(d2, cfg)
         G.check_close(G.bf16_to_np(out), ref["out"], f"offload step {step}")
         touched = set(int(e) for e in np.unique(ref["ids"]))
         assert st.experts == len(touched)
@@ -71,7 +72,7 @@ def test_offload_lookahead_prefetch(G):
     x = G.t(d["x"])
     seeds = [1, 2, 3, 4, 5, 6]
     logits = [gen.generate(gen.config("tiny", T=4, E=16, k=2, H=256, I=256, G=64, seed=s))["logits"] for s in seeds]
-    nxt = [oracle.route_topk(lg, cfg.k)[0] for lg in logits]  # the pre-gate's ids, known ahead
+    nxt = [REF.route_topk(lg, cfg.k)[0] for lg in logits]  # the pre-gate's ids, known ahead
     queued = 0
     for i, lg in enumerate(logits):
         out, st = layer.forward(x, G.t(lg), cfg.k)
@@ -83,7 +84,7 @@ def test_offload_lookahead_prefetch(G):
         ref_buf = G.q.moe_layer_forward(x, G.t(lg), cfg.k, gu, dn)
         torch.cuda.synchronize()
         assert torch.equal(out, ref_buf.out), f"step {i}"
-        ref = oracle.moe_forward(dict(d, logits=lg), cfg)
+        ref = REF.moe_forward(dict(d, logits=lg), cfg)
         G.check_close(G.bf16_to_np(out), ref["out"], f"lookahead step {i}")
     assert queued > 0
 
@@ -125,7 +126,7 @@ def test_offload_split_k_down_keeps_earlier_rows(G):
         torch.cuda.synchronize()
         assert torch.equal(out, ref_buf.out), f"step {i}"
         d2 = dict(d, logits=lg)
-        G.check_close(G.bf16_to_np(out), oracle.moe_forward(d2, cfg)["out"], f"split-K offload step {i}")
+        G.check_close(G.bf16_to_np(out), REF.moe_forward(d2, cfg)["out"], f"split-K offload step {i}")
 
 
 def test_grouped_gemm_on_offset_slices(G):
@@ -135,7 +136,7 @@ def test_grouped_gemm_on_offset_slices(G):
     cfg = gen.config("tiny", T=12, E=3, k=1, H=256, I=2048, G=128, seed=125)
     d = gen.generate(cfg)
     gu, dn = G.tiled_layer(d, cfg)
-    ids_np = oracle.route_topk(d["logits"], 1)[0].astype(np.int32)
+    ids_np = REF.route_topk(d["logits"], 1)[0].astype(np.int32)
     half = (np.arange(cfg.T) % 2).reshape(-1, 1).astype(np.int32)
     keys = G.t(ids_np + cfg.E * half)
     perm2 = G.q.moe_permute(keys, 2 * cfg.E)

@@ -12,6 +12,7 @@ import torch
 
 import gen
 import oracle
+from oracle import cpp as REF  # the C++17 float64 oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +32,7 @@ def test_route_topk_parity(G, name, k):
     cfg = gen.config(name)
     logits = gen._logits(cfg)
     ids, w = G.q.moe_route_topk(G.t(logits), k)
-    ref_ids, ref_w = oracle.route_topk(logits, k)
+    ref_ids, ref_w = REF.route_topk(logits, k)
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
     np.testing.assert_allclose(w.cpu().numpy().astype(np.float64), ref_w, rtol=G.GATE_RTOL, atol=0)
 
@@ -42,7 +43,7 @@ def test_route_topk_edges_and_ties(G, T, E, k):
     logits = rng.integers(-2, 3, size=(T, E)).astype(np.float32)  # heavy ties
     logits[0, :] = 0.0
     ids, w = G.q.moe_route_topk(G.t(logits), k)
-    ref_ids, ref_w = oracle.route_topk(logits, k)
+    ref_ids, ref_w = REF.route_topk(logits, k)
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
     np.testing.assert_allclose(w.cpu().numpy().astype(np.float64), ref_w, rtol=G.GATE_RTOL, atol=0)
 
@@ -53,7 +54,7 @@ def _perm_check(G, ids_np, E, bits_np=None):
     bits = G.t(bits_np.astype(np.uint8)) if bits_np is not None else None
     p = G.q.moe_permute(ids, E, pair_bits=bits)
     torch.cuda.synchronize()
-    c, s, sp, pp = oracle.permute(ids_np, E, bits_np)
+    c, s, sp, pp = REF.permute(ids_np, E, bits_np)
     assert np.array_equal(p.counts.cpu().numpy(), c)
     assert np.array_equal(p.seg_offsets.cpu().numpy(), s)
     assert np.array_equal(p.sorted_pair.cpu().numpy(), sp)
@@ -122,8 +123,8 @@ def test_route_permute_matches_oracle(G, T, E, k, mwq):
     logits = rng.standard_normal((T, E)).astype(np.float32)
     logits[:, 3 % E] = logits[:, 1 % E]                      # exact ties
     bits = rng.integers(2, 5, size=T * k).astype(np.uint8) if mwq else None
-    rid, rw = oracle.route_topk(logits.astype(np.float64), k)
-    counts, offsets, sorted_pair, pair_pos = oracle.permute(rid, E, pair_bits=bits)
+    rid, rw = REF.route_topk(logits.astype(np.float64), k)
+    counts, offsets, sorted_pair, pair_pos = REF.permute(rid, E, pair_bits=bits)
     p = None
     for _ in range(2):
         ids, w, p = G.q.moe_route_permute(G.t(logits), k, pair_bits=None if bits is None else G.t(bits), out=p)
@@ -142,7 +143,7 @@ def test_route_permute_matches_oracle(G, T, E, k, mwq):
 def _layer_parity(G, cfg, tokens=None, kernel=0, d=None):
     d = gen.generate(cfg) if d is None else d
     buf = G.run_layer(d, cfg, kernel=kernel)
-    ref = oracle.moe_forward(d, cfg, tokens=tokens)
+    ref = REF.moe_forward(d, cfg, tokens=tokens)
     assert np.array_equal(buf.ids.cpu().numpy(), ref["ids"])
     np.testing.assert_allclose(buf.w.cpu().numpy().astype(np.float64), ref["w"], rtol=G.GATE_RTOL, atol=0)
     assert np.array_equal(buf.perm.counts.cpu().numpy(), ref["counts"])
@@ -194,7 +195,7 @@ def test_layer_g128_one_hot_expert(G):
     d = gen.generate(cfg)
     d["logits"][:, 3] = 50.0
     buf = G.run_layer(d, cfg)
-    ref = oracle.moe_forward(d, cfg)
+    ref = REF.moe_forward(d, cfg)
     G.check_close(G.bf16_to_np(buf.out), ref["out"], "one expert")
     G.check_ulp(G.bf16_to_np(buf.out), ref["out_h16"], "one expert")
 
@@ -242,7 +243,7 @@ def test_layer_mwq_all_b4_equals_int4(G):
     d = gen.generate(cfg)
     d["pair_bits"][:] = 4
     buf = G.run_layer(d, cfg)
-    ref = oracle.moe_forward(d, cfg)
+    ref = REF.moe_forward(d, cfg)
     G.check_close(G.bf16_to_np(buf.out), ref["out"], "mwq b=4")
 
 
@@ -284,7 +285,7 @@ def test_layer_mwq_prefill_widths(G, bits):
         d["pair_bits"][:] = (4 - np.arange(d["pair_bits"].size) % 3).reshape(d["pair_bits"].shape)
     else:
         d["pair_bits"][:] = bits
-    ref = oracle.moe_forward(d, cfg)
+    ref = REF.moe_forward(d, cfg)
     buf = G.run_layer(d, cfg, kernel=G.q.MOE_KERNEL_LDS_DMA)
     assert np.array_equal(buf.perm.seg_offsets.cpu().numpy(), ref["seg_offsets"])
     out = G.bf16_to_np(buf.out)
@@ -305,7 +306,7 @@ def test_layer_mwq_decode_widths(G, bits):
         d["pair_bits"][:] = (4 - np.arange(d["pair_bits"].size) % 3).reshape(d["pair_bits"].shape)
     elif bits != "drawn":
         d["pair_bits"][:] = bits
-    ref = oracle.moe_forward(d, cfg)
+    ref = REF.moe_forward(d, cfg)
     buf = G.run_layer(d, cfg)
     assert np.array_equal(buf.perm.seg_offsets.cpu().numpy(), ref["seg_offsets"])
     out_fused = G.bf16_to_np(buf.out)
@@ -327,7 +328,7 @@ def test_decode_split_k(G, name, over):
     d = gen.generate(cfg)
     gu, dn = G.tiled_layer(d, cfg)
     buf = G.run_layer(d, cfg, gu, dn)
-    ref = oracle.moe_forward(d, cfg)
+    ref = REF.moe_forward(d, cfg)
     assert np.array_equal(buf.perm.seg_offsets.cpu().numpy(), ref["seg_offsets"])
     assert oracle.compare(buf.y_perm.cpu().numpy(), ref["y_perm_h16"])["rel_l2"] < 1e-2
     G.check_close(G.bf16_to_np(buf.out), ref["out"], name)
@@ -362,7 +363,7 @@ def test_layer_mixed_widths(G, over):
 def _delta_parity(G, cfg, tokens=None, kernel=0):
     d = gen.generate(cfg)
     perm, y_perm, out = G.run_delta(d, cfg, kernel=kernel)
-    ref = oracle.delta_linear(d, cfg, tokens=tokens)
+    ref = REF.delta_linear(d, cfg, tokens=tokens)
     assert np.array_equal(perm.counts.cpu().numpy(), ref["counts"])
     assert np.array_equal(perm.sorted_pair.cpu().numpy(), ref["sorted_pair"])
     sel = np.arange(cfg.T) if tokens is None else np.asarray(tokens)

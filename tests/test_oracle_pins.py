@@ -1,6 +1,7 @@
-"""Pins for the CPU oracle: checks against facts the pages and plain mathematics
-fix, written independently of the oracle's own code (brute force over subsets,
-pure-Python packing and dense evaluation, closed forms, invariants)."""
+"""Pins for the CPU oracles (numpy, and C++17 in oracle/moe_oracle.cpp): checks
+against facts the pages and plain mathematics fix, written independently of
+the oracles' own code (brute force over subsets, pure-Python packing and dense
+evaluation, closed forms, invariants).  Layer-level pins run on both."""
 import itertools
 import json
 import math
@@ -14,6 +15,15 @@ import gen
 import oracle
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(params=["numpy", "cpp"])
+def impl(request):
+    """Each pin runs on both oracle implementations: the numpy one and the C++17 one."""
+    if request.param == "numpy":
+        return oracle
+    from oracle import cpp
+    return cpp
 
 
 # ----------------------------------------------------------- pure-Python helpers
@@ -98,13 +108,13 @@ def _brute_topk_set(row, k):
 
 @pytest.mark.parametrize("k", [1, 2, 3, 8])
 @pytest.mark.parametrize("ties", [False, True])
-def test_route_matches_bruteforce_subsets(k, ties):
+def test_route_matches_bruteforce_subsets(k, ties, impl):
     rng = np.random.default_rng(7 + k)
     if ties:
         logits = rng.integers(0, 3, size=(40, 8)).astype(np.float32)
     else:
         logits = gen.gen_moe_int4(gen.config("tiny"))["logits"][:40]
-    ids, w = oracle.route_topk(logits, k)
+    ids, w = impl.route_topk(logits, k)
     for t in range(logits.shape[0]):
         row = [float(v) for v in logits[t]]
         assert set(ids[t].tolist()) == _brute_topk_set(row, k)
@@ -113,48 +123,48 @@ def test_route_matches_bruteforce_subsets(k, ties):
             assert row[a] > row[b] or (row[a] == row[b] and a < b)
 
 
-def test_gates_closed_form():
+def test_gates_closed_form(impl):
     logits = gen.gen_moe_int4(gen.config("olmoe_decode"))["logits"]
-    ids, w = oracle.route_topk(logits, 8)
+    ids, w = impl.route_topk(logits, 8)
     for t in range(logits.shape[0]):
         sel = [float(logits[t][e]) for e in ids[t]]
         assert abs(sum(w[t]) - 1.0) < 1e-14
         for i in range(8):
             for j in range(8):
                 assert abs(w[t][i] / w[t][j] - math.exp(sel[i] - sel[j])) < 1e-12 * math.exp(sel[i] - sel[j])
-    _, w1 = oracle.route_topk(logits, 1)
+    _, w1 = impl.route_topk(logits, 1)
     assert np.all(w1 == 1.0)
 
 
-def test_route_rejects_bad_k_and_nonfinite():
+def test_route_rejects_bad_k_and_nonfinite(impl):
     with pytest.raises(ValueError):
-        oracle.route_topk(np.zeros((2, 4), np.float32), 5)
+        impl.route_topk(np.zeros((2, 4), np.float32), 5)
     with pytest.raises(ValueError):
-        oracle.route_topk(np.array([[0, np.nan]], np.float32), 1)
+        impl.route_topk(np.array([[0, np.nan]], np.float32), 1)
 
 
-def test_golden_route_permute_hand_example():
+def test_golden_route_permute_hand_example(impl):
     """Hand-worked routing + grouping example (derivation in the fixture)."""
     with open(os.path.join(GOLDEN, "route_permute_hand.json")) as f:
         g = json.load(f)
     logits = np.array(g["logits"], dtype=np.float32)
-    ids, w = oracle.route_topk(logits, g["k"])
+    ids, w = impl.route_topk(logits, g["k"])
     assert ids.tolist() == g["ids"]
     np.testing.assert_allclose(w, np.array(g["w"]), rtol=1e-15, atol=0)
-    counts, seg, sp, pp = oracle.permute(ids, g["E"])
+    counts, seg, sp, pp = impl.permute(ids, g["E"])
     assert counts.tolist() == g["counts"]
     assert seg.tolist() == g["seg_offsets"]
     assert sp.tolist() == g["sorted_pair"]
     assert pp.tolist() == g["pair_pos"]
-    counts, seg, sp, pp = oracle.permute(ids, g["E"], np.array(g["mwq_bits"], np.uint8))
+    counts, seg, sp, pp = impl.permute(ids, g["E"], np.array(g["mwq_bits"], np.uint8))
     assert seg.tolist() == g["mwq_seg_offsets"]
     assert sp.tolist() == g["mwq_sorted_pair"]
 
 
 # --------------------------------------------------------------------- grouping
-def _check_permutation(ids, E, bits=None):
+def _check_permutation(ids, E, bits=None, impl=oracle):
     P = ids.size
-    counts, seg, sp, pp = oracle.permute(ids, E, bits)
+    counts, seg, sp, pp = impl.permute(ids, E, bits)
     S = 1 if bits is None else 3
     flat = [int(v) for v in ids.ravel()]
     keys = [flat[p] * S + (0 if bits is None else 4 - int(bits.ravel()[p])) for p in range(P)]
@@ -179,16 +189,16 @@ def _check_permutation(ids, E, bits=None):
     return counts, seg, sp, pp
 
 
-def test_permute_invariants_random_and_edges():
+def test_permute_invariants_random_and_edges(impl):
     rng = np.random.default_rng(3)
-    _check_permutation(rng.integers(0, 8, size=(50, 2)), 8)
-    _check_permutation(np.zeros((17, 1), np.int64), 5)                       # all on one expert, others empty
-    _check_permutation(np.tile(np.arange(6), (9, 1)), 6)                      # k = E
-    _check_permutation(np.zeros((0, 2), np.int64), 4)                         # no tokens
+    _check_permutation(rng.integers(0, 8, size=(50, 2)), 8, impl=impl)
+    _check_permutation(np.zeros((17, 1), np.int64), 5, impl=impl)            # all on one expert, others empty
+    _check_permutation(np.tile(np.arange(6), (9, 1)), 6, impl=impl)           # k = E
+    _check_permutation(np.zeros((0, 2), np.int64), 4, impl=impl)              # no tokens
     bits = rng.integers(2, 5, size=60).astype(np.uint8)
-    _check_permutation(rng.integers(0, 8, size=(30, 2)), 8, bits)            # MWQ sub-keys
+    _check_permutation(rng.integers(0, 8, size=(30, 2)), 8, bits, impl=impl)  # MWQ sub-keys
     with pytest.raises(ValueError):
-        oracle.permute(np.array([[0, 9]]), 8)
+        impl.permute(np.array([[0, 9]]), 8)
 
 
 def test_permute_unpermute_round_trip():
@@ -303,7 +313,7 @@ def test_delta2_special_cases():
     assert np.array_equal(D, D2)
 
 
-def test_delta_linear_reductions():
+def test_delta_linear_reductions(impl):
     """codes all 2 and salient values 0 => y = x W_base^T; zero base with a
     one-hot x on a salient channel returns that salient row, on another
     channel step * (c - 2)."""
@@ -312,7 +322,7 @@ def test_delta_linear_reductions():
     x = oracle.bf16_to_f64(d["x"])
     base = oracle.bf16_to_f64(d["base"])
     d0 = dict(d, codes=np.full_like(d["codes"], 0xAA), salient_val=np.zeros_like(d["salient_val"]))
-    y = oracle.delta_linear(d0, cfg)["out"]
+    y = impl.delta_linear(d0, cfg)["out"]
     ref = [[sum(x[t][kk] * base[n][kk] for kk in range(cfg.K)) for n in range(cfg.N)] for t in range(cfg.T)]
     assert rel_err(y, ref) < 1e-13
     e = int(d["ids"][0])
@@ -320,7 +330,7 @@ def test_delta_linear_reductions():
         xb = np.zeros_like(d["x"])
         xb[0, ch] = 0x3F80  # 1.0
         d1 = dict(d, x=xb, base=np.zeros_like(d["base"]))
-        y = oracle.delta_linear(d1, cfg, tokens=[0])["out"][0]
+        y = impl.delta_linear(d1, cfg, tokens=[0])["out"][0]
         if ch in d["salient_idx"][e]:
             s = list(d["salient_idx"][e]).index(ch)
             expect = [bf16_val(int(v)) for v in d["salient_val"][e][s]]
@@ -330,7 +340,7 @@ def test_delta_linear_reductions():
         assert y.tolist() == expect
 
 
-def test_delta_linear_matches_dense_bruteforce_several_experts():
+def test_delta_linear_matches_dense_bruteforce_several_experts(impl):
     """y[t] = x[t] (W_base + D_{e(t)})^T evaluated densely in pure Python, per
     token with its own expert (ME-Switch: expert weight = shared base + its
     delta), against the grouped oracle: three experts, tokens on each, base
@@ -338,7 +348,7 @@ def test_delta_linear_matches_dense_bruteforce_several_experts():
     cfg = gen.config("meswitch_delta", requests=6, tokens_per_request=2, K=32, N=8, E=3, n_salient=2, seed=13)
     d = gen.gen_delta_linear(cfg)
     d["ids"] = np.array([0, 2, 1, 1, 2, 0, 0, 1, 2, 2, 1, 0], np.int32)
-    res = oracle.delta_linear(d, cfg)
+    res = impl.delta_linear(d, cfg)
     x = [[bf16_val(int(v)) for v in row] for row in d["x"]]
     base = [[bf16_val(int(v)) for v in row] for row in d["base"]]
 
@@ -378,12 +388,12 @@ def _py_dequant_int4(packed_row_bytes, scale_bits, G):
     return [f16_val(int(scale_bits[kk // G])) * (codes[kk] - 8) for kk in range(len(codes))]
 
 
-def test_moe_forward_matches_dense_bruteforce_int4():
+def test_moe_forward_matches_dense_bruteforce_int4(impl):
     """Per token: sum_j w_j * FFN_{e_j}(x_t), evaluated densely in pure Python
     (no grouping), equals the grouped oracle path."""
     cfg = gen.config("tiny", T=6, H=8, I=4, E=3, k=2, G=4)
     d = gen.gen_moe_int4(cfg)
-    res = oracle.moe_forward(d, cfg)
+    res = impl.moe_forward(d, cfg)
     x = [[bf16_val(int(v)) for v in row] for row in d["x"]]
     for t in range(cfg.T):
         row = [float(v) for v in d["logits"][t]]
@@ -403,14 +413,14 @@ def test_moe_forward_matches_dense_bruteforce_int4():
         assert rel_err(res["out_h16"][t], acc) > 1e-6   # the bf16 rounding of h is visible
 
 
-def test_moe_forward_k1_identical_experts_is_dense_ffn():
+def test_moe_forward_k1_identical_experts_is_dense_ffn(impl):
     """k = 1 with every expert identical and gate 1: the layer is one plain
     dense SwiGLU FFN on every token."""
     cfg = gen.config("tiny", T=5, H=8, I=4, E=4, k=1, G=4)
     d = gen.gen_moe_int4(cfg)
     for key in ("gu_codes", "gu_scales", "dn_codes", "dn_scales"):
         d[key] = np.repeat(d[key][:1], cfg.E, axis=0)
-    res = oracle.moe_forward(d, cfg)
+    res = impl.moe_forward(d, cfg)
     wgu = [_py_dequant_int4(d["gu_codes"][0][n], d["gu_scales"][0][n], cfg.G) for n in range(2 * cfg.I)]
     wd = [_py_dequant_int4(d["dn_codes"][0][m], d["dn_scales"][0][m], cfg.G) for m in range(cfg.H)]
     for t in range(cfg.T):
@@ -419,10 +429,10 @@ def test_moe_forward_k1_identical_experts_is_dense_ffn():
         assert rel_err(res["out_h16"][t], py_ffn(xt, wgu, wd, cfg.I, h16=True)) < 1e-12
 
 
-def test_moe_forward_matches_dense_bruteforce_mwq():
+def test_moe_forward_matches_dense_bruteforce_mwq(impl):
     cfg = gen.config("mixtral_mwq", T=6, H=16, I=8, E=3, k=2, G=8)
     d = gen.gen_moe_mwq(cfg)
-    res = oracle.moe_forward(d, cfg)
+    res = impl.moe_forward(d, cfg)
     for t in range(cfg.T):
         xt = [bf16_val(int(v)) for v in d["x"][t]]
         row = [float(v) for v in d["logits"][t]]
@@ -452,11 +462,11 @@ def test_moe_forward_matches_dense_bruteforce_mwq():
         assert rel_err(res["out_h16"][t], acc16) < 1e-12
 
 
-def test_moe_forward_token_subset_matches_full():
+def test_moe_forward_token_subset_matches_full(impl):
     cfg = gen.config("tiny")
     d = gen.gen_moe_int4(cfg)
-    full = oracle.moe_forward(d, cfg)
-    sub = oracle.moe_forward(d, cfg, tokens=[0, 5, 63])
+    full = impl.moe_forward(d, cfg)
+    sub = impl.moe_forward(d, cfg, tokens=[0, 5, 63])
     assert rel_err(sub["out"][[0, 5, 63]], full["out"][[0, 5, 63]]) < 1e-14
     assert np.isnan(sub["out"][1]).all()
 
@@ -547,12 +557,12 @@ def test_mixed_expert_widths_recipe():
     assert d["dn_codes"].size == oracle.expert_stream_offsets(bits, cfg.H, cfg.I)[-1]
 
 
-def test_moe_forward_matches_dense_bruteforce_mixed():
+def test_moe_forward_matches_dense_bruteforce_mixed(impl):
     """Per-expert widths: the grouped oracle equals a pure-Python dense evaluation
     that decodes each expert's bit stream itself."""
     cfg = gen.config("olmoe_mixed_decode", T=5, H=16, I=8, E=4, k=2, G=8, zipf=None)
     d = gen.generate(cfg)
-    res = oracle.moe_forward(d, cfg)
+    res = impl.moe_forward(d, cfg)
 
     def mat(prefix, e, n_rows, kdim):
         b, z = int(d["expert_bits"][e]), int(d["expert_zero"][e])
