@@ -302,6 +302,27 @@ moe_status moe_grouped_qgemm(const moe_wdesc* w, const uint16_t* A, int32_t A_ro
                              int32_t kernel, void* out, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation as moe_grouped_qgemm, with the same arguments except the
+ * workspace.  The kernels' scratch (activation row sums, split-K partial
+ * sums) lives in a static device array of moe_grouped_qgemm_noalloc_scratch_bytes()
+ * bytes (8 MiB) that each GPU the library runs on holds until the process
+ * ends; a call needing more (moe_grouped_qgemm_workspace_size() above that)
+ * returns MOE_ERR_UNSUPPORTED and launches nothing.  Nothing is allocated,
+ * freed or copied by the call.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on the device (other streams, or concurrent host
+ * threads issuing to different streams) race on it and must be ordered by the
+ * caller.  Nothing in the array needs to start at zero, and each call
+ * rewrites what it reads.  Results are bit for bit those of moe_grouped_qgemm
+ * with the same kernel choice.
+ */
+size_t moe_grouped_qgemm_noalloc_scratch_bytes(void);
+moe_status moe_grouped_qgemm_noalloc(const moe_wdesc* w, const uint16_t* A, int32_t A_rows,
+                                     const int32_t* gather_pair, int32_t k,
+                                     const int32_t* seg_offsets, int32_t M_total, int32_t epilogue,
+                                     int32_t kernel, void* out, void* stream);
+
 /* ----------------------------------------------------------------- combine
  * out[t] = sum_{j<k} w[t][j] * y_perm[pair_pos[t*k + j]], accumulated in fp32
  * in slot order j = 0..k-1 and rounded once to bf16 (gate-weighted combine of

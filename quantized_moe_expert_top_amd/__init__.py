@@ -30,6 +30,7 @@ EXPORTED = [
     "moe_status_string", "moe_last_error_detail", "moe_abi_version", "moe_route_topk",
     "moe_permute_workspace_size", "moe_permute", "moe_route_permute", "moe_weight_field_bytes", "moe_repack_weights",
     "moe_grouped_qgemm_workspace_size", "moe_grouped_qgemm", "moe_unpermute_combine",
+    "moe_grouped_qgemm_noalloc", "moe_grouped_qgemm_noalloc_scratch_bytes",
 ]
 
 
@@ -71,6 +72,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_grouped_qgemm_workspace_size": (sz, [ctypes.POINTER(WDesc), i32, i32, i32]),
         "moe_grouped_qgemm": (i32, [ctypes.POINTER(WDesc), vp, i32, vp, i32, vp, i32, i32, i32, vp, vp, sz, vp]),
         "moe_unpermute_combine": (i32, [vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]),
+        "moe_grouped_qgemm_noalloc": (i32, [ctypes.POINTER(WDesc), vp, i32, vp, i32, vp, i32, i32, i32, vp, vp]),
+        "moe_grouped_qgemm_noalloc_scratch_bytes": (sz, []),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -268,6 +271,23 @@ def moe_grouped_qgemm(w: QuantizedExperts, A: torch.Tensor, seg_offsets: torch.T
                                    M_total, epilogue, kernel, _ptr(out), _ptr(workspace), ws_bytes,
                                    _stream(stream)),
            "moe_grouped_qgemm")
+    return out
+
+
+def moe_grouped_qgemm_noalloc(w: QuantizedExperts, A: torch.Tensor, seg_offsets: torch.Tensor, M_total: int,
+                              epilogue: int = MOE_EPI_NONE, gather_pair: torch.Tensor = None, k: int = 1,
+                              out: torch.Tensor = None, stream=None, kernel: int = MOE_KERNEL_AUTO) -> torch.Tensor:
+    """moe_grouped_qgemm without a workspace: the library's static device scratch
+    (moe_grouped_qgemm_noalloc_scratch_bytes()) serves instead.  Pass `out` to
+    allocate nothing at all."""
+    _bf16(A)
+    n_out = w.N // 2 if epilogue == MOE_EPI_SWIGLU else w.N
+    if out is None:
+        dt = torch.float32 if epilogue == MOE_EPI_NONE_F32 else torch.bfloat16
+        out = torch.empty((M_total, n_out), dtype=dt, device=A.device)
+    _check(lib().moe_grouped_qgemm_noalloc(ctypes.byref(w.desc), _ptr(A), A.shape[0], _ptr(gather_pair), k,
+                                           _ptr(seg_offsets), M_total, epilogue, kernel, _ptr(out),
+                                           _stream(stream)), "moe_grouped_qgemm_noalloc")
     return out
 
 

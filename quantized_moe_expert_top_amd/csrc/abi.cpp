@@ -291,9 +291,15 @@ size_t moe_grouped_qgemm_workspace_size(const moe_wdesc* w, int32_t A_rows, int3
   return moe::qgemm_workspace_bytes(to_q(w), A_rows, M_total, kernel);
 }
 
-moe_status moe_grouped_qgemm(const moe_wdesc* w, const uint16_t* A, int32_t A_rows, const int32_t* gather_pair,
-                             int32_t k, const int32_t* seg_offsets, int32_t M_total, int32_t epilogue,
-                             int32_t kernel, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// Everything moe_grouped_qgemm checks before its workspace.  Sets *empty for
+// a problem with no rows (a success with nothing to launch).
+moe_status check_qgemm(const moe_wdesc* w, const uint16_t* A, int32_t A_rows, const int32_t* gather_pair, int32_t k,
+                       const int32_t* seg_offsets, int32_t M_total, int32_t epilogue, int32_t kernel, void* out,
+                       bool* empty) {
+  *empty = false;
   moe_status st = check_desc(w, MOE_LAYOUT_TILED, true);
   if (st != MOE_OK) return st;
   if (M_total < 0 || A_rows < 0) return fail(MOE_ERR_BAD_SHAPE, "M_total=%d A_rows=%d", M_total, A_rows);
@@ -311,23 +317,65 @@ moe_status moe_grouped_qgemm(const moe_wdesc* w, const uint16_t* A, int32_t A_ro
   } else if (A_rows < M_total) {
     return fail(MOE_ERR_BAD_SHAPE, "A_rows=%d < M_total=%d", A_rows, M_total);
   }
-  if (M_total == 0) return ok();
+  if (M_total == 0) {
+    *empty = true;
+    return ok();
+  }
   if (!A || !seg_offsets || !out) return fail(MOE_ERR_NULL_ARG, "A, seg_offsets and out are required");
   if (!aligned(A, 16) || !aligned(out, 16)) return fail(MOE_ERR_MISALIGNED, "A and out must be 16-byte aligned");
-  const moe::QWeights q = to_q(w);
-  const size_t need = moe::qgemm_workspace_bytes(q, A_rows, M_total, kernel);
+  if ((int64_t)A_rows * w->K * 2 >= ((int64_t)1 << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "activation matrix of %lld bytes (4 GiB or more)", (long long)A_rows * w->K * 2);
+  return MOE_OK;
+}
+
+moe_status run_qgemm(const moe_wdesc* w, const uint16_t* A, int32_t A_rows, const int32_t* gather_pair, int32_t k,
+                     const int32_t* seg_offsets, int32_t M_total, int32_t epilogue, int32_t kernel, void* out,
+                     void* workspace, void* stream) {
+  moe::QGemmArgs a{to_q(w), A, A_rows, gather_pair, k, seg_offsets, w->E * (w->format == MOE_W_MWQ_2_3_4 ? 3 : 1),
+                   M_total, epilogue, kernel, out, workspace};
+  return hip_status(moe::launch_qgemm(a, stream), "grouped_qgemm launch");
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_grouped_qgemm(const moe_wdesc* w, const uint16_t* A, int32_t A_rows, const int32_t* gather_pair,
+                             int32_t k, const int32_t* seg_offsets, int32_t M_total, int32_t epilogue,
+                             int32_t kernel, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  moe_status st = check_qgemm(w, A, A_rows, gather_pair, k, seg_offsets, M_total, epilogue, kernel, out, &empty);
+  if (st != MOE_OK || empty) return st;
+  const size_t need = moe::qgemm_workspace_bytes(to_q(w), A_rows, M_total, kernel);
   if (workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, %zu needed", workspace_bytes, need);
   if (need && !workspace) return fail(MOE_ERR_NULL_ARG, "workspace is NULL");
   if (need && !aligned(workspace, 16)) return fail(MOE_ERR_MISALIGNED, "workspace must be 16-byte aligned");
-  if ((int64_t)A_rows * w->K * 2 >= ((int64_t)1 << 32))
-    return fail(MOE_ERR_UNSUPPORTED, "activation matrix of %lld bytes (4 GiB or more)", (long long)A_rows * w->K * 2);
   st = check_device();
   if (st != MOE_OK) return st;
-  moe::QGemmArgs a{q, A, A_rows, gather_pair, k, seg_offsets, w->E * (w->format == MOE_W_MWQ_2_3_4 ? 3 : 1), M_total,
-                   epilogue, kernel, out, workspace};
-  return hip_status(moe::launch_qgemm(a, stream), "grouped_qgemm launch");
+  return run_qgemm(w, A, A_rows, gather_pair, k, seg_offsets, M_total, epilogue, kernel, out, workspace, stream);
 }
+
+moe_status moe_grouped_qgemm_noalloc(const moe_wdesc* w, const uint16_t* A, int32_t A_rows,
+                                     const int32_t* gather_pair, int32_t k, const int32_t* seg_offsets,
+                                     int32_t M_total, int32_t epilogue, int32_t kernel, void* out, void* stream) {
+  bool empty = false;
+  moe_status st = check_qgemm(w, A, A_rows, gather_pair, k, seg_offsets, M_total, epilogue, kernel, out, &empty);
+  if (st != MOE_OK || empty) return st;
+  const size_t need = moe::qgemm_workspace_bytes(to_q(w), A_rows, M_total, kernel);
+  if (need > moe::kStaticScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED, "this call needs %zu bytes of scratch; the static scratch holds %zu "
+                "(use moe_grouped_qgemm with a workspace)", need, moe::kStaticScratchBytes);
+  st = check_device();
+  if (st != MOE_OK) return st;
+  void* scratch = nullptr;
+  if (need) {
+    const int e = moe::qgemm_static_scratch(&scratch);
+    if (e != 0) return fail(MOE_ERR_HIP, "static scratch address: %s", moe::rt_error_string(e));
+  }
+  return run_qgemm(w, A, A_rows, gather_pair, k, seg_offsets, M_total, epilogue, kernel, out, scratch, stream);
+}
+
+size_t moe_grouped_qgemm_noalloc_scratch_bytes(void) { return moe::kStaticScratchBytes; }
 
 moe_status moe_unpermute_combine(const void* y_perm, int32_t y_dtype, const int32_t* pair_pos,
                                  const int32_t* n_valid, const float* topk_w, int32_t T, int32_t k, int32_t H,

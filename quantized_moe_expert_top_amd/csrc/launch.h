@@ -87,6 +87,10 @@ bool qgemm_kernel_supported(int fmt, int kernel);
 // Workspace bytes for either epilogue (the larger need) with that kernel choice.
 size_t qgemm_workspace_bytes(const QWeights& w, int A_rows, int M_total, int kernel);
 int launch_qgemm(const QGemmArgs& a, void* stream);
+// The no-allocation grouped GEMM's device scratch: its size, and its address
+// on the current device (looked up once per device).
+constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+int qgemm_static_scratch(void** ptr);
 // Planning (plan.cpp).  path: 0 = 16-row tiles (DELTA2: 32-row tiles), 1 = 16-row
 // tiles of one width (MWQ), 64 / 65 = 64-row tiles with 8 / 4 wavefront
 // columns, 128 = 128-row register-fed tiles, 2 = 128-row LDS-DMA (INT4, MWQ),

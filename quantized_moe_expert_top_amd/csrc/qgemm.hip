@@ -33,6 +33,7 @@
 //                                repack); salient channels are one more MFMA
 //                                K chunk with bf16 values; the shared base is a
 //                                plain bf16 MFMA on the same A operand
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -1753,6 +1754,34 @@ int launch_qgemm(const QGemmArgs& a, void* stream) {
   else if (a.epilogue == 2) launch_epi<2>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, t, s);
   else launch_epi<0>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, t, s);
   return (int)hipGetLastError();
+}
+
+// ------------------------------------------------ static scratch (no allocation)
+// Device scratch of the no-allocation grouped GEMM: the same workspace the
+// kernels take from the caller elsewhere (activation row sums, split-K
+// partial sums), held in a device array that each GPU keeps until the process
+// ends.  In host code `scratch` is only a stand-in for the symbol: its device
+// address, one per GPU, comes from hipGetSymbolAddress with that GPU current
+// and is what the kernels receive.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+int qgemm_static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return 0;
 }
 
 }  // namespace moe

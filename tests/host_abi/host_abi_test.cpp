@@ -90,6 +90,20 @@ int main() {
   CHECK(strstr(moe_last_error_detail(), "grouped_qgemm") != nullptr);
   stub::launch_error = 0;
 
+  // the no-allocation variant: the static scratch stands in for the workspace;
+  // a call needing more than it holds is refused before anything is launched
+  CHECK(moe_grouped_qgemm_noalloc_scratch_bytes() == ((size_t)8 << 20));
+  CHECK(moe_grouped_qgemm_noalloc(&d, static_cast<const uint16_t*>(fake(0x1000)), 4096,
+                                  static_cast<const int32_t*>(fake(0x2000)), 2, static_cast<const int32_t*>(fake(0x3000)),
+                                  8192, MOE_EPI_SWIGLU, MOE_KERNEL_AUTO, fake(0x4000), nullptr) == MOE_OK);
+  CHECK(stub::last_ws == fake(0x7000000));
+  const int launches3 = stub::launches;
+  CHECK(moe_grouped_qgemm_noalloc(&d, static_cast<const uint16_t*>(fake(0x1000)), 1 << 20,
+                                  static_cast<const int32_t*>(fake(0x2000)), 2, static_cast<const int32_t*>(fake(0x3000)),
+                                  1 << 21, MOE_EPI_SWIGLU, MOE_KERNEL_AUTO, fake(0x4000), nullptr) == MOE_ERR_UNSUPPORTED);
+  CHECK(strstr(moe_last_error_detail(), "static scratch") != nullptr);
+  CHECK(stub::launches == launches3);
+
   // per-expert width tables are read (under the sanitizers) and checked
   int32_t bits[4] = {4, 2, 3, 2}, zero[4] = {8, 1, 3, 2};
   moe_wdesc m = int4_desc();

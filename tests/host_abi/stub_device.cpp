@@ -13,6 +13,7 @@ int device_error = 0;
 int launches = 0;
 int taken = 0;
 const char* arch = "gfx950:sramecc+:xnack-";
+void* last_ws = nullptr;
 }  // namespace stub
 
 namespace {
@@ -49,6 +50,13 @@ int launch_route_permute(const float*, int, int, int, const uint8_t*, int32_t*, 
 int launch_combine(const void*, bool, const int32_t*, const int32_t*, const float*, int, int, int, uint16_t*, void*) {
   return launched();
 }
-int launch_qgemm(const QGemmArgs&, void*) { return launched(); }
+int launch_qgemm(const QGemmArgs& a, void*) {
+  stub::last_ws = a.ws;
+  return launched();
+}
+int qgemm_static_scratch(void** ptr) {
+  *ptr = reinterpret_cast<void*>(0x7000000);
+  return 0;
+}
 int launch_repack(const QWeights&, const QWeights&, void*) { return launched(); }
 }  // namespace moe

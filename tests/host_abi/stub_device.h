@@ -7,4 +7,5 @@ extern int device_error;   // returned by the current-device query
 extern int launches;       // launchers called so far
 extern int taken;          // pending-error queries so far
 extern const char* arch;   // architecture name the device reports
+extern void* last_ws;      // workspace the last grouped-GEMM launch received
 }  // namespace stub
