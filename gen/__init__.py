@@ -24,6 +24,9 @@ five summarised systems; no page fixes a seed, so the seeds are ours):
                   often routed to (Zipf rank) keep 4 bits, the next 3, the rest 2,
                   in the proportions 0.25 / 0.35 / 0.40; codes packed at their
                   own width, zero point per expert, group scales U(lo,hi) x 2^(4-b)
+  olmoe_edge_decode  the same with the INT2 / INT4 / INT8 widths EdgeMoE names:
+                  8 bits for the most routed-to quarter, 4 for the next 0.35, 2
+                  for the rest
   meswitch_delta  256 requests x 16 tok, linear 4096 -> 14336, 16 experts,
                   shared bf16 base N(0,0.02), 2-bit delta codes with per-output
                   channel fp16 step U(0.0005,0.002), 41 salient input channels
@@ -69,7 +72,8 @@ class MoeConfig:
     scale_hi: float
     zipf: Optional[float]  # popularity exponent added to the logits, or None
     seed: int
-    bit_probs: tuple = ()  # mwq: probabilities of bit-widths (2, 3, 4); mixed: shares of experts at 2, 3, 4 bits
+    bit_probs: tuple = ()  # mwq: probabilities of bit-widths (2, 3, 4); mixed: shares of experts at each width
+    widths: tuple = (2, 3, 4)  # mixed: the widths bit_probs refers to, ascending
 
     @property
     def pairs(self) -> int:
@@ -111,6 +115,8 @@ CONFIGS = {
                                     406, bit_probs=(0.40, 0.35, 0.25)),
     "olmoe_mixed_decode": MoeConfig("olmoe_mixed_decode", 32, 2048, 1024, 64, 8, 128, "mixed", 0.002, 0.01, 1.1,
                                     707, bit_probs=(0.40, 0.35, 0.25)),
+    "olmoe_edge_decode": MoeConfig("olmoe_edge_decode", 32, 2048, 1024, 64, 8, 128, "mixed", 0.002, 0.01, 1.1,
+                                   708, bit_probs=(0.40, 0.35, 0.25), widths=(2, 4, 8)),
     "meswitch_delta": DeltaConfig("meswitch_delta", 256, 16, 4096, 14336, 16, 41, 0.02, 0.002,
                                   0.0005, 0.002, 1.0, 505),
 }
@@ -218,20 +224,24 @@ def gen_moe_mwq(cfg: MoeConfig) -> dict:
 
 
 def expert_widths(cfg: MoeConfig) -> np.ndarray:
-    """Static bit-width per expert (int32 [E], values 2, 3, 4).
+    """Static bit-width per expert (int32 [E], values from cfg.widths).
 
     With a popularity bias the experts are ranked by it (expert 0 is the most
-    popular): the top share bit_probs[2] keeps 4 bits, the next bit_probs[1]
-    3 bits, the rest 2.  Without one the widths are a seeded permutation of
-    the same counts.
+    popular): the top share bit_probs[-1] keeps the widest width, the next
+    bit_probs[-2] the next, and so on down to the narrowest for the rest.
+    Without one the widths are a seeded permutation of the same counts.
     """
     E = cfg.E
     p = np.asarray(cfg.bit_probs, dtype=np.float64)
     p = p / p.sum()
-    n4 = int(round(p[2] * E))
-    n3 = int(round(p[1] * E))
-    n3 = min(n3, E - n4)
-    ranked = np.array([4] * n4 + [3] * n3 + [2] * (E - n4 - n3), dtype=np.int32)
+    w = list(cfg.widths)
+    counts, left = [], E
+    for i in range(len(w) - 1, 0, -1):   # widest first
+        n = min(int(round(p[i] * E)), left)
+        counts.append((w[i], n))
+        left -= n
+    counts.append((w[0], left))
+    ranked = np.array([b for b, n in counts for _ in range(n)], dtype=np.int32)
     if cfg.zipf is None:
         ranked = ranked[rng_for(cfg.seed, "expert_bits").permutation(E)]
     return ranked
@@ -243,7 +253,8 @@ def _bitstream(rng, E, N, K, bits) -> np.ndarray:
 
 
 def gen_moe_mixed(cfg: MoeConfig) -> dict:
-    """MoE layer with a static bit-width b_e in {2, 3, 4} per expert, canonical layout.
+    """MoE layer with a static bit-width b_e per expert (cfg.widths: {2, 3, 4}
+    or the INT2 / INT4 / INT8 mix {2, 4, 8}), canonical layout.
 
     expert_bits int32 [E]; expert_zero int32 [E], z_e in {2^(b_e-1) - 1, 2^(b_e-1)}
     gu_codes uint8 flat: expert e's [2I][H] codes of b_e bits, each row a

@@ -155,15 +155,15 @@ moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t 
  *                    scales fp16 [E][N][K/G].
  * MOE_W_INT_PER_EXPERT  static bit-width per expert (EdgeMoE page, expert-wise
  *                    bit-width adaptation): expert e stores b_e-bit codes,
- *                    b_e in {2, 3, 4}, with its own zero point z_e in
+ *                    b_e in {2, 3, 4, 8}, with its own zero point z_e in
  *                    [0, 2^b_e - 1]: w = s[n][k/G] * (c - z_e).  expert_bits
  *                    and expert_zero (host int32 [E], read on every call)
  *                    give b_e and z_e; zero_point is ignored; E <= 256.
  *                    codes u8, experts back to back, expert e's [N][K] codes
  *                    as one little-endian bit stream per row (code k at bits
  *                    k*b_e .. k*b_e + b_e - 1): N*K*b_e/8 bytes per expert;
- *                    scales fp16 [E][N][K/G].  No 8-bit width: 8-bit codes do
- *                    not fit the exact 16-bit dequantisation of the kernels.
+ *                    scales fp16 [E][N][K/G].  Other widths (1, 5, 6, 7, ...)
+ *                    are MOE_ERR_UNSUPPORTED.
  * MOE_W_DELTA2_SALIENT  ME-Switch delta: d[n][k] = salient value if k is a
  *                    salient input channel of expert e, else
  *                    step[n] * (c - z) with c in [0,3] (z = 2 normally).
@@ -203,8 +203,11 @@ moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t 
 #define MOE_KERNEL_TILE64_WIDE 3     /* INT4, MWQ: 64-row tiles, 128 SwiGLU / 256 plain channels */
 #define MOE_KERNEL_TILE64 4          /* INT4, MWQ: 64-row tiles, 64 SwiGLU / 128 plain channels */
 #define MOE_KERNEL_TILE128 5         /* INT4, MWQ: 128-row tiles fed through registers */
-#define MOE_KERNEL_LDS_DMA 6         /* INT4, MWQ, DELTA2 with a base and a plain epilogue: 128-row
-                                        tiles fed by LDS-DMA (activation row sums in the workspace) */
+#define MOE_KERNEL_LDS_DMA 6         /* INT4, MWQ, DELTA2 with a base and a plain epilogue: 64- or
+                                        128-row tiles fed by LDS-DMA (activation row sums in the
+                                        workspace); nested MWQ: 16-row chunks of all widths */
+#define MOE_KERNEL_LDS_DMA_PER_WIDTH 7 /* nested MWQ only: the LDS-DMA kernel on row tiles of one
+                                          width each, loading only that width's planes */
 
 #define MOE_EPI_NONE 0      /* out bf16 [M_total][N] */
 #define MOE_EPI_SWIGLU 1    /* N = 2*I; rows [0,I) gate, [I,2I) up; out = bf16(silu(gate) * up), width I */
@@ -229,7 +232,7 @@ typedef struct moe_wdesc {
   const int32_t* salient_idx;  /* DELTA2 [E][n_salient] */
   const uint16_t* salient_val; /* DELTA2 bf16 */
   const uint16_t* base;        /* DELTA2 shared bf16 base [N][K], or NULL */
-  const int32_t* expert_bits;  /* INT_PER_EXPERT: host int32 [E], each 2, 3 or 4; else NULL */
+  const int32_t* expert_bits;  /* INT_PER_EXPERT: host int32 [E], each 2, 3, 4 or 8; else NULL */
   const int32_t* expert_zero;  /* INT_PER_EXPERT: host int32 [E], zero point of each expert; else NULL */
 } moe_wdesc;
 

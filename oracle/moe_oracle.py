@@ -37,7 +37,8 @@ specification, not by code):
 * DELTA2: d = salient_val if k is salient else step[n] * (c - 2), c in [0, 3],
   packed like q2.
 * Static bit-width per expert (EdgeMoE, expert-wise bit-width adaptation):
-  expert e stores b_e-bit codes, b_e in {2, 3, 4}, with its own zero point:
+  expert e stores b_e-bit codes, b_e in {2, 3, 4, 8} (the page names INT2,
+  INT4 and INT8 experts), with its own zero point:
   w = scale[n][k // G] * (c - z_e).  Each row of an expert is a little-endian
   bit stream (code k in bits k*b .. k*b + b - 1); experts are back to back.
 * SwiGLU expert: h = silu(x Wg^T) * (x Wu^T), y = h Wd^T, with gate rows
@@ -149,8 +150,8 @@ def unpack_bits(stream, n_codes: int, b: int) -> np.ndarray:
 def dequant_per_expert(stream, scales, N: int, K: int, G: int, b: int, zero_point: int) -> np.ndarray:
     """Expert matrix [N][K] stored at its own bit-width b (EdgeMoE expert-wise
     bit-width adaptation), exact in float64: w = scale[n][k // G] * (c - z)."""
-    if b not in (2, 3, 4):
-        raise ValueError("bit-width must be 2, 3 or 4")
+    if b not in (2, 3, 4, 8):
+        raise ValueError("bit-width must be 2, 3, 4 or 8")
     c = unpack_bits(stream, N * K, b).reshape(N, K)
     s = f16_to_f64(scales)
     assert s.shape == (N, K // G)

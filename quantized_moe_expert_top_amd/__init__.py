@@ -22,7 +22,7 @@ MOE_LAYOUT_CANONICAL, MOE_LAYOUT_TILED = 0, 1
 MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_NONE_F32 = 0, 1, 2
 MOE_DTYPE_BF16, MOE_DTYPE_F32 = 0, 1
 (MOE_KERNEL_AUTO, MOE_KERNEL_SMALL, MOE_KERNEL_SMALL_PER_WIDTH, MOE_KERNEL_TILE64_WIDE, MOE_KERNEL_TILE64,
- MOE_KERNEL_TILE128, MOE_KERNEL_LDS_DMA) = range(7)
+ MOE_KERNEL_TILE128, MOE_KERNEL_LDS_DMA, MOE_KERNEL_LDS_DMA_PER_WIDTH) = range(8)
 (MOE_FIELD_CODES, MOE_FIELD_PLANE3, MOE_FIELD_PLANE4, MOE_FIELD_SCALES,
  MOE_FIELD_SALIENT_IDX, MOE_FIELD_SALIENT_VAL, MOE_FIELD_BASE) = range(7)
 

@@ -68,7 +68,8 @@ moe_status check_desc(const moe_wdesc* w, int layout, bool need_buffers) {
     if (!w->expert_bits || !w->expert_zero) return fail(MOE_ERR_NULL_ARG, "expert_bits / expert_zero is NULL");
     for (int e = 0; e < w->E; ++e) {
       const int b = w->expert_bits[e], z = w->expert_zero[e];
-      if (b < 2 || b > 4) return fail(MOE_ERR_UNSUPPORTED, "expert %d: %d bits (2, 3 or 4 supported)", e, b);
+      if (!(b == 2 || b == 3 || b == 4 || b == 8))
+        return fail(MOE_ERR_UNSUPPORTED, "expert %d: %d bits (2, 3, 4 or 8 supported)", e, b);
       if (z < 0 || z >= (1 << b)) return fail(MOE_ERR_BAD_SHAPE, "expert %d: zero point %d for %d bits", e, z, b);
     }
   }
@@ -305,7 +306,7 @@ moe_status check_qgemm(const moe_wdesc* w, const uint16_t* A, int32_t A_rows, co
   if (M_total < 0 || A_rows < 0) return fail(MOE_ERR_BAD_SHAPE, "M_total=%d A_rows=%d", M_total, A_rows);
   if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SWIGLU && epilogue != MOE_EPI_NONE_F32)
     return fail(MOE_ERR_BAD_FORMAT, "unknown epilogue %d", epilogue);
-  if (kernel < MOE_KERNEL_AUTO || kernel > MOE_KERNEL_LDS_DMA)
+  if (kernel < MOE_KERNEL_AUTO || kernel > MOE_KERNEL_LDS_DMA_PER_WIDTH)
     return fail(MOE_ERR_BAD_FORMAT, "unknown kernel choice %d", kernel);
   if (!moe::qgemm_kernel_supported(w->format, kernel))
     return fail(MOE_ERR_UNSUPPORTED, "kernel choice %d does not run weight format %d", kernel, w->format);

@@ -54,20 +54,22 @@ int decode_row_tiles(int fmt, int path, int M_total, int E) {
 // 1 = 16-row tiles of one width each (nested MWQ), 64 / 65 = 64-row tiles with
 // 8 / 4 wavefront columns, 128 = 128-row register-fed tiles, 2 = the 128-row
 // LDS-DMA kernel (INT4, nested MWQ; row sums in the workspace), 3 = the
-// 128-row LDS-DMA delta kernel (with a shared base, plain epilogues).
+// 128-row LDS-DMA delta kernel (with a shared base, plain epilogues), 5 = the
+// LDS-DMA kernel on row tiles of one width each (nested MWQ).
 //
 // MOE_KERNEL_AUTO chooses from the mean rows per segment (the host never sees
 // the device counts): few rows -> 16-row tiles (decode kernel); many -> the
 // 128-row LDS-DMA kernel for INT4, 64-row tiles otherwise (and for INT4
 // segments of under ~96 rows, where 128-row tiles would be mostly padding),
 // with 8 wavefront columns (activations re-read half as often) when the
-// activations outweigh the weights, else 4.  Nested MWQ -> the 128-row kernel
-// over 16-row chunks of every width from about 256 rows per expert for SwiGLU
-// and 512 for the plain epilogues (measured on the Mixtral-shaped layer: with
-// fewer rows, 64-row tiles of one width are as fast or faster, the 128-row
-// kernel leaving many chunks of its last workgroup per expert empty); few rows
-// -> 16-row tiles that take all widths of an expert together (one read of each
-// bit plane).  Any other MOE_KERNEL_* value is taken as given.
+// activations outweigh the weights, else 4.  Nested MWQ -> from about 24 rows
+// per width sub-segment the LDS-DMA kernel on row tiles of one width each
+// (measured on the Mixtral-shaped layer at 512 tokens, ~43 rows per
+// sub-segment: 447 us for gate/up against 595 us for 16-row chunks of all
+// widths per workgroup, whose per-row-tile width masks cost 4 VALU operations
+// per MFMA); fewer rows -> 16-row tiles that take all widths of an expert
+// together (one read of each bit plane).  Any other MOE_KERNEL_* value is
+// taken as given.
 int pick_path(const QWeights& w, int M_total, int nseg, int epi, int kernel) {
   const int fmt = w.fmt;
   switch (kernel) {
@@ -77,13 +79,14 @@ int pick_path(const QWeights& w, int M_total, int nseg, int epi, int kernel) {
     case 4: return 65;
     case 5: return 128;
     case 6: return fmt == 3 ? 3 : 2;
+    case 7: return 5;
     default: break;
   }
   if (fmt == 4) return 0;  // a width per expert: 16-row tiles at every batch size
   const double avg = (double)M_total / (double)(nseg > 0 ? nseg : 1);
   if (fmt == 3) return (avg >= 96.0 && w.base && epi != 1) ? 3 : 0;
-  if (fmt == 2 && 3.0 * avg >= (epi == 1 ? 256.0 : 512.0)) return 2;
   if (avg < 24.0) return 0;
+  if (fmt == 2) return 5;
   if (fmt == 1 && avg >= 96.0) return 2;
   const int E = fmt == 2 ? nseg / 3 : nseg;
   const double a_bytes = (double)M_total * w.K * 2.0;
@@ -97,13 +100,14 @@ bool qgemm_kernel_supported(int fmt, int kernel) {
     case 2: return fmt == 2;
     case 3: case 4: case 5: return fmt == 1 || fmt == 2;
     case 6: return fmt == 1 || fmt == 2 || fmt == 3;
+    case 7: return fmt == 2;
     default: return false;
   }
 }
 
 namespace {
 size_t ws_need(const QWeights& w, int path, int epi, int A_rows, int M_total) {
-  if (path == 2) return ((size_t)A_rows * (w.K / w.G) * 4 + 255) & ~(size_t)255;  // row sums per group
+  if (path == 2 || path == 5) return ((size_t)A_rows * (w.K / w.G) * 4 + 255) & ~(size_t)255;  // row sums per group
   if (path == 3) return ((size_t)A_rows * 4 + 255) & ~(size_t)255;                 // row sums over all of K
   if (w.fmt != 3 && epi != 1 && (path == 0 || path == 1)) {
     // split-K partial sums of the plain epilogues (the SwiGLU one never splits)

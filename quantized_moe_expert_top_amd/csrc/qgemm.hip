@@ -106,8 +106,7 @@ __device__ __forceinline__ uint32_t shr(uint32_t v, int sh) { return sh >= 0 ? (
 // 4*(i>>1); masking the low / high nibble of every byte leaves one code per
 // byte, and a byte permute with the constant 0x43 builds each pair
 // (elements 2p, 2p+1) as two bf16 values: 7 VALU operations per 8 weights.
-__device__ __forceinline__ bf16x8 deq_u4(const u32x4& cd, int t) {
-  const uint32_t d = cd[t];
+__device__ __forceinline__ u32x4 deq_nib(uint32_t d) {
   const uint32_t lo = d & 0x0F0F0F0Fu;         // bytes: e0 e4 e1 e5
   const uint32_t hi = (d >> 4) & 0x0F0F0F0Fu;  // bytes: e2 e6 e3 e7
   const uint32_t K = 0x43434343u;
@@ -116,24 +115,23 @@ __device__ __forceinline__ bf16x8 deq_u4(const u32x4& cd, int t) {
   r[1] = __builtin_amdgcn_perm(K, hi, 0x04020400u);  // (e2, e3)
   r[2] = __builtin_amdgcn_perm(K, lo, 0x04030401u);  // (e4, e5)
   r[3] = __builtin_amdgcn_perm(K, hi, 0x04030401u);  // (e6, e7)
-  return as_bf16x8(r);
-}
-
-// MWQ: c_b = 4*q2 + 2*d3*[b>=3] + d4*[b==4], placed straight into the low
-// mantissa bits (q2 at bits 2-3, d3 at bit 1, d4 at bit 0 of each half).
-__device__ __forceinline__ u32x4 deq_mwq_bits(const u32x2& q2, uint32_t d3, uint32_t d4, int t, int b) {
-  const uint32_t Q = q2[t >> 1];
-  u32x4 r;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int P = 4 * (t & 1) + p;
-    const int P3 = 4 * t + p;
-    uint32_t v = (shr(Q, 2 * P - 2) & 0x000C000Cu) | 0x43004300u;
-    if (b >= 3) v |= shr(d3, P3 - 1) & 0x00020002u;
-    if (b == 4) v |= shr(d4, P3) & 0x00010001u;
-    r[p] = v;
-  }
   return r;
+}
+__device__ __forceinline__ bf16x8 deq_u4(const u32x4& cd, int t) { return as_bf16x8(deq_nib(cd[t])); }
+
+// MWQ: c_b = 4*q2 + 2*d3*[b>=3] + d4*[b==4] as 4-bit nibbles in the INT4
+// order, from the nested planes' tiled layout (each plane masked and shifted
+// by the step: q2 at bits 2-3 of each nibble for even steps, 0-1 for odd ones;
+// d3 / d4 at bit 3 - t), then the INT4 conversion.
+__device__ __forceinline__ uint32_t mwq_nib(const u32x2& q2, uint32_t d3, uint32_t d4, int t, int b) {
+  const uint32_t Q = q2[t >> 1];
+  uint32_t n = ((t & 1) ? (Q << 2) : Q) & 0xCCCCCCCCu;
+  if (b >= 3) n |= shr(d3, 2 - t) & 0x22222222u;
+  if (b == 4) n |= shr(d4, 3 - t) & 0x11111111u;
+  return n;
+}
+__device__ __forceinline__ u32x4 deq_mwq_bits(const u32x2& q2, uint32_t d3, uint32_t d4, int t, int b) {
+  return deq_nib(mwq_nib(q2, d3, d4, t, b));
 }
 __device__ __forceinline__ bf16x8 deq_mwq(const u32x2& q2, uint32_t d3, uint32_t d4, int t, int b) {
   return as_bf16x8(deq_mwq_bits(q2, d3, d4, t, b));
@@ -228,9 +226,30 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // fragment per tile; MWQ = q2 (8 bytes) + d3 + d4 (4 bytes each) per tile.
 struct BRegs {
   u32x4 c[2];
+  u32x4 c8[2];  // 8-bit codes: MFMA steps 2 and 3 (steps 0 and 1 in c)
   u32x2 q[2];
   uint32_t d3[2], d4[2];
 };
+
+// Two floats that are exact in bf16 (here integers of at most 8 significant
+// bits) as a bf16 pair, the first in the low half: their high halves.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
+}
+
+// 8-bit codes: the 8 codes of MFMA step t (bytes 8t .. 8t + 7 of the lane's 32)
+// become the exact bf16 values c - z (|c - z| <= 255 needs 8 significant bits).
+__device__ __forceinline__ bf16x8 deq_u8(const u32x4& lo, const u32x4& hi, int t, float z) {
+  const u32x4& v = t < 2 ? lo : hi;
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t d = v[2 * (t & 1) + h];
+    r[2 * h] = pack_bf16x2((float)(d & 0xFFu) - z, (float)((d >> 8) & 0xFFu) - z);
+    r[2 * h + 1] = pack_bf16x2((float)((d >> 16) & 0xFFu) - z, (float)(d >> 24) - z);
+  }
+  return as_bf16x8(r);
+}
 
 // ------------------------------------------------------------ decode, deep
 // One workgroup per (16-row tile of one segment, channel group of 64 SwiGLU /
@@ -269,12 +288,14 @@ struct BRegs {
 // FMT 5 (static width per expert, from `tab`): the codes, shifted to 4 bits,
 // are stored as the nested planes, only the first b of them per tile block
 // (256 * b bytes); the correction uses z << (4 - b) and the group scale is
-// multiplied by 2^(b - 4), both exact.
+// multiplied by 2^(b - 4), both exact.  An 8-bit expert keeps plain bytes (32
+// per lane and tile block, 2 KB per block) that convert straight to the exact
+// bf16 values c - z: no correction chain.
 // The per-expert table travels only with FMT 5: 1.5 KB of launch arguments
 // would slow every launch of the other formats.
 struct NoTab {};
 template <int FMT>
-using TabOf = typename std::conditional<FMT == 5, XTab, NoTab>::type;
+using TabOf = typename std::conditional<FMT == 5 || FMT == 6, XTab, NoTab>::type;
 __device__ __forceinline__ int tab_bits(const XTab& t, int e) { return t.bits[e]; }
 __device__ __forceinline__ int tab_zero(const XTab& t, int e) { return t.zero[e]; }
 __device__ __forceinline__ size_t tab_off(const XTab& t, int e) { return t.off[e]; }
@@ -287,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
                                                            TabOf<FMT> tab) {
   constexpr bool MW = FMT != 1;                // nested bit planes
   constexpr bool FU = FMT == 4;                // all widths of an expert per tile
-  constexpr bool FX = FMT == 5;                // one width per expert
+  constexpr bool FX = FMT == 5 || FMT == 6;    // one width per expert (6: the 8-bit experts, 5: the others)
   constexpr int SPG = 4 / GPB;                 // MFMA steps per scale group
   constexpr int PF = 3, R = 4;                 // prefetch distance, ring size
   __shared__ u32x4 lds_a[3][4][64];            // [slot][step][lane], 12 KB
@@ -311,6 +332,8 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
   const int o1 = FU ? uniform(p.seg_offsets[seg * SS + 1]) : 0;
   const int o2 = FU ? uniform(p.seg_offsets[seg * SS + 2]) : 0;
   if (FX) c.bits = uniform(tab_bits(tab, c.e));
+  // the 8-bit experts' larger register ring runs in a launch of its own
+  if (FX && ((c.bits == 8) != (FMT == 6))) return;
   const bool need3 = FU ? c.row0 < o2 : c.bits >= 3;
   const bool need4 = FU ? c.row0 < o1 : c.bits == 4;
   const int lrow = c.row0 + (lane & 15);
@@ -341,10 +364,11 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
                       wvalid ? (16 * KBt * GPB - kb_lo * GPB) * 2 : 0);
   }
   const uint32_t soff = (uint32_t)((lane & 15) * KBt * GPB * 2);
-  const uint32_t zl = FX ? uniform(tab_zero(tab, c.e) << (4 - c.bits)) : (uint32_t)p.z;
+  const uint32_t zl = FX ? (c.bits < 8 ? uniform(tab_zero(tab, c.e) << (4 - c.bits)) : 0u) : (uint32_t)p.z;
   const uint32_t negc = (0xC300u | zl) * 0x00010001u;
   const bf16x8 neg = as_bf16x8(u32x4{negc, negc, negc, negc});
-  const float smul = FX ? __builtin_ldexpf(1.0f, c.bits - 4) : 1.0f;  // 4-bit-shifted codes: exact
+  const float smul = (FX && c.bits < 8) ? __builtin_ldexpf(1.0f, c.bits - 4) : 1.0f;  // 4-bit-shifted codes: exact
+  const float zf = FX ? (float)tab_zero(tab, c.e) : 0.f;  // 8-bit experts
 
   f32x4 acc[2] = {f32x4{}, f32x4{}};
   u32x4 ra[R];
@@ -358,6 +382,9 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
     _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                      \
       if (FMT == 1) {                                                                    \
         rb[SLOT].c[u] = buf_x4(br[u], 16 * lane, kbi * CB);                              \
+      } else if (B8) {                                                                   \
+        rb[SLOT].c[u] = buf_x4(br[u], 32 * lane, kbi * CB);                              \
+        rb[SLOT].c8[u] = buf_x4(br[u], 32 * lane + 16, kbi * CB);                        \
       } else {                                                                           \
         rb[SLOT].q[u] = buf_x2(br[u], 8 * lane, kbi * CB);                               \
         rb[SLOT].d3[u] = L3 ? buf_x1(r3[u], 4 * lane, kbi * CB) : 0u;                    \
@@ -373,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
     const int sl = (I) % 3;                                                                              \
     _Pragma("unroll") for (int t0 = 0; t0 < 4; t0 += SPG) {                                              \
       f32x4 cr = f32x4{};                                                                                \
-      _Pragma("unroll") for (int t = t0; t < t0 + SPG; ++t) cr = mfma16(as_bf16x8(lds_a[sl][t][lane]), neg, cr); \
+      _Pragma("unroll") for (int t = t0; t < t0 + SPG; ++t) if (!B8) cr = mfma16(as_bf16x8(lds_a[sl][t][lane]), neg, cr); \
       f32x4 tm[2] = {cr, cr};                                                                            \
       _Pragma("unroll") for (int t = t0; t < t0 + SPG; ++t) {                                            \
         const u32x4 araw = lds_a[sl][t][lane];                                                           \
@@ -386,6 +413,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
             tm[u] = mfma16(as_bf16x8(and4(araw, m2)), as_bf16x8(and4(b4, 0xFFFCFFFCu)), tm[u]);          \
           } else {                                                                                       \
             const bf16x8 bv = (FMT == 1) ? deq_u4(rb[J].c[u], t)                                         \
+                              : B8       ? deq_u8(rb[J].c[u], rb[J].c8[u], t, zf)                        \
                                          : deq_mwq(rb[J].q[u], rb[J].d3[u], rb[J].d4[u], t, BW ? BW : 4); \
             tm[u] = mfma16(av, bv, tm[u]);                                                               \
           }                                                                                              \
@@ -421,7 +449,8 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
   // nor decodes the planes it does not have.
   auto k_loop = [&](auto bw_tag) {
     constexpr int BW = decltype(bw_tag)::value;
-    constexpr bool L3 = BW != 2, L4 = BW == 0 || BW == 4;  // d3 / d4 planes loaded
+    constexpr bool B8 = BW == 8;                            // plain 8-bit codes
+    constexpr bool L3 = BW != 2 && !B8, L4 = BW == 0 || BW == 4;  // d3 / d4 planes loaded
     // prologue: activations and weights of K blocks 0..PF-1 in flight, block 0 staged
 #pragma unroll
     for (int j = 0; j < PF; ++j)
@@ -441,7 +470,13 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
       QD_STEP(3)
     }
   };
-  if constexpr (FMT == 2 || FX) {
+  if constexpr (FMT == 6) {
+    k_loop(std::integral_constant<int, 8>{});
+  } else if constexpr (FX) {
+    if (c.bits == 2) k_loop(std::integral_constant<int, 2>{});
+    else if (c.bits == 3) k_loop(std::integral_constant<int, 3>{});
+    else k_loop(std::integral_constant<int, 4>{});
+  } else if constexpr (FMT == 2) {
     if (c.bits == 2) k_loop(std::integral_constant<int, 2>{});
     else if (c.bits == 3) k_loop(std::integral_constant<int, 3>{});
     else k_loop(std::integral_constant<int, 4>{});
@@ -862,19 +897,29 @@ __global__ __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) void qgemm_p_kernel(KA
 }
 
 // ------------------------------------------------------- prefill, LDS-DMA
-// INT4 with many rows per segment.  One workgroup of 8 wavefronts per
-// (128-row tile, 256-channel block); wavefront (wm, wn) owns 64 rows x 4
-// channel tiles, so every activation fragment read from LDS feeds 4 MFMAs and
-// every dequantised weight fragment 4.  Activations, weight codes and the
-// activation row sums of each K block go straight from memory into one of
-// three LDS stages (global_load_lds, no register staging), two blocks ahead
-// of the block being multiplied: each wavefront waits for its own loads with
-// an explicit vmcnt, and one barrier per K block publishes the stage to the
-// others and retires the stage the next loads overwrite.  The group scales
+// INT4 and nested MWQ with many rows per segment.  One workgroup per (64-row
+// tile, 256-channel block) of 4 wavefronts, two workgroups per CU (or, with 4
+// scale groups per K block, per 128-row tile of 8 wavefronts); wavefront
+// (wm, wn) owns 64 rows x 4 channel tiles, so every activation fragment read
+// from LDS feeds 4 MFMAs and every dequantised weight fragment 4.
+// Activations, weight codes and the activation row sums of each K block go
+// straight from memory into an LDS stage (global_load_lds, no register
+// staging), one block ahead of the block being multiplied (two with three
+// stages): each wavefront waits for its own loads with an explicit vmcnt, and
+// one barrier per K block publishes the stage to the others and retires the
+// stage the next loads overwrite.  Two 64-row workgroups with two stages each
+// (70 KB of LDS apiece) beat one 128-row workgroup with three: while one
+// waits at its barrier the other issues MFMAs.  The group scales
 // (two bytes per channel and group) come through registers.  The row sums are
 // those of the bias correction, -(128 + z) * sum_k a_k per scale group,
 // written by rowsum_kernel into the workspace.
 constexpr int kP2Threads = 512, kP2Rows = 128;
+#ifndef P2_WM
+#define P2_WM 1  // 64-row workgroups
+#endif
+#ifndef P2_NS
+#define P2_NS 2  // two LDS stages
+#endif
 
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -904,11 +949,13 @@ __global__ __launch_bounds__(256) void rowsum_kernel(const uint16_t* __restrict_
   }
 }
 
+// One LDS stage of a K block for a workgroup of 4 * WM wavefronts (64 * WM rows).
+template <int WM>
 struct __attribute__((aligned(16))) P2Stage {
-  u32x4 a[8][4][64];  // activations [row tile][MFMA step][lane], 32 KB
-  u32x4 b[16][64];    // codes [workgroup tile][lane], 16 KB
-  float r[512];       // row sums [group][row] (+ padding), 2 KB
-  uint32_t s[512];    // group scales, one dword (two fp16) per channel and group pair, 2 KB
+  u32x4 a[4 * WM][4][64];  // activations [row tile][MFMA step][lane], 16 KB per 64 rows
+  u32x4 b[16][64];         // codes [workgroup tile][lane], 16 KB
+  float r[256 * WM];       // row sums [group][row] (+ padding)
+  uint32_t s[256 * WM];    // group scales, one dword (two fp16) per channel and group pair
 };
 
 // SL: the group scales of each K block travel by LDS-DMA with the block, one
@@ -916,23 +963,23 @@ struct __attribute__((aligned(16))) P2Stage {
 // nothing but LDS-DMA loads.  It needs an even number of groups per channel
 // (K/G); otherwise every K block loads its scales into registers.
 
-// Nested MWQ in the 128-row kernel: the rows of an expert are cut into
-// 16-row chunks inside each width's sub-segment (b = 4, 3, 2 in grouped
-// order), so that every MFMA row tile has one width, and a workgroup takes 8
-// chunks of one expert.  All planes of a tile block are loaded once for all
+// Nested MWQ in the 64- and 128-row kernels: the rows of an expert are cut
+// into 16-row chunks inside each width's sub-segment (b = 4, 3, 2 in grouped
+// order), so that every MFMA row tile has one width, and a workgroup takes 4
+// or 8 chunks of one expert.  All planes of a tile block are loaded once for all
 // of them; each row tile multiplies the codes truncated to its width.
 __device__ __forceinline__ int mwq_chunks(const int32_t* so, int e) {
   const int o0 = so[3 * e], o1 = so[3 * e + 1], o2 = so[3 * e + 2], o3 = so[3 * e + 3];
   return (o1 - o0 + 15) / 16 + (o2 - o1 + 15) / 16 + (o3 - o2 + 15) / 16;
 }
-// Work item y (in expert order, ceil(chunks / 8) per expert) -> expert e and
+// Work item y (in expert order, ceil(chunks / cpg) per expert) -> expert e and
 // its chunk group g.
-__device__ __forceinline__ bool find_mwq_group(const int32_t* so, int E, int y, int& e, int& g) {
+__device__ __forceinline__ bool find_mwq_group(const int32_t* so, int E, int y, int& e, int& g, int cpg) {
   const int lane = threadIdx.x & 63;
   int carry = 0;
   for (int s0 = 0; s0 < E; s0 += 64) {
     const int s = s0 + lane;
-    const int tiles = s < E ? (mwq_chunks(so, s) + 7) / 8 : 0;
+    const int tiles = s < E ? (mwq_chunks(so, s) + cpg - 1) / cpg : 0;
     int incl = tiles;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -952,17 +999,32 @@ __device__ __forceinline__ bool find_mwq_group(const int32_t* so, int E, int y, 
   return false;
 }
 
-template <int EPI, int GPB, bool SL, bool MW>
-__global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const float* __restrict__ rowsum, int n_nblk,
-                                                              int n_mt, int GM) {
+// MW: 0 INT4; 1 nested MWQ, workgroups of 16-row chunks of every width of an
+// expert (above); 2 nested MWQ, row tiles inside one width sub-segment (a
+// segment per expert and width, like INT4's per expert): the workgroup's width
+// is then known, so the K loop is compiled once per width, loads no plane
+// it does not use (those lanes read past the buffer's end: no traffic) and
+// decodes its codes at that width with no per-row-tile mask.
+// WM: wavefront rows of the workgroup (1: 4 wavefronts on 64 rows, 2: 8 on
+// 128 rows); NS: LDS stages (K blocks in flight: NS - 1).  A 64-row workgroup
+// with two stages takes 70 KB of LDS, so two run on one CU and fill each
+// other's barrier and load waits.  The kernels below declare their LDS stages
+// (one object per stage) and run this body.
+template <int EPI, int GPB, bool SL, int MW, int WM, int NS, class Stage>
+__device__ __forceinline__ void qgemm_p2_body(const KArgs& p, const float* __restrict__ rowsum, int n_nblk, int n_mt,
+                                              int GM, Stage& st0, Stage& st1, Stage& st2) {
+  static_assert(WM == 1 || WM == 2, "64 or 128 rows per workgroup");
+  static_assert(NS == 2 || NS == 3, "two or three LDS stages");
+  static_assert(WM == 2 || GPB <= 2, "64-row workgroups keep one scale dword per channel");
+  static_assert(MW >= 0 && MW <= 2, "INT4, nested chunks or nested per width");
   constexpr int RT = 4, UT = 4, SPG = 4 / GPB;
+  constexpr int MT = 64 * WM;          // rows per workgroup
+  constexpr int CPW = 4 / WM;          // code tiles loaded per wavefront
   // vector-memory instructions per K block and wavefront (MW: four dword loads per code tile)
-  constexpr int NB = MW ? 8 : 2;
+  constexpr int NB = MW ? 4 * CPW : CPW;
   constexpr int V = SL ? 6 + NB : 5 + NB + UT * GPB;
+  constexpr int VW = NS == 3 ? V : 0;  // loads that may stay in flight before a block is read
   constexpr int PPS = (6 + NB + 3) / 4;  // load parts issued per MFMA step (one scale group per block)
-  // one object per stage: the compiler tracks outstanding LDS-DMA writes per
-  // LDS object, and only a few objects at a time
-  __shared__ P2Stage st0, st1, st2;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = uniform(tid >> 6), wm = wv >> 2, wn = wv & 3;
 
@@ -972,27 +1034,29 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
   const int nb = rem / GM, mt = grp * GM + rem % GM;
   if (mt >= n_mt) return;
   int seg = 0, m0 = 0;
-  if (MW) {
-    if (!find_mwq_group(p.seg_offsets, p.nseg / 3, mt, seg, m0)) return;  // seg = expert, m0 = chunk group
-  } else if (!find_tile(p.seg_offsets, p.nseg, mt, seg, m0, kP2Rows)) {
+  if (MW == 1) {
+    if (!find_mwq_group(p.seg_offsets, p.nseg / 3, mt, seg, m0, 4 * WM)) return;  // seg = expert, m0 = chunk group
+  } else if (!find_tile(p.seg_offsets, p.nseg, mt, seg, m0, MT)) {
     return;
   }
-  const Ctx c = MW ? Ctx{0, 0, uniform(seg), 4}
-                   : Ctx{uniform(p.seg_offsets[seg] + m0),
-                         uniform(min(kP2Rows, p.seg_offsets[seg + 1] - p.seg_offsets[seg] - m0)), uniform(seg), 4};
+  const Ctx c = MW == 1 ? Ctx{0, 0, uniform(seg), 4}
+                        : Ctx{uniform(p.seg_offsets[seg] + m0),
+                              uniform(min(MT, p.seg_offsets[seg + 1] - p.seg_offsets[seg] - m0)),
+                              uniform(MW == 2 ? seg / 3 : seg), 4};
+  const int tile_bits = MW == 2 ? 4 - seg % 3 : 4;  // sub-segments in grouped order: 4, 3, 2 bits
   const int KB = p.K / 128, NT = p.N / 16;
 
-  // MW: chunk j (0..7) of the workgroup -> first grouped row, rows (0 past the
+  // MW: chunk j (0 .. 4 WM - 1) of the workgroup -> first grouped row, rows (0 past the
   // expert's last chunk, whose loads then repeat the expert's first row), width
   int o[4] = {0, 0, 0, 0}, nc[3] = {0, 0, 0};
-  if (MW) {
+  if (MW == 1) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) o[q] = uniform(p.seg_offsets[3 * c.e + q]);
 #pragma unroll
     for (int q = 0; q < 3; ++q) nc[q] = (o[q + 1] - o[q] + 15) / 16;
   }
   auto chunk = [&](int j, int& start, int& rows, int& bits) {
-    int ci = 8 * m0 + j;
+    int ci = 4 * WM * m0 + j;
     start = o[0];
     rows = 0;
     bits = 2;
@@ -1008,7 +1072,7 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
   };
   // grouped row -> source row of A
   auto a_row = [&](int gi) -> size_t { return p.gather ? (size_t)(p.gather[gi] / p.k) : (size_t)gi; };
-  // MW: source row of row r (0..127) of the workgroup tile
+  // MW: source row of row r (0 .. MT - 1) of the workgroup tile
   auto mw_src_row = [&](int r) -> size_t {
     int st, rw, bt;
     chunk(r >> 4, st, rw, bt);
@@ -1031,46 +1095,50 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
   };
 
   // loads issued by this wavefront: activation row tile wv (4 steps), workgroup
-  // tiles 2wv, 2wv + 1, row-sum entries 64wv .. 64wv + 63.  Buffer loads: the
-  // per-lane offset stays fixed and each K block only moves the scalar offset.
+  // tiles CPW wv .. CPW wv + CPW - 1, row-sum entries 64wv .. 64wv + 63.  Buffer
+  // loads: the per-lane offset stays fixed and each K block only moves the
+  // scalar offset.
   const rsrc_t ar = make_rsrc(p.A, p.A_bytes);
-  const uint32_t a_off = (uint32_t)((MW ? mw_src_row(16 * wv + (lane & 15)) : src_row(p, c, 16 * wv + (lane & 15))) *
+  const uint32_t a_off = (uint32_t)((MW == 1 ? mw_src_row(16 * wv + (lane & 15)) : src_row(p, c, 16 * wv + (lane & 15))) *
                                          (size_t)p.K * 2 + 16 * (lane >> 4));
-  rsrc_t br[2];
+  rsrc_t br[4];  // CPW used
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < CPW; ++q) {
     bool v;
-    const int t = wg_tile(2 * wv + q, v);
+    const int t = wg_tile(CPW * wv + q, v);
     br[q] = make_rsrc(p.codes + ((size_t)c.e * NT + t) * (size_t)KB * 1024, KB * 1024);
   }
   // MW: the four dword loads j = 0..3 of a code tile build, in LDS, lane L's
   // 16-byte record (q2 dwords 2L and 2L + 1, d3 dword L, d4 dword L) for
   // L = 16 j .. 16 j + 15: load lane m writes dword m % 4 of record 16 j + m / 4
+  // (MW 2: the lanes of a plane the tile's width does not use read past the end)
   uint32_t bo[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int L = 16 * j + (lane >> 2), w = lane & 3;
-    bo[j] = (uint32_t)(w < 2 ? 8 * L + 4 * w : 512 + 256 * (w - 2) + 4 * L);
+    const bool unused = (w == 2 && tile_bits < 3) || (w == 3 && tile_bits < 4);
+    bo[j] = unused ? 0x80000000u : (uint32_t)(w < 2 ? 8 * L + 4 * w : 512 + 256 * (w - 2) + 4 * L);
   }
   const int ng = KB * GPB;
   const int en = 64 * wv + lane;
-  const bool ren = en < 128 * GPB;
+  const bool ren = en < MT * GPB;
   const rsrc_t rr = make_rsrc(rowsum, (p.A_bytes / (2u * p.K)) * ng * 4);
   const uint32_t r_off =
-      (uint32_t)(((MW ? mw_src_row(ren ? (en & 127) : 0) : src_row(p, c, ren ? (en & 127) : 0)) * (size_t)ng +
-                  (ren ? (en >> 7) : 0)) * 4);
+      (uint32_t)(((MW == 1 ? mw_src_row(ren ? (en % MT) : 0) : src_row(p, c, ren ? (en % MT) : 0)) * (size_t)ng +
+                  (ren ? (en / MT) : 0)) * 4);
   // MW: this wavefront's row tiles (chunks 4wm + rt): codes truncated to their width
   uint32_t mrt[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     int st, rw, bt;
     chunk(4 * wm + rt, st, rw, bt);
-    mrt[rt] = uniform(bt == 4 ? 0xFFFFFFFFu : bt == 3 ? 0xFFFEFFFEu : 0xFFFCFFFCu);
+    mrt[rt] = MW == 1 ? uniform(bt == 4 ? 0xFFFFFFFFu : bt == 3 ? 0xFFFEFFFEu : 0xFFFCFFFCu) : 0xFFFFFFFFu;
   }
 
   // scale entries: dword 64wv + lane of the stage holds, for GPB <= 2,
-  // channel (j, c) = (entry / 16, entry % 16) (entries 256.. are padding, they
-  // reload entry 0), for GPB = 4 the group pair entry % 2 of channel entry / 2
+  // channel (j, c) = (entry / 16, entry % 16) (with 8 wavefronts, entries 256..
+  // are padding, they reload entry 0), for GPB = 4 the group pair entry % 2 of
+  // channel entry / 2
   const rsrc_t scr = make_rsrc(p.scales, (uint32_t)((size_t)(p.nseg / p.S) * p.N * ng * 2));
   uint32_t s_off;
   {
@@ -1096,12 +1164,12 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int u = 0; u < UT; ++u) acc[rt][u] = f32x4{};
-  uint32_t rsc[3][UT][GPB];  // one register per scale: packing two would wait for both loads
+  uint32_t rsc[NS][UT][GPB];  // one register per scale: packing two would wait for both loads
 
 #define P2_ISSUE(S, ST, KBI) \
   _Pragma("unroll") for (int q_ = 0; q_ < 6 + NB; ++q_) P2_PART(S, ST, KBI, q_)
 // Part Q (0 .. 5 + NB) of the loads of block KBI into stage ST: activations
-// step 0..3, the two code tiles (MW: four parts each), row sums, scales; with
+// step 0..3, the CPW code tiles (MW: four parts each), row sums, scales; with
 // register scales (!SL) the last part loads them into slot S.  Offsets go in
 // the scalar operand: the immediate one would move the LDS address too.
 #define P2_PART(S, ST, KBI, Q)                                                                         \
@@ -1111,10 +1179,10 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, &ST.a[wv][(Q) & 3][0], 16, a_off, kbi * 256 + 64 * ((Q) & 3), 0, 0); \
     else if ((Q) < 4 + NB) {                                                                           \
       if (MW)                                                                                          \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(br[((Q) - 4) >> 2], &ST.b[2 * wv + (((Q) - 4) >> 2)][16 * (((Q) - 4) & 3)], \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(br[((Q) - 4) >> 2], &ST.b[CPW * wv + (((Q) - 4) >> 2)][16 * (((Q) - 4) & 3)], \
                                                  4, bo[((Q) - 4) & 3], kbi * 1024, 0, 0);              \
       else                                                                                             \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(br[((Q) - 4) & 1], &ST.b[2 * wv + (((Q) - 4) & 1)][0], 16, 16 * lane, \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(br[(Q) - 4], &ST.b[CPW * wv + (Q) - 4][0], 16, 16 * lane, \
                                                  kbi * 1024, 0, 0);                                    \
     } else if ((Q) == 4 + NB)                                                                          \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, &ST.r[64 * wv], 4, r_off, kbi * GPB * 4, 0, 0);     \
@@ -1137,7 +1205,7 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
     _Pragma("unroll") for (int g = 0; g < GPB; ++g) {                                                      \
       f32x4 rv[RT];                                                                                        \
       _Pragma("unroll") for (int rt = 0; rt < RT; ++rt)                                                    \
-          rv[rt] = *reinterpret_cast<const f32x4*>(&ST.r[g * 128 + 64 * wm + 16 * rt + 4 * (lane >> 4)]); \
+          rv[rt] = *reinterpret_cast<const f32x4*>(&ST.r[g * MT + 64 * wm + 16 * rt + 4 * (lane >> 4)]); \
       u32x4 av[2][RT];                                                                                     \
       _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) av[0][rt] = ST.a[4 * wm + rt][g * SPG][lane];      \
       f32x4 tmp[RT][UT];                                                                                   \
@@ -1154,12 +1222,12 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
         }                                                                                                  \
         u32x4 bv[UT];                                                                                      \
         _Pragma("unroll") for (int u = 0; u < UT; ++u)                                                     \
-            bv[u] = MW ? deq_mwq_bits(u32x2{cb[u][0], cb[u][1]}, cb[u][2], cb[u][3], t, 4)                 \
+            bv[u] = MW ? deq_mwq_bits(u32x2{cb[u][0], cb[u][1]}, cb[u][2], cb[u][3], t, BW)                \
                        : __builtin_bit_cast(u32x4, deq_u4(cb[u], t));                                      \
         _Pragma("unroll") for (int rt = 0; rt < RT; ++rt) {                                                \
           const bf16x8 a = as_bf16x8(av[tt & 1][rt]);                                                      \
           _Pragma("unroll") for (int u = 0; u < UT; ++u)                                                   \
-              tmp[rt][u] = mfma16(a, as_bf16x8(MW ? and4(bv[u], mrt[rt]) : bv[u]), tt == 0 ? rv[rt] : tmp[rt][u]); \
+              tmp[rt][u] = mfma16(a, as_bf16x8(MW == 1 ? and4(bv[u], mrt[rt]) : bv[u]), tt == 0 ? rv[rt] : tmp[rt][u]); \
         }                                                                                                  \
       }                                                                                                    \
       _Pragma("unroll") for (int u = 0; u < UT; ++u) {                                                     \
@@ -1178,14 +1246,14 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
 #define P2_READY(I)                  \
   {                                  \
     __builtin_amdgcn_sched_barrier(0); \
-    if ((I) + 1 < KB) vm_wait<V>();  \
+    if ((I) + 1 < KB) vm_wait<VW>(); \
     else vm_wait<0>();               \
     __builtin_amdgcn_s_barrier();    \
   }
 #define P2_READY_U                     \
   {                                    \
     __builtin_amdgcn_sched_barrier(0); \
-    vm_wait<V>();                      \
+    vm_wait<VW>();                     \
     __builtin_amdgcn_s_barrier();      \
   }
 #define P2_STEP_U(J, CS, IS, I)                                                     \
@@ -1200,8 +1268,8 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
         const int half = GPB == 1 ? ((I) & 1) : (g & 1);                            \
         sc16[u][g] = (uint16_t)(d >> (16 * half));                                   \
       }                                                                             \
-    if (GPB != 1) P2_ISSUE(((J) + 2) % 3, IS, (I) + 2);                             \
-    P2_COMPUTE(J, CS, I, GPB == 1, ((J) + 2) % 3, IS, (I) + 2);                     \
+    if (GPB != 1) P2_ISSUE(((J) + NS - 1) % NS, IS, (I) + NS - 1);                  \
+    P2_COMPUTE(J, CS, I, GPB == 1, ((J) + NS - 1) % NS, IS, (I) + NS - 1);          \
   }
 #define P2_STEP(J, CS, IS, I)                                                       \
   {                                                                                 \
@@ -1215,38 +1283,66 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
         const int half = GPB == 1 ? ((I) & 1) : (g & 1);                            \
         sc16[u][g] = (uint16_t)(d >> (16 * half));                                   \
       }                                                                             \
-    if (GPB != 1 && (I) + 2 < KB) P2_ISSUE(((J) + 2) % 3, IS, (I) + 2);             \
-    P2_COMPUTE(J, CS, I, GPB == 1 && (I) + 2 < KB, ((J) + 2) % 3, IS, (I) + 2);     \
+    if (GPB != 1 && (I) + NS - 1 < KB) P2_ISSUE(((J) + NS - 1) % NS, IS, (I) + NS - 1); \
+    P2_COMPUTE(J, CS, I, GPB == 1 && (I) + NS - 1 < KB, ((J) + NS - 1) % NS, IS, (I) + NS - 1); \
   }
 
+  // The K loop, once per code width known at compile time (BW: 4 unless MW 2).
+  auto k_loop = [&](auto bw_tag) {
+  constexpr int BW = decltype(bw_tag)::value;
   P2_ISSUE(0, st0, 0);
-  if (1 < KB) P2_ISSUE(1, st1, 1);
+  if (NS == 3 && 1 < KB) P2_ISSUE(1, st1, 1);
   P2_READY(0)
-  // Steady state: three blocks per iteration with no branch inside (every
-  // load it issues is in range): the compiler then keeps track of which stage
-  // each load in flight writes and waits only for the stage read next (a
-  // merge of control-flow paths, or more load instructions per loop body,
-  // makes it wait for every load in flight); then the tail.
+  // Steady state: NS blocks per iteration with no branch inside (every load
+  // it issues is in range): the compiler then keeps track of which stage each
+  // load in flight writes and waits only for the stage read next (a merge of
+  // control-flow paths, or more load instructions per loop body, makes it
+  // wait for every load in flight); then the tail.
   int kb0 = 0;
-  for (; kb0 + 5 <= KB; kb0 += 3) {
-    P2_STEP_U(0, st0, st2, kb0)
-    P2_READY_U
-    P2_STEP_U(1, st1, st0, kb0 + 1)
-    P2_READY_U
-    P2_STEP_U(2, st2, st1, kb0 + 2)
-    P2_READY_U
+  if constexpr (NS == 3) {
+    for (; kb0 + 5 <= KB; kb0 += 3) {
+      P2_STEP_U(0, st0, st2, kb0)
+      P2_READY_U
+      P2_STEP_U(1, st1, st0, kb0 + 1)
+      P2_READY_U
+      P2_STEP_U(2, st2, st1, kb0 + 2)
+      P2_READY_U
+    }
+    for (; kb0 < KB; kb0 += 3) {
+      P2_STEP(0, st0, st2, kb0)
+      if (kb0 + 1 < KB) {
+        P2_READY(kb0 + 1)
+        P2_STEP(1, st1, st0, kb0 + 1)
+      }
+      if (kb0 + 2 < KB) {
+        P2_READY(kb0 + 2)
+        P2_STEP(2, st2, st1, kb0 + 2)
+      }
+      if (kb0 + 3 < KB) P2_READY(kb0 + 3)
+    }
+  } else {
+    for (; kb0 + 3 <= KB; kb0 += 2) {
+      P2_STEP_U(0, st0, st1, kb0)
+      P2_READY_U
+      P2_STEP_U(1, st1, st0, kb0 + 1)
+      P2_READY_U
+    }
+    for (; kb0 < KB; kb0 += 2) {
+      P2_STEP(0, st0, st1, kb0)
+      if (kb0 + 1 < KB) {
+        P2_READY(kb0 + 1)
+        P2_STEP(1, st1, st0, kb0 + 1)
+      }
+      if (kb0 + 2 < KB) P2_READY(kb0 + 2)
+    }
   }
-  for (; kb0 < KB; kb0 += 3) {
-    P2_STEP(0, st0, st2, kb0)
-    if (kb0 + 1 < KB) {
-      P2_READY(kb0 + 1)
-      P2_STEP(1, st1, st0, kb0 + 1)
-    }
-    if (kb0 + 2 < KB) {
-      P2_READY(kb0 + 2)
-      P2_STEP(2, st2, st1, kb0 + 2)
-    }
-    if (kb0 + 3 < KB) P2_READY(kb0 + 3)
+  };
+  if constexpr (MW == 2) {
+    if (tile_bits == 2) k_loop(std::integral_constant<int, 2>{});
+    else if (tile_bits == 3) k_loop(std::integral_constant<int, 3>{});
+    else k_loop(std::integral_constant<int, 4>{});
+  } else {
+    k_loop(std::integral_constant<int, 4>{});
   }
 #undef P2_STEP_U
 #undef P2_READY_U
@@ -1261,7 +1357,7 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2_kernel(KArgs p, const flo
   for (int rt = 0; rt < RT; ++rt) {
     // grouped rows of row tile rt: row0 + 16 rt + .. (a 16-row chunk for MW)
     int row0 = c.row0 + 64 * wm + 16 * rt, rows = c.rows - 64 * wm - 16 * rt;
-    if (MW) {
+    if (MW == 1) {
       int bt;
       chunk(4 * wm + rt, row0, rows, bt);
     }
@@ -1561,15 +1657,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
-
-
 template <int FMT, int EPI>
-void launch_d(const KArgs& ka, int n_cg, int n_rt, const XTab& tab, hipStream_t s) {
-  TabOf<FMT> targ{};
-  if constexpr (FMT == 5) targ = tab;
-  const int KBt = ka.K / 128;
-  const int n_ks = (EPI == 1 || !ka.part) ? 1 : decode_splits(n_cg * n_rt, ka.K);
-  const int kb_per = (KBt + n_ks - 1) / n_ks;
+void launch_d_one(const KArgs& ka, int n_cg, int n_rt, int n_ks, int kb_per, const TabOf<FMT>& targ, hipStream_t s) {
   const int items = n_cg * n_ks * n_rt;
   const dim3 grid((unsigned)(((items + 7) / 8) * 8));  // multiple of 8: one equal share per XCD
   switch (ka.G) {
@@ -1585,6 +1674,23 @@ void launch_d(const KArgs& ka, int n_cg, int n_rt, const XTab& tab, hipStream_t 
       hipLaunchKernelGGL((qgemm_d_kernel<FMT, EPI, 4>), grid, dim3(kThreads), 0, s, ka, n_cg, n_rt, n_ks, kb_per,
                          targ);
       break;
+  }
+}
+
+// FMT 5 (a width per expert): one launch for the experts of 2, 3 and 4 bits
+// and one for those of 8 bits, each only if there are such experts.
+template <int FMT, int EPI>
+void launch_d(const KArgs& ka, int n_cg, int n_rt, const XTab& tab, hipStream_t s) {
+  const int KBt = ka.K / 128;
+  const int n_ks = (EPI == 1 || !ka.part) ? 1 : decode_splits(n_cg * n_rt, ka.K);
+  const int kb_per = (KBt + n_ks - 1) / n_ks;
+  if constexpr (FMT == 5) {
+    bool narrow = false, wide = false;
+    for (int e = 0; e < ka.nseg; ++e) (tab.bits[e] == 8 ? wide : narrow) = true;
+    if (narrow) launch_d_one<5, EPI>(ka, n_cg, n_rt, n_ks, kb_per, tab, s);
+    if (wide) launch_d_one<6, EPI>(ka, n_cg, n_rt, n_ks, kb_per, tab, s);
+  } else {
+    launch_d_one<FMT, EPI>(ka, n_cg, n_rt, n_ks, kb_per, NoTab{}, s);
   }
   if (n_ks > 1) {
     const size_t n4 = (size_t)ka.M_total * ka.N / 4;
@@ -1619,22 +1725,50 @@ void launch_p(const KArgs& ka, int M_total, hipStream_t s) {
   }
 }
 
-template <int EPI, bool MW>
+// One LDS object per stage: the compiler tracks outstanding LDS-DMA writes per
+// LDS object, and only a few objects at a time.
+template <int EPI, int GPB, bool SL, int MW, int NS>
+__global__ __launch_bounds__(512, 1) void qgemm_p2_kernel(KArgs p, const float* __restrict__ rowsum, int n_nblk,
+                                                          int n_mt, int GM) {
+  __shared__ P2Stage<2> st0, st1, st2;
+  qgemm_p2_body<EPI, GPB, SL, MW, 2, NS>(p, rowsum, n_nblk, n_mt, GM, st0, st1, st2);
+}
+template <int EPI, int GPB, bool SL, int MW, int NS>
+__global__ __launch_bounds__(256, 2) void qgemm_p2h_kernel(KArgs p, const float* __restrict__ rowsum, int n_nblk,
+                                                           int n_mt, int GM) {
+  __shared__ P2Stage<1> st0, st1, st2;
+  qgemm_p2_body<EPI, GPB, SL, MW, 1, NS>(p, rowsum, n_nblk, n_mt, GM, st0, st1, NS == 3 ? st2 : st0);
+}
+
+template <int EPI, int MW, int WM, int NS>
 void launch_p2(const KArgs& ka, const float* rowsum, int M_total, hipStream_t s) {
+  constexpr int MT = 64 * WM;
   const int n_nblk = EPI == 1 ? (ka.N / 2 + 127) / 128 : (ka.N + 255) / 256;
-  // nested MWQ: at most one partial 16-row chunk per width sub-segment, 8 chunks per workgroup
-  const int n_mt = MW ? (M_total / 16 + ka.nseg + 7) / 8 + ka.nseg / 3 : (M_total + kP2Rows - 1) / kP2Rows + ka.nseg;
-  const int GM = group_rows(ka, M_total, n_mt, kP2Rows, 1, 4u << 20);  // measured best: about 4 MB
+  // nested MWQ in chunks: at most one partial 16-row chunk per width sub-segment, 4 WM chunks per
+  // workgroup; otherwise at most one partial row tile per segment
+  const int n_mt = MW == 1 ? (M_total / 16 + ka.nseg + 4 * WM - 1) / (4 * WM) + ka.nseg / 3
+                           : (M_total + MT - 1) / MT + ka.nseg;
+  const int GM = group_rows(ka, M_total, n_mt, MT, 1, 4u << 20);  // measured best: about 4 MB
   const int items = n_nblk * ((n_mt + GM - 1) / GM) * GM;
   const dim3 grid((unsigned)(((items + 7) / 8) * 8));
-  const dim3 block(kP2Threads);
-#define P2_LAUNCH(GPB, SL) \
-  hipLaunchKernelGGL((qgemm_p2_kernel<EPI, GPB, SL, MW>), grid, block, 0, s, ka, rowsum, n_nblk, n_mt, GM)
+  const dim3 block(256 * WM);
+#define P2_LAUNCH(GPB, SL)                                                                                   \
+  do {                                                                                                       \
+    if constexpr (WM == 2)                                                                                   \
+      hipLaunchKernelGGL((qgemm_p2_kernel<EPI, GPB, SL, MW, NS>), grid, block, 0, s, ka, rowsum, n_nblk, n_mt, GM); \
+    else                                                                                                     \
+      hipLaunchKernelGGL((qgemm_p2h_kernel<EPI, GPB, SL, MW, NS>), grid, block, 0, s, ka, rowsum, n_nblk, n_mt, GM); \
+  } while (0)
   const bool sl = ((ka.K / ka.G) & 1) == 0;
   switch (ka.G) {
     case 128: if (sl) P2_LAUNCH(1, true); else P2_LAUNCH(1, false); break;
     case 64: if (sl) P2_LAUNCH(2, true); else P2_LAUNCH(2, false); break;
-    default: if (sl) P2_LAUNCH(4, true); else P2_LAUNCH(4, false); break;
+    default:  // G = 32: 128-row workgroups only (one scale dword per channel and group pair)
+      if constexpr (WM == 2) {
+        if (sl) P2_LAUNCH(4, true);
+        else P2_LAUNCH(4, false);
+      }
+      break;
   }
 #undef P2_LAUNCH
 }
@@ -1661,13 +1795,22 @@ void launch_epi(const KArgs& ka, int fmt, int path, int M_total, int A_rows, voi
     launch_p2d<EPI>(ka, rs, M_total, s);
     return;
   }
-  if (path == 2) {
+  if (path == 2 || path == 5) {
     float* rs = static_cast<float*>(ws);
     const int rows = A_rows;
     hipLaunchKernelGGL(rowsum_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, ka.A, rows, ka.K, ka.G,
                        -(128.0f + (float)ka.z), rs);
-    if (fmt == 2) launch_p2<EPI, true>(ka, rs, M_total, s);
-    else launch_p2<EPI, false>(ka, rs, M_total, s);
+    // 64-row workgroups (two per CU) unless G = 32 (four groups per K block)
+    const int mw = fmt == 2 ? (path == 5 ? 2 : 1) : 0;
+    if (ka.G == 32) {
+      if (mw == 1) launch_p2<EPI, 1, 2, 3>(ka, rs, M_total, s);
+      else if (mw == 2) launch_p2<EPI, 2, 2, 3>(ka, rs, M_total, s);
+      else launch_p2<EPI, 0, 2, 3>(ka, rs, M_total, s);
+    } else {
+      if (mw == 1) launch_p2<EPI, 1, P2_WM, P2_NS>(ka, rs, M_total, s);
+      else if (mw == 2) launch_p2<EPI, 2, P2_WM, P2_NS>(ka, rs, M_total, s);
+      else launch_p2<EPI, 0, P2_WM, P2_NS>(ka, rs, M_total, s);
+    }
     return;
   }
   if (fmt != 3 && path != 0 && path != 1) {

@@ -10,17 +10,21 @@
 // t = 0..3, the 8 inputs k = kb*128 + 32*t + 8*(l/16) + i, i = 0..7 (the
 // operand layout of v_mfma_f32_16x16x32_bf16).  The bits of one lane and step
 // are placed so that pairs (i = 2p, 2p+1) land in the low / high halfword of a
-// dword after one shift and mask:
-//   4-bit  (1 KB / tile block): dword at 16*l + 4*t; element i at bit
-//          16*(i&1) + 4*(i>>1).
-//   2-bit  (512 B): dword at 8*l + 4*(t/2); with P = 4*(t%2) + (i>>1), element
-//          i at bit 16*(i&1) + 2*P.
-//   1-bit  (256 B): dword at 4*l; with P = 4*t + (i>>1), element i at bit
-//          16*(i&1) + P.
-//   nested MWQ (1 KB, all in `codes`): the q2 plane as 2-bit at byte 0, d3 and
-//          d4 as 1-bit at bytes 512 and 768, so one tile block is one
-//          contiguous kilobyte (read whole by the prefill kernels, plane by
-//          plane by the decode kernel, which skips the planes it needs not).
+// dword after one shift and mask.  Nibble j of a dword (bits 4j .. 4j+3)
+// stands for element i = 2 (j % 4) + j / 4 (j = 4 (i&1) + (i>>1)):
+//   4-bit  (1 KB / tile block): dword at 16*l + 4*t; element i's code in its
+//          nibble (bit 16*(i&1) + 4*(i>>1)).
+//   2-bit delta (512 B): dword at 8*l + 4*(t/2); with P = 4*(t%2) + (i>>1),
+//          element i at bit 16*(i&1) + 2*P.
+//   nested MWQ (1 KB, all in `codes`): planes at bytes 0 (q2), 512 (d3) and
+//          768 (d4), so one tile block is one contiguous kilobyte (read whole
+//          by the prefill kernels, plane by plane by the decode kernel, which
+//          skips the planes it needs not).  q2: dword at 8*l + 4*(t/2), in
+//          element i's nibble at bits 2-3 for even t, 0-1 for odd t; d3 and
+//          d4: dword at 4*l, element i's bit of step t at bit 3 - t of its
+//          nibble.  Masking and shifting each plane by t then ORs the three
+//          into the 4-bit codes of step t in the INT4 order: about five
+//          operations per step and lane, then the INT4 conversion.
 //   bf16 base (4 KB, no expert index): 16 bytes at 1024*t + 16*l hold the 8
 //          inputs in order.
 //   salient values: per (e, ct) ceil(S/32) blocks of 1 KB; lane l holds slots
@@ -62,11 +66,15 @@ __global__ __launch_bounds__(kThreads) void repack_u4_kernel(const uint8_t* __re
   dst[d] = o;
 }
 
+// nibble position of element i (0..7) of an MFMA step
+__device__ __forceinline__ int nib_of(int i) { return 4 * (i & 1) + (i >> 1); }
+
 // 2-bit plane, one 128-thread workgroup per 512-byte tile block; zero_code >= 0
-// replaces the codes of salient channels (2-bit delta).
+// replaces the codes of salient channels (2-bit delta).  q2: the nested
+// planes' layout (nibbles) instead of the delta's.
 __global__ __launch_bounds__(128) void repack_u2_kernel(const uint8_t* __restrict__ src, int N, int K,
                                                         uint32_t* __restrict__ dst, int blk_dw, const int32_t* sal_idx,
-                                                        int n_sal, int zero_code) {
+                                                        int n_sal, int zero_code, bool q2) {
   __shared__ uint32_t salmask[4];
   const TileIdx ti = tile_of(blockIdx.x, N, K);
   if (threadIdx.x < 4) salmask[threadIdx.x] = 0;
@@ -91,13 +99,14 @@ __global__ __launch_bounds__(128) void repack_u2_kernel(const uint8_t* __restric
       const int kk = koff + i;
       if (zero_code >= 0 && ((salmask[kk >> 5] >> (kk & 31)) & 1u)) f = (uint32_t)zero_code;
       const int P = 4 * tt + (i >> 1);
-      o |= f << (16 * (i & 1) + 2 * P);
+      o |= f << (q2 ? 4 * nib_of(i) + 2 - 2 * tt : 16 * (i & 1) + 2 * P);
     }
   }
   dst[(size_t)blockIdx.x * blk_dw + threadIdx.x] = o;  // tile blocks blk_dw dwords apart
 }
 
-// d = dword index of the plane; written at dword off_dw of a tile block of blk_dw dwords
+// d3 / d4 plane of the nested layout.  d = dword index of the plane; written
+// at dword off_dw of a tile block of blk_dw dwords
 __global__ __launch_bounds__(kThreads) void repack_u1_kernel(const uint8_t* __restrict__ src, int N, int K,
                                                              uint32_t* __restrict__ dst, int blk_dw, int off_dw,
                                                              size_t ndw) {
@@ -112,10 +121,7 @@ __global__ __launch_bounds__(kThreads) void repack_u1_kernel(const uint8_t* __re
     const int k0 = ti.kb * 128 + 32 * t + 8 * (l >> 4);
     const uint32_t v = src[(ti.e * N + ch) * (size_t)(K / 8) + k0 / 8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int P = 4 * t + (i >> 1);
-      o |= ((v >> i) & 1u) << (16 * (i & 1) + P);
-    }
+    for (int i = 0; i < 8; ++i) o |= ((v >> i) & 1u) << (4 * nib_of(i) + 3 - t);
   }
   dst[(d / 64) * blk_dw + off_dw + d % 64] = o;
 }
@@ -180,16 +186,19 @@ __global__ __launch_bounds__(kThreads) void repack_mixed_kernel(const uint8_t* _
     return ((v >> (pos & 7)) & ((1u << b) - 1)) << (4 - b);
   };
   uint32_t o = 0;
-  if (w < 128) {  // q2: lane l = w / 2, steps 2 (w & 1) and 2 (w & 1) + 1
+  if (b == 8) {  // 8-bit codes as bytes: lane l = w / 8 holds 32 bytes, step t = (w % 8) / 2 at bytes 8t .. 8t + 7
+    const int l = w >> 3, j = w & 7, t = j >> 1, ch = ct * 16 + (l & 15);
+    const uint8_t* row = src + (size_t)ch * K + kb * 128 + 32 * t + 8 * (l >> 4) + 4 * (j & 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o |= (uint32_t)row[q] << (8 * q);
+  } else if (w < 128) {  // q2: lane l = w / 2, steps 2 (w & 1) and 2 (w & 1) + 1
     const int l = w >> 1, ch = ct * 16 + (l & 15);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int t = 2 * (w & 1) + tt;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int P = 4 * tt + (i >> 1);
-        o |= (code4(ch, kb * 128 + 32 * t + 8 * (l >> 4) + i) >> 2) << (16 * (i & 1) + 2 * P);
-      }
+      for (int i = 0; i < 8; ++i)
+        o |= (code4(ch, kb * 128 + 32 * t + 8 * (l >> 4) + i) >> 2) << (4 * nib_of(i) + 2 - 2 * tt);
     }
   } else {  // d3 (w < 192) or d4: lane l = w % 64, all four steps
     const int l = (w - 128) & 63, ch = ct * 16 + (l & 15);
@@ -197,10 +206,8 @@ __global__ __launch_bounds__(kThreads) void repack_mixed_kernel(const uint8_t* _
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int P = 4 * t + (i >> 1);
-        o |= ((code4(ch, kb * 128 + 32 * t + 8 * (l >> 4) + i) >> sh) & 1u) << (16 * (i & 1) + P);
-      }
+      for (int i = 0; i < 8; ++i)
+        o |= ((code4(ch, kb * 128 + 32 * t + 8 * (l >> 4) + i) >> sh) & 1u) << (4 * nib_of(i) + 3 - t);
   }
   dst[d] = o;
 }
@@ -236,7 +243,7 @@ int launch_repack(const QWeights& src, const QWeights& dst, void* stream) {
     // DELTA2: 512-byte blocks of 2-bit codes; MWQ: 1 KB blocks, q2 at dword 0, d3 at 128, d4 at 192
     const int blk_dw = delta ? 128 : 256;
     hipLaunchKernelGGL(repack_u2_kernel, dim3((unsigned)nblk), dim3(128), 0, s, src.codes, src.N, src.K, codes,
-                       blk_dw, delta ? src.sal_idx : nullptr, delta ? src.n_sal : 0, delta ? src.z : -1);
+                       blk_dw, delta ? src.sal_idx : nullptr, delta ? src.n_sal : 0, delta ? src.z : -1, !delta);
     if (src.fmt == 2) {
       const size_t ndw = ENK / 32;
       hipLaunchKernelGGL(repack_u1_kernel, dim3(grid_for(ndw)), dim3(kThreads), 0, s, src.p3, src.N, src.K, codes,

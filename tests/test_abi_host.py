@@ -145,7 +145,8 @@ def test_grouped_qgemm_validation(lib):
     assert gemm(lib, desc(), out=0x4004) == MISALIGNED
     assert gemm(lib, desc(), M=0, A=0, seg=0, out=0) == OK           # empty problem
     # kernel choices: unknown, or not for this format
-    assert gemm(lib, desc(), kernel=7) == BAD_FORMAT
+    assert gemm(lib, desc(), kernel=8) == BAD_FORMAT
+    assert gemm(lib, desc(), kernel=q.MOE_KERNEL_LDS_DMA_PER_WIDTH) == UNSUPPORTED          # nested MWQ only
     assert gemm(lib, desc(), kernel=-1) == BAD_FORMAT
     assert gemm(lib, desc(), kernel=q.MOE_KERNEL_SMALL_PER_WIDTH) == UNSUPPORTED            # nested MWQ only
     delta = dict(fmt=q.MOE_W_DELTA2_SALIENT, z=2, ns=4)
@@ -241,7 +242,12 @@ def test_per_expert_width_validation_and_sizes(lib):
         assert fb(d, q.MOE_FIELD_SCALES) == 4 * 256 * (512 // 128) * 2
     assert fb(desc(fmt=P, E=4), q.MOE_FIELD_CODES) == 0                     # tables missing
     assert gemm(lib, desc(fmt=P, E=4)) == NULL_ARG
-    assert gemm(lib, desc(fmt=P, E=4, bits=[4, 8, 2, 2], zero=[0, 0, 0, 0])) == UNSUPPORTED   # no 8-bit width
+    for w in (1, 5, 6, 7, 9, 16):                                                             # 2, 3, 4, 8 only
+        assert gemm(lib, desc(fmt=P, E=4, bits=[4, w, 2, 2], zero=[0, 0, 0, 0])) == UNSUPPORTED
+    d8 = desc(fmt=P, E=4, N=256, K=512, bits=[4, 8, 2, 2], zero=[0, 255, 0, 0])                # an INT8 expert
+    assert gemm(lib, d8, M=0, A=0, seg=0, out=0) == OK
+    assert fb(d8, q.MOE_FIELD_CODES) == 256 * 512 * 16 // 8
+    assert gemm(lib, desc(fmt=P, E=4, bits=[4, 8, 2, 2], zero=[0, 256, 0, 0])) == BAD_SHAPE
     assert gemm(lib, desc(fmt=P, E=4, bits=[4, 2, 2, 2], zero=[0, 4, 0, 0])) == BAD_SHAPE     # z >= 2^b
     assert gemm(lib, desc(fmt=P, E=300, bits=[2] * 300, zero=[1] * 300)) == UNSUPPORTED       # E > 256
     src = desc(fmt=P, layout=q.MOE_LAYOUT_CANONICAL, E=4, bits=bits, zero=zero)

@@ -266,18 +266,19 @@ def test_layer_mwq_decode_full(G):
     dict(T=150, E=8, k=4, H=512, I=256, G=128, seed=83),   # ~75 rows per expert, ragged chunks
     dict(T=64, E=2, k=2, H=128, I=128, G=128, seed=84),    # one K block: odd groups per channel, register scales
 ])
-def test_layer_mwq_prefill_dma_kernel(G, over):
-    """Nested planes in the 128-row LDS-DMA kernel (chosen by itself from 256
-    rows per expert for gate/up, 512 for down): 16-row chunks of every width,
-    one expert per workgroup."""
+@pytest.mark.parametrize("kernel", ["LDS_DMA", "LDS_DMA_PER_WIDTH"])
+def test_layer_mwq_prefill_dma_kernel(G, over, kernel):
+    """Nested planes in the LDS-DMA kernel: 16-row chunks of every width, one
+    expert per workgroup; or row tiles of one width each."""
     cfg = gen.config("mixtral_mwq", **over)
-    buf, ref = _layer_parity(G, cfg, kernel=G.q.MOE_KERNEL_LDS_DMA)
+    buf, ref = _layer_parity(G, cfg, kernel=getattr(G.q, "MOE_KERNEL_" + kernel))
     G.check_ulp(G.bf16_to_np(buf.out), ref["out_h16"], str(over))
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, "cycle"])
-def test_layer_mwq_prefill_widths(G, bits):
-    """The 128-row kernel with one width everywhere, or widths cycling per pair
+@pytest.mark.parametrize("kernel", ["LDS_DMA", "LDS_DMA_PER_WIDTH"])
+def test_layer_mwq_prefill_widths(G, bits, kernel):
+    """The LDS-DMA kernels with one width everywhere, or widths cycling per pair
     (chunks of every width in each workgroup, partial chunks at each end)."""
     cfg = gen.config("mixtral_mwq", T=150, E=3, k=2, H=512, I=1024, seed=85)
     d = gen.generate(cfg)
@@ -286,7 +287,7 @@ def test_layer_mwq_prefill_widths(G, bits):
     else:
         d["pair_bits"][:] = bits
     ref = REF.moe_forward(d, cfg)
-    buf = G.run_layer(d, cfg, kernel=G.q.MOE_KERNEL_LDS_DMA)
+    buf = G.run_layer(d, cfg, kernel=getattr(G.q, "MOE_KERNEL_" + kernel))
     assert np.array_equal(buf.perm.seg_offsets.cpu().numpy(), ref["seg_offsets"])
     out = G.bf16_to_np(buf.out)
     G.check_close(out, ref["out"], f"mwq prefill widths {bits}")
@@ -342,6 +343,24 @@ def test_layer_mixed_decode_full(G):
     """OLMoE decode batch with 4 / 3 / 2 bits by expert popularity (EdgeMoE
     expert-wise bit-width adaptation), every token."""
     _layer_parity(G, gen.config("olmoe_mixed_decode"))
+
+
+def test_layer_edge_decode_full(G):
+    """OLMoE decode batch with INT8 / INT4 / INT2 experts by popularity (the
+    widths EdgeMoE names), every token."""
+    buf, ref = _layer_parity(G, gen.config("olmoe_edge_decode"))
+    G.check_ulp(G.bf16_to_np(buf.out), ref["out_h16"], "olmoe_edge_decode")
+
+
+@pytest.mark.parametrize("over", [
+    dict(T=50, E=5, k=2, H=256, I=512, G=128, bit_probs=(0, 0, 1), seed=98),   # every expert 8 bits
+    dict(T=33, E=6, k=3, H=384, I=256, G=32, zipf=None, seed=99),             # 4 groups per K block, ragged
+    dict(T=8, E=3, k=1, H=256, I=2048, G=64, bit_probs=(0, 0, 1), seed=100),  # down K 2048: split K
+])
+def test_layer_edge_widths(G, over):
+    cfg = gen.config("olmoe_edge_decode", **over)
+    buf, ref = _layer_parity(G, cfg)
+    G.check_ulp(G.bf16_to_np(buf.out), ref["out_h16"], str(over))
 
 
 @pytest.mark.parametrize("over", [

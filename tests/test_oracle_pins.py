@@ -509,7 +509,7 @@ def _py_bitstream(codes, b):
     return np.array(out, dtype=np.uint8)
 
 
-@pytest.mark.parametrize("b", [2, 3, 4])
+@pytest.mark.parametrize("b", [2, 3, 4, 8])
 def test_unpack_bits_against_python_packing(b):
     rng = random.Random(30 + b)
     codes = [rng.randrange(1 << b) for _ in range(8 * 24)]
@@ -531,6 +531,10 @@ def test_per_expert_width_reduces_to_int4_and_2bit_layouts():
     w2 = oracle.dequant_per_expert(st2, s, N, K, G, 2, 1)
     ref2 = np.repeat(oracle.f16_to_f64(s), G, axis=-1) * (oracle.unpack_u2(st2.reshape(N, K // 4)).astype(np.int64) - 1)
     assert np.array_equal(w2, ref2)
+    st8 = rng.integers(0, 256, size=N * K, dtype=np.uint8)  # at 8 bits the stream is the codes, one a byte
+    w8 = oracle.dequant_per_expert(st8, s, N, K, G, 8, 128)
+    ref8 = np.repeat(oracle.f16_to_f64(s), G, axis=-1) * (st8.reshape(N, K).astype(np.int64) - 128)
+    assert np.array_equal(w8, ref8)
 
 
 def test_per_expert_3bit_one_hot_probe():
@@ -557,10 +561,22 @@ def test_mixed_expert_widths_recipe():
     assert d["dn_codes"].size == oracle.expert_stream_offsets(bits, cfg.H, cfg.I)[-1]
 
 
-def test_moe_forward_matches_dense_bruteforce_mixed(impl):
+def test_edge_expert_widths_recipe():
+    """INT2 / INT4 / INT8 experts: the widest width goes to the most popular experts."""
+    cfg = gen.config("olmoe_edge_decode")
+    d = gen.generate(cfg)
+    bits, zero = d["expert_bits"], d["expert_zero"]
+    assert np.bincount(bits, minlength=9)[[2, 4, 8]].tolist() == [26, 22, 16]
+    assert (bits[:16] == 8).all() and (bits[16:38] == 4).all() and (bits[-26:] == 2).all()
+    assert ((zero == 2 ** (bits - 1)) | (zero == 2 ** (bits - 1) - 1)).all()
+    assert d["gu_codes"].size == oracle.expert_stream_offsets(bits, 2 * cfg.I, cfg.H)[-1]
+
+
+@pytest.mark.parametrize("name", ["olmoe_mixed_decode", "olmoe_edge_decode"])
+def test_moe_forward_matches_dense_bruteforce_mixed(impl, name):
     """Per-expert widths: the grouped oracle equals a pure-Python dense evaluation
     that decodes each expert's bit stream itself."""
-    cfg = gen.config("olmoe_mixed_decode", T=5, H=16, I=8, E=4, k=2, G=8, zipf=None)
+    cfg = gen.config(name, T=5, H=16, I=8, E=4, k=2, G=8, zipf=None)
     d = gen.generate(cfg)
     res = impl.moe_forward(d, cfg)
 
@@ -578,6 +594,7 @@ def test_moe_forward_matches_dense_bruteforce_mixed(impl):
                 row.append(f16_val(int(d[prefix + "scales"][e][n][kk // cfg.G])) * (c - z))
             rows.append(row)
         return rows
+    assert set(d["expert_bits"].tolist()) == set(cfg.widths)  # every width of the recipe is exercised
     for t in range(cfg.T):
         xt = [bf16_val(int(v)) for v in d["x"][t]]
         row = [float(v) for v in d["logits"][t]]
