@@ -949,11 +949,12 @@ __global__ __launch_bounds__(256) void rowsum_kernel(const uint16_t* __restrict_
   }
 }
 
-// One LDS stage of a K block for a workgroup of 4 * WM wavefronts (64 * WM rows).
-template <int WM>
+// One LDS stage of a K block for a workgroup of 4 * WM wavefronts (64 * WM
+// rows); LB: the code tiles go through LDS too.
+template <int WM, bool LB>
 struct __attribute__((aligned(16))) P2Stage {
   u32x4 a[4 * WM][4][64];  // activations [row tile][MFMA step][lane], 16 KB per 64 rows
-  u32x4 b[16][64];         // codes [workgroup tile][lane], 16 KB
+  u32x4 b[LB ? 16 : 1][64];  // codes [workgroup tile][lane], 16 KB
   float r[256 * WM];       // row sums [group][row] (+ padding)
   uint32_t s[256 * WM];    // group scales, one dword (two fp16) per channel and group pair
 };
@@ -1020,11 +1021,9 @@ __device__ __forceinline__ void qgemm_p2_body(const KArgs& p, const float* __res
   constexpr int RT = 4, UT = 4, SPG = 4 / GPB;
   constexpr int MT = 64 * WM;          // rows per workgroup
   constexpr int CPW = 4 / WM;          // code tiles loaded per wavefront
-  // vector-memory instructions per K block and wavefront (MW: four dword loads per code tile)
-  constexpr int NB = MW ? 4 * CPW : CPW;
-  constexpr int V = SL ? 6 + NB : 5 + NB + UT * GPB;
-  constexpr int VW = NS == 3 ? V : 0;  // loads that may stay in flight before a block is read
-  constexpr int PPS = (6 + NB + 3) / 4;  // load parts issued per MFMA step (one scale group per block)
+  // 64-row workgroups: each wavefront multiplies the 4 code tiles it loads, so
+  // they go straight into its registers (a ring of NS blocks), not through LDS
+  constexpr bool RB = WM == 1 && MW != 1;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = uniform(tid >> 6), wm = wv >> 2, wn = wv & 3;
 
@@ -1169,16 +1168,29 @@ __device__ __forceinline__ void qgemm_p2_body(const KArgs& p, const float* __res
 #define P2_ISSUE(S, ST, KBI) \
   _Pragma("unroll") for (int q_ = 0; q_ < 6 + NB; ++q_) P2_PART(S, ST, KBI, q_)
 // Part Q (0 .. 5 + NB) of the loads of block KBI into stage ST: activations
-// step 0..3, the CPW code tiles (MW: four parts each), row sums, scales; with
-// register scales (!SL) the last part loads them into slot S.  Offsets go in
-// the scalar operand: the immediate one would move the LDS address too.
+// step 0..3, the CPW code tiles (MW 1: four parts each; RB: into the register
+// ring slot S, nested planes one part per plane the width uses), row sums,
+// scales; with register scales (!SL) the last part loads them into slot S.
+// Offsets go in the scalar operand: the immediate one would move the LDS
+// address too.
 #define P2_PART(S, ST, KBI, Q)                                                                         \
   {                                                                                                    \
     const int kbi = (KBI);                                                                             \
     if ((Q) < 4)                                                                                       \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, &ST.a[wv][(Q) & 3][0], 16, a_off, kbi * 256 + 64 * ((Q) & 3), 0, 0); \
     else if ((Q) < 4 + NB) {                                                                           \
-      if (MW)                                                                                          \
+      if constexpr (RB && MW == 2) {                                                                   \
+        const int pt = ((Q) - 4) / NPT, pl = ((Q) - 4) % NPT;                                          \
+        if (pl == 0) {                                                                                 \
+          const u32x2 q2v = buf_x2(br[pt], 8 * lane, kbi * 1024);                                      \
+          rcb[S][pt][0] = q2v[0];                                                                      \
+          rcb[S][pt][1] = q2v[1];                                                                      \
+        } else {                                                                                       \
+          rcb[S][pt][1 + pl] = buf_x1(br[pt], 256 + 256 * pl + 4 * lane, kbi * 1024);                  \
+        }                                                                                              \
+      } else if constexpr (RB)                                                                         \
+        rcb[S][(Q) - 4] = buf_x4(br[(Q) - 4], 16 * lane, kbi * 1024);                                  \
+      else if (MW)                                                                                     \
         __builtin_amdgcn_raw_ptr_buffer_load_lds(br[((Q) - 4) >> 2], &ST.b[CPW * wv + (((Q) - 4) >> 2)][16 * (((Q) - 4) & 3)], \
                                                  4, bo[((Q) - 4) & 3], kbi * 1024, 0, 0);              \
       else                                                                                             \
@@ -1259,7 +1271,7 @@ __device__ __forceinline__ void qgemm_p2_body(const KArgs& p, const float* __res
 #define P2_STEP_U(J, CS, IS, I)                                                     \
   {                                                                                 \
     u32x4 cb[UT];                                                                   \
-    _Pragma("unroll") for (int u = 0; u < UT; ++u) cb[u] = CS.b[4 * wn + u][lane];  \
+    _Pragma("unroll") for (int u = 0; u < UT; ++u) cb[u] = RB ? rcb[J][u] : CS.b[RB ? 0 : 4 * wn + u][lane]; \
     uint16_t sc16[UT][GPB];                                                         \
     if (SL)                                                                         \
       _Pragma("unroll") for (int u = 0; u < UT; ++u) _Pragma("unroll") for (int g = 0; g < GPB; ++g) { \
@@ -1274,7 +1286,7 @@ __device__ __forceinline__ void qgemm_p2_body(const KArgs& p, const float* __res
 #define P2_STEP(J, CS, IS, I)                                                       \
   {                                                                                 \
     u32x4 cb[UT];                                                                   \
-    _Pragma("unroll") for (int u = 0; u < UT; ++u) cb[u] = CS.b[4 * wn + u][lane];  \
+    _Pragma("unroll") for (int u = 0; u < UT; ++u) cb[u] = RB ? rcb[J][u] : CS.b[RB ? 0 : 4 * wn + u][lane]; \
     uint16_t sc16[UT][GPB];                                                         \
     if (SL)                                                                         \
       _Pragma("unroll") for (int u = 0; u < UT; ++u) _Pragma("unroll") for (int g = 0; g < GPB; ++g) { \
@@ -1290,6 +1302,14 @@ __device__ __forceinline__ void qgemm_p2_body(const KArgs& p, const float* __res
   // The K loop, once per code width known at compile time (BW: 4 unless MW 2).
   auto k_loop = [&](auto bw_tag) {
   constexpr int BW = decltype(bw_tag)::value;
+  constexpr int NPT = MW == 2 ? 1 + (BW >= 3) + (BW == 4) : 1;  // RB, nested: plane loads per code tile
+  // vector-memory instructions per K block and wavefront for the code tiles
+  // (through LDS, MW: four dword loads per code tile)
+  constexpr int NB = RB ? CPW * NPT : MW ? 4 * CPW : CPW;
+  constexpr int V = SL ? 6 + NB : 5 + NB + UT * GPB;
+  constexpr int VW = NS == 3 ? V : 0;  // loads that may stay in flight before a block is read
+  constexpr int PPS = (6 + NB + 3) / 4;  // load parts issued per MFMA step (one scale group per block)
+  u32x4 rcb[NS][UT];  // RB: code tiles of the blocks in flight
   P2_ISSUE(0, st0, 0);
   if (NS == 3 && 1 < KB) P2_ISSUE(1, st1, 1);
   P2_READY(0)
@@ -1730,13 +1750,13 @@ void launch_p(const KArgs& ka, int M_total, hipStream_t s) {
 template <int EPI, int GPB, bool SL, int MW, int NS>
 __global__ __launch_bounds__(512, 1) void qgemm_p2_kernel(KArgs p, const float* __restrict__ rowsum, int n_nblk,
                                                           int n_mt, int GM) {
-  __shared__ P2Stage<2> st0, st1, st2;
+  __shared__ P2Stage<2, true> st0, st1, st2;
   qgemm_p2_body<EPI, GPB, SL, MW, 2, NS>(p, rowsum, n_nblk, n_mt, GM, st0, st1, st2);
 }
 template <int EPI, int GPB, bool SL, int MW, int NS>
 __global__ __launch_bounds__(256, 2) void qgemm_p2h_kernel(KArgs p, const float* __restrict__ rowsum, int n_nblk,
                                                            int n_mt, int GM) {
-  __shared__ P2Stage<1> st0, st1, st2;
+  __shared__ P2Stage<1, MW == 1> st0, st1, st2;
   qgemm_p2_body<EPI, GPB, SL, MW, 1, NS>(p, rowsum, n_nblk, n_mt, GM, st0, st1, NS == 3 ? st2 : st0);
 }
 
