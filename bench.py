@@ -307,7 +307,7 @@ def run_workload(q, name, steps, warmup, copies_arg=0):
                 layer_flops=layer_flops)
 
 
-HBM_BOUND = ("olmoe_decode", "mixtral_mwq_decode", "olmoe_mixed_decode", "tiny")
+HBM_BOUND = ("olmoe_decode", "mixtral_mwq_decode", "olmoe_mixed_decode", "olmoe_edge_decode", "tiny")
 
 
 def roofline_of(r, ceilings):
