@@ -52,8 +52,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU oracle sample")
     ap.add_argument("--offload-slots", type=int, default=0,
-                    help="INT4 layers: keep the experts in pinned host memory with this many GPU slots "
+                    help="INT4 or nested-MWQ layers: keep the experts in pinned host memory with this many GPU slots "
                          "(a separate measurement; routing changes every step)")
+    ap.add_argument("--offload-tokens", type=int, default=0,
+                    help="with --offload-slots: tokens per step (0: the workload's batch)")
     ap.add_argument("--hbm-probe", action="store_true",
                     help="only time a plain 512 MiB device copy (achievable HBM rate; counter calibration)")
     return ap.parse_args()
@@ -96,6 +98,59 @@ def weight_bytes_per_expert(cfg, matrix):
     return N * K // 2 + N * (K // G) * 2
 
 
+def offload_bench_mwq(args, cfg):
+    """Nested-MWQ experts host-resident, loaded plane by plane in HEBF order
+    (hottest expert first, q2 -> d3 -> d4, up to the widest width its pairs
+    need); 16 seeded routings and width draws in turn.  Against the same with
+    every copy finished before any GEMM, and with every expert resident."""
+    import torch
+    import quantized_moe_expert_top_amd as q
+    from quantized_moe_expert_top_amd.offload import OffloadedMwqLayer
+    if args.offload_tokens:
+        cfg = gen.config(args.config, T=args.offload_tokens)
+    data = gen.generate(cfg)
+    gu, dn = tiled_weights(q, cfg, data)
+    x = to_dev(data["x"])
+    draws = [gen.generate(gen.config(args.config, T=cfg.T, seed=cfg.seed + 1000 + i)) for i in range(16)]
+    batches = [(to_dev(dd["logits"]), to_dev(dd["pair_bits"])) for dd in draws]
+    res = {}
+    for mode in ("overlap", "serial"):
+        layer = OffloadedMwqLayer(gu, dn, args.offload_slots)
+        hits = experts = copied = 0
+        t0 = 0.0
+        for i in range(args.warmup + args.steps):
+            if i == args.warmup:
+                torch.cuda.synchronize()
+                hits = experts = copied = 0
+                t0 = time.perf_counter()
+            lg, bits = batches[i % 16]
+            _, st = layer.forward(x, lg, cfg.k, bits, overlap=mode != "serial")
+            hits, experts, copied = hits + st.hits, experts + st.experts, copied + st.bytes_copied
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        res[mode] = dict(ms=dt / args.steps * 1e3, tps=cfg.T * args.steps / dt, hit=hits / max(experts, 1),
+                         mb=copied / args.steps / 1e6, gbs=copied / dt / 1e9)
+    for i in range(3):
+        q.moe_layer_forward(x, batches[i][0], cfg.k, gu, dn, pair_bits=batches[i][1])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        q.moe_layer_forward(x, batches[i % 16][0], cfg.k, gu, dn, pair_bits=batches[i % 16][1])
+    torch.cuda.synchronize()
+    resident_ms = (time.perf_counter() - t0) / args.steps * 1e3
+    o, n = res["overlap"], res["serial"]
+    print(json.dumps({
+        "metric": "routed-expert nested-MWQ layer tokens/s with experts in host memory (HEBF plane loading)",
+        "value": round(o["tps"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(o["ms"], 4), "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}_offload", "slots": args.offload_slots, "experts": cfg.E,
+                   "tokens": cfg.T, "top_k": cfg.k, "routings": 16},
+        "hit_rate": round(o["hit"], 3), "copied_mb_per_step": round(o["mb"], 2), "h2d_gbs": round(o["gbs"], 2),
+        "no_overlap": {"ms_per_step": round(n["ms"], 4), "tokens_s": round(n["tps"], 1), "h2d_gbs": round(n["gbs"], 2)},
+        "all_resident_ms_per_step": round(resident_ms, 4),
+    }))
+
+
 def offload_bench(args):
     """Experts host-resident, `--offload-slots` GPU slots, a new routing every step
     (16 seeded logit batches of the workload's distribution, in turn): tokens/s with the
@@ -105,8 +160,10 @@ def offload_bench(args):
     import quantized_moe_expert_top_amd as q
     from quantized_moe_expert_top_amd.offload import OffloadedMoeLayer
     cfg = gen.config(args.config)
+    if cfg.fmt == "mwq":
+        return offload_bench_mwq(args, cfg)
     if cfg.fmt != "int4":
-        print(json.dumps({"error": "--offload-slots takes an INT4 workload"}))
+        print(json.dumps({"error": "--offload-slots takes an INT4 or nested-MWQ workload"}))
         sys.exit(2)
     data = gen.generate(cfg)
     gu = q.moe_repack_weights(q.int4_experts(to_dev(data["gu_codes"]), to_dev(data["gu_scales"]), cfg.G))

@@ -259,6 +259,21 @@ size_t moe_weight_field_bytes(const moe_wdesc* w, int32_t field);
  */
 moe_status moe_repack_weights(const moe_wdesc* src, const moe_wdesc* dst, void* stream);
 
+/* --------------------------------------------------------- expert offload
+ * Plane-by-plane loading of host-resident experts (D2MoE page, Design,
+ * bit-width-aware I/O-compute pipeline and its HEBF order): in the tiled
+ * nested-MWQ layout the planes of an expert are interleaved per 1 KB tile
+ * block (q2 at bytes 0..511, d3 at 512..767, d4 at 768..1023), so one plane
+ * of one expert is `rows` pieces of `width` bytes, `pitch` bytes apart.
+ * Copies those pieces from `src` (pinned host memory) to `dst` (device
+ * memory), both laid out with the same pitch (pass pointers already offset
+ * to the plane), ordered on `stream` and asynchronous to the host.
+ * Errors, before anything is queued: MOE_ERR_NULL_ARG (NULL buffer with
+ * rows > 0), MOE_ERR_BAD_SHAPE (width > pitch).  MOE_ERR_HIP if the copy
+ * cannot be queued.  rows == 0 or width == 0: nothing to do.
+ */
+moe_status moe_copy_rows_async(void* dst, const void* src, size_t rows, size_t pitch, size_t width, void* stream);
+
 /* ---------------------------------------------------------- grouped GEMM
  * For every segment s of seg_offsets (E*S segments; S = 3 for MWQ, else 1)
  * and every row i in [seg_offsets[s], seg_offsets[s+1]):

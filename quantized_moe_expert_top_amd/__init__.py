@@ -30,7 +30,7 @@ EXPORTED = [
     "moe_status_string", "moe_last_error_detail", "moe_abi_version", "moe_route_topk",
     "moe_permute_workspace_size", "moe_permute", "moe_route_permute", "moe_weight_field_bytes", "moe_repack_weights",
     "moe_grouped_qgemm_workspace_size", "moe_grouped_qgemm", "moe_unpermute_combine",
-    "moe_grouped_qgemm_noalloc", "moe_grouped_qgemm_noalloc_scratch_bytes",
+    "moe_grouped_qgemm_noalloc", "moe_grouped_qgemm_noalloc_scratch_bytes", "moe_copy_rows_async",
 ]
 
 
@@ -74,6 +74,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_unpermute_combine": (i32, [vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]),
         "moe_grouped_qgemm_noalloc": (i32, [ctypes.POINTER(WDesc), vp, i32, vp, i32, vp, i32, i32, i32, vp, vp]),
         "moe_grouped_qgemm_noalloc_scratch_bytes": (sz, []),
+        "moe_copy_rows_async": (i32, [vp, vp, sz, sz, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -289,6 +290,21 @@ def moe_grouped_qgemm_noalloc(w: QuantizedExperts, A: torch.Tensor, seg_offsets:
                                            _ptr(seg_offsets), M_total, epilogue, kernel, _ptr(out),
                                            _stream(stream)), "moe_grouped_qgemm_noalloc")
     return out
+
+
+def moe_copy_rows_async(dst: torch.Tensor, dst_offset: int, src: torch.Tensor, src_offset: int, rows: int,
+                        pitch: int, width: int, stream=None) -> None:
+    """Queues `rows` pieces of `width` bytes, `pitch` bytes apart, from pinned
+    host tensor `src` (from byte src_offset) to device tensor `dst` (from byte
+    dst_offset) on `stream` (one plane of a tiled nested-MWQ expert)."""
+    if not src.is_pinned() or not dst.is_cuda:
+        raise ValueError("moe_copy_rows_async copies pinned host memory to device memory")
+    span = (rows - 1) * pitch + width if rows and width else 0
+    for t, off in ((src, src_offset), (dst, dst_offset)):
+        if off < 0 or off + span > t.numel() * t.element_size():
+            raise ValueError("copy range outside the tensor")
+    _check(lib().moe_copy_rows_async(dst.data_ptr() + dst_offset, src.data_ptr() + src_offset, rows, pitch, width,
+                                     _stream(stream)), "moe_copy_rows_async")
 
 
 def moe_unpermute_combine(y_perm: torch.Tensor, pair_pos: torch.Tensor, topk_w: Optional[torch.Tensor],

@@ -286,6 +286,13 @@ moe_status moe_repack_weights(const moe_wdesc* src, const moe_wdesc* dst, void* 
   return hip_status(moe::launch_repack(to_q(src), to_q(dst), stream), "repack launch");
 }
 
+moe_status moe_copy_rows_async(void* dst, const void* src, size_t rows, size_t pitch, size_t width, void* stream) {
+  if (rows == 0 || width == 0) return ok();
+  if (!dst || !src) return fail(MOE_ERR_NULL_ARG, "dst and src are required");
+  if (width > pitch) return fail(MOE_ERR_BAD_SHAPE, "width %zu > pitch %zu", width, pitch);
+  return hip_status(moe::rt_copy_rows_h2d(dst, src, rows, pitch, width, stream), "copy_rows");
+}
+
 size_t moe_grouped_qgemm_workspace_size(const moe_wdesc* w, int32_t A_rows, int32_t M_total, int32_t kernel) {
   if (check_desc(w, MOE_LAYOUT_TILED, false) != MOE_OK) return 0;
   if (A_rows < 0 || M_total < 0 || !moe::qgemm_kernel_supported(w->format, kernel)) return 0;

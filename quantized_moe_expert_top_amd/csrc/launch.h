@@ -20,6 +20,8 @@ int rt_device_arch(int dev, char* name, size_t n);
 // Returns and clears the calling thread's last HIP error (0 if none).
 int rt_take_error();
 const char* rt_error_string(int err);
+// rows pieces of width bytes, pitch bytes apart in both buffers, host (pinned) to device, on stream
+int rt_copy_rows_h2d(void* dst, const void* src, size_t rows, size_t pitch, size_t width, void* stream);
 
 // ---------------------------------------------------------------- routing
 int launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, void* stream);

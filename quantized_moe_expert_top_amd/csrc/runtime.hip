@@ -21,4 +21,9 @@ int rt_take_error() { return (int)hipGetLastError(); }
 
 const char* rt_error_string(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }
 
+int rt_copy_rows_h2d(void* dst, const void* src, size_t rows, size_t pitch, size_t width, void* stream) {
+  return (int)hipMemcpy2DAsync(dst, pitch, src, pitch, width, rows, hipMemcpyHostToDevice,
+                               static_cast<hipStream_t>(stream));
+}
+
 }  // namespace moe

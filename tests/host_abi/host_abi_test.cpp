@@ -120,6 +120,19 @@ int main() {
                               static_cast<const int32_t*>(fake(0x3000)), nullptr, 4, 2, 16,
                               static_cast<uint16_t*>(fake(0x4000)), nullptr) == MOE_OK);
 
+  // strided plane copies: argument checks before anything is queued, failures reported
+  CHECK(moe_copy_rows_async(fake(0x1000), fake(0x2000), 0, 1024, 512, nullptr) == MOE_OK);  // nothing to do
+  CHECK(stub::copies == 0);
+  CHECK(moe_copy_rows_async(nullptr, fake(0x2000), 4, 1024, 512, nullptr) == MOE_ERR_NULL_ARG);
+  CHECK(moe_copy_rows_async(fake(0x1000), fake(0x2000), 4, 256, 512, nullptr) == MOE_ERR_BAD_SHAPE);
+  CHECK(stub::copies == 0);
+  CHECK(moe_copy_rows_async(fake(0x1000), fake(0x2000), 4, 1024, 512, nullptr) == MOE_OK);
+  CHECK(stub::copies == 1);
+  stub::launch_error = 1;
+  CHECK(moe_copy_rows_async(fake(0x1000), fake(0x2000), 4, 1024, 512, nullptr) == MOE_ERR_HIP);
+  CHECK(strstr(moe_last_error_detail(), "copy_rows") != nullptr);
+  stub::launch_error = 0;
+
   // the current-device query fails: MOE_ERR_HIP before any launch
   stub::device_error = 100;
   const int launches2 = stub::launches;

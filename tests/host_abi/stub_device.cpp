@@ -14,6 +14,7 @@ int launches = 0;
 int taken = 0;
 const char* arch = "gfx950:sramecc+:xnack-";
 void* last_ws = nullptr;
+int copies = 0;
 }  // namespace stub
 
 namespace {
@@ -40,6 +41,10 @@ int rt_take_error() {
   return e;
 }
 const char* rt_error_string(int err) { return err ? "stub device error" : "no error"; }
+int rt_copy_rows_h2d(void*, const void*, size_t, size_t, size_t, void*) {
+  ++stub::copies;
+  return stub::launch_error;
+}
 
 int launch_route_topk(const float*, int, int, int, int32_t*, float*, void*) { return launched(); }
 int launch_permute(const PermuteArgs&, void*) { return launched(); }

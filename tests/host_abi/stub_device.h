@@ -8,4 +8,5 @@ extern int launches;       // launchers called so far
 extern int taken;          // pending-error queries so far
 extern const char* arch;   // architecture name the device reports
 extern void* last_ws;      // workspace the last grouped-GEMM launch received
+extern int copies;         // strided copies queued
 }  // namespace stub

@@ -154,3 +154,51 @@ def test_grouped_gemm_on_offset_slices(G):
                                G.q.MOE_EPI_NONE_F32)
     torch.cuda.synchronize()
     assert torch.equal(y[perm2.pair_pos.long()], y1[perm1.pair_pos.long()])
+
+
+# ------------------------------------------------------ nested MWQ planes, HEBF
+def _mwq_step_data(seed, bits=None):
+    c = gen.config("mixtral_mwq_decode", T=4, E=16, k=2, H=512, I=1024, seed=seed)
+    dd = gen.generate(c)
+    if bits is not None:
+        dd["pair_bits"][:] = bits
+    return dd
+
+
+@pytest.mark.parametrize("overlap", [True, False])
+def test_mwq_offload_hebf_steps_match_oracle(G, overlap):
+    """Plane-wise loading in HEBF order: every step meets the bar against the
+    oracle and agrees with the all-resident layer; hits, misses, evictions and
+    slots that only gain planes (a width-2 expert later asked for 4 bits)."""
+    from quantized_moe_expert_top_amd.offload import OffloadedMwqLayer
+    cfg = gen.config("mixtral_mwq_decode", T=4, E=16, k=2, H=512, I=1024, seed=131)
+    d = gen.generate(cfg)
+    gu, dn = G.tiled_layer(d, cfg)
+    layer = OffloadedMwqLayer(gu, dn, n_slots=8)
+    x = G.t(d["x"])
+    plane = {b: layer.gu.plane_bytes(b) + layer.dn.plane_bytes(b) for b in (2, 3, 4)}
+    plan = [(132, 2), (132, 4), (132, 3), (133, None), (134, None), (132, None), (135, 4)]
+    seen = set()
+    for step, (seed, bits) in enumerate(plan):
+        dd = _mwq_step_data(seed, bits)
+        print(f"[gpu] mwq offload step {step} seed {seed} bits {bits} overlap {overlap}", flush=True)
+        out, st = layer.forward(x, G.t(dd["logits"]), cfg.k, G.t(dd["pair_bits"]), overlap=overlap)
+        torch.cuda.synchronize()
+        d2 = dict(d)
+        d2["logits"], d2["pair_bits"] = dd["logits"], dd["pair_bits"]
+        ref = REF.moe_forward(d2, cfg)
+        got = G.bf16_to_np(out)
+        G.check_close(got, ref["out"], f"mwq offload step {step}")
+        res = G.q.moe_layer_forward(x, G.t(dd["logits"]), cfg.k, gu, dn, pair_bits=G.t(dd["pair_bits"]))
+        torch.cuda.synchronize()
+        assert oracle.compare(got, G.bf16_to_np(res.out))["rel_l2"] < 2e-3
+        touched = set(int(e) for e in np.unique(ref["ids"]))
+        assert st.experts == len(touched)
+        if step == 1:   # same routing, all pairs now 4 bits: every expert resident, d3 and d4 copied
+            assert st.hits == len(touched) and st.bytes_copied == len(touched) * (plane[3] + plane[4])
+        if step == 2:   # 3 bits: everything already there
+            assert st.hits == len(touched) and st.bytes_copied == 0
+        if step == 0:   # cold: q2 only
+            assert st.hits == 0 and st.bytes_copied == len(touched) * plane[2]
+        seen |= touched
+    assert len(seen) > layer.S   # the cache had to evict
