@@ -303,6 +303,9 @@ __device__ __forceinline__ int tab_bits(const NoTab&, int) { return 4; }
 __device__ __forceinline__ int tab_zero(const NoTab&, int) { return 0; }
 __device__ __forceinline__ size_t tab_off(const NoTab&, int) { return 0; }
 
+#ifndef QD_PF
+#define QD_PF 3  // K blocks of weights in flight per wavefront
+#endif
 template <int FMT, int EPI, int GPB>
 __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, int n_rt, int n_ks, int kb_per,
                                                            TabOf<FMT> tab) {
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
   constexpr bool FU = FMT == 4;                // all widths of an expert per tile
   constexpr bool FX = FMT == 5 || FMT == 6;    // one width per expert (6: the 8-bit experts, 5: the others)
   constexpr int SPG = 4 / GPB;                 // MFMA steps per scale group
-  constexpr int PF = 3, R = 4;                 // prefetch distance, ring size
+  constexpr int PF = QD_PF, R = QD_PF + 1;     // prefetch distance, ring size
   __shared__ u32x4 lds_a[3][4][64];            // [slot][step][lane], 12 KB
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = uniform(tid >> 6);
@@ -458,16 +461,12 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
     lds_a[0][wv][lane] = ra[0];
     int kb0 = 0;
     for (; kb0 + R + PF <= KB; kb0 += R) {
-      QD_STEP_U(0)
-      QD_STEP_U(1)
-      QD_STEP_U(2)
-      QD_STEP_U(3)
+#pragma unroll
+      for (int j_ = 0; j_ < R; ++j_) QD_STEP_U(j_)
     }
     for (; kb0 < KB; kb0 += R) {
-      QD_STEP(0)
-      QD_STEP(1)
-      QD_STEP(2)
-      QD_STEP(3)
+#pragma unroll
+      for (int j_ = 0; j_ < R; ++j_) QD_STEP(j_)
     }
   };
   if constexpr (FMT == 6) {
