@@ -212,9 +212,13 @@ moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t 
 #define MOE_EPI_NONE 0      /* out bf16 [M_total][N] */
 #define MOE_EPI_SWIGLU 1    /* N = 2*I; rows [0,I) gate, [I,2I) up; out = bf16(silu(gate) * up), width I */
 #define MOE_EPI_NONE_F32 2  /* out fp32 [M_total][N], not rounded (expert outputs feeding the combine) */
+#define MOE_EPI_NONE_F16 3  /* out fp16 [M_total][N], rounded to nearest even: expert outputs for the combine
+                               as 16-bit values (the FP16 pipeline of the D2MoE page), half the bytes of
+                               fp32 with 11 significant bits; magnitudes past 65504 become +-inf */
 
 #define MOE_DTYPE_BF16 0
 #define MOE_DTYPE_F32 1
+#define MOE_DTYPE_F16 2
 
 typedef struct moe_wdesc {
   int32_t abi_version;   /* MOE_ABI_VERSION */
@@ -282,11 +286,12 @@ moe_status moe_copy_rows_async(void* dst, const void* src, size_t rows, size_t p
  *     y_i = a_i W_e^T  with W_e dequantised from the format, e = s / S
  *           (MWQ: bit-width b = 4 - s % 3 for all of W_e)
  *           (DELTA2: y_i = a_i W_base^T + a_i D_e^T if base != NULL)
- *     out[i] = y_i                       (MOE_EPI_NONE: bf16, MOE_EPI_NONE_F32: fp32, width N)
+ *     out[i] = y_i                       (MOE_EPI_NONE: bf16, MOE_EPI_NONE_F32: fp32,
+ *                                         MOE_EPI_NONE_F16: fp16, width N)
  *     out[i] = silu(y_i[:I]) * y_i[I:]   (MOE_EPI_SWIGLU: bf16, width I = N/2)
  * Dequantisation is exact: codes become exact 16-bit values, products are
  * accumulated in fp32 and the group / channel scales are applied in fp32;
- * a bf16 out is rounded once (pipeline equation of the D2MoE page:
+ * a 16-bit out is rounded once (pipeline equation of the D2MoE page:
  * dequantise, then a 16-bit GEMM; the SwiGLU output is the 16-bit
  * activation of the next GEMM).
  *
@@ -345,8 +350,8 @@ moe_status moe_grouped_qgemm_noalloc(const moe_wdesc* w, const uint16_t* A, int3
  * out[t] = sum_{j<k} w[t][j] * y_perm[pair_pos[t*k + j]], accumulated in fp32
  * in slot order j = 0..k-1 and rounded once to bf16 (gate-weighted combine of
  * the selected experts' outputs).
- *   y_perm   [T*k][H] (grouped order) of y_dtype (MOE_DTYPE_BF16 or
- *            MOE_DTYPE_F32), 16-byte aligned, H % 8 == 0
+ *   y_perm   [T*k][H] (grouped order) of y_dtype (MOE_DTYPE_BF16,
+ *            MOE_DTYPE_F32 or MOE_DTYPE_F16), 16-byte aligned, H % 8 == 0
  *   pair_pos i32 [T*k]
  *   n_valid  device i32 [1], or NULL: the number of rows the GEMMs wrote
  *            (seg_offsets[E*S] of the grouping).  A pair whose pair_pos is at

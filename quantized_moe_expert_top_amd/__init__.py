@@ -19,8 +19,11 @@ LIB_PATH = os.path.join(_HERE, "libmoe_qexpert.so")
 MOE_ABI_VERSION = 3
 MOE_W_INT4_GROUP, MOE_W_MWQ_2_3_4, MOE_W_DELTA2_SALIENT, MOE_W_INT_PER_EXPERT = 1, 2, 3, 4
 MOE_LAYOUT_CANONICAL, MOE_LAYOUT_TILED = 0, 1
-MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_NONE_F32 = 0, 1, 2
-MOE_DTYPE_BF16, MOE_DTYPE_F32 = 0, 1
+MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_NONE_F32, MOE_EPI_NONE_F16 = 0, 1, 2, 3
+MOE_DTYPE_BF16, MOE_DTYPE_F32, MOE_DTYPE_F16 = 0, 1, 2
+# plain-epilogue output dtype of each epilogue, and the epilogue that writes a dtype
+_EPI_DTYPE = {MOE_EPI_NONE_F32: torch.float32, MOE_EPI_NONE_F16: torch.float16}
+_DTYPE_EPI = {torch.float32: MOE_EPI_NONE_F32, torch.float16: MOE_EPI_NONE_F16, torch.bfloat16: MOE_EPI_NONE}
 (MOE_KERNEL_AUTO, MOE_KERNEL_SMALL, MOE_KERNEL_SMALL_PER_WIDTH, MOE_KERNEL_TILE64_WIDE, MOE_KERNEL_TILE64,
  MOE_KERNEL_TILE128, MOE_KERNEL_LDS_DMA, MOE_KERNEL_LDS_DMA_PER_WIDTH) = range(8)
 (MOE_FIELD_CODES, MOE_FIELD_PLANE3, MOE_FIELD_PLANE4, MOE_FIELD_SCALES,
@@ -262,7 +265,7 @@ def moe_grouped_qgemm(w: QuantizedExperts, A: torch.Tensor, seg_offsets: torch.T
     A_rows = A.shape[0]
     n_out = w.N // 2 if epilogue == MOE_EPI_SWIGLU else w.N
     if out is None:
-        dt = torch.float32 if epilogue == MOE_EPI_NONE_F32 else torch.bfloat16
+        dt = _EPI_DTYPE.get(epilogue, torch.bfloat16)
         out = torch.empty((M_total, n_out), dtype=dt, device=A.device)
     ws_need = moe_grouped_qgemm_workspace_size(w, A_rows, M_total, kernel)
     if workspace is None and ws_need:
@@ -284,7 +287,7 @@ def moe_grouped_qgemm_noalloc(w: QuantizedExperts, A: torch.Tensor, seg_offsets:
     _bf16(A)
     n_out = w.N // 2 if epilogue == MOE_EPI_SWIGLU else w.N
     if out is None:
-        dt = torch.float32 if epilogue == MOE_EPI_NONE_F32 else torch.bfloat16
+        dt = _EPI_DTYPE.get(epilogue, torch.bfloat16)
         out = torch.empty((M_total, n_out), dtype=dt, device=A.device)
     _check(lib().moe_grouped_qgemm_noalloc(ctypes.byref(w.desc), _ptr(A), A.shape[0], _ptr(gather_pair), k,
                                            _ptr(seg_offsets), M_total, epilogue, kernel, _ptr(out),
@@ -312,7 +315,7 @@ def moe_unpermute_combine(y_perm: torch.Tensor, pair_pos: torch.Tensor, topk_w: 
                           n_valid: torch.Tensor = None) -> torch.Tensor:
     """y_perm: fp32 or 16-bit (bf16 bit pattern) rows in grouped order.  n_valid: optional
     one-element int32 device tensor (e.g. seg_offsets[-1:]); pairs at or past it add nothing."""
-    y_dtype = MOE_DTYPE_F32 if y_perm.dtype == torch.float32 else MOE_DTYPE_BF16
+    y_dtype = {torch.float32: MOE_DTYPE_F32, torch.float16: MOE_DTYPE_F16}.get(y_perm.dtype, MOE_DTYPE_BF16)
     if y_dtype == MOE_DTYPE_BF16:
         _bf16(y_perm)
     H = y_perm.shape[1]
@@ -369,7 +372,12 @@ class LayerBuffers:
     out: torch.Tensor
 
 
-def alloc_layer(T: int, E: int, k: int, H: int, I: int, mwq: bool, device) -> LayerBuffers:
+def alloc_layer(T: int, E: int, k: int, H: int, I: int, mwq: bool, device,
+                y_dtype: torch.dtype = torch.float16) -> LayerBuffers:
+    """y_dtype: the experts' outputs before the combine: float16 (default),
+    float32 or bfloat16."""
+    if y_dtype not in _DTYPE_EPI:
+        raise ValueError(f"expert outputs in {y_dtype}: float16, float32 or bfloat16")
     S = 3 if mwq else 1
     ws = lib().moe_permute_workspace_size(T, k, E, S)
     perm = Permutation(
@@ -383,14 +391,15 @@ def alloc_layer(T: int, E: int, k: int, H: int, I: int, mwq: bool, device) -> La
         w=torch.empty((T, k), dtype=torch.float32, device=device),
         perm=perm,
         h=torch.empty((T * k, I), dtype=torch.bfloat16, device=device),
-        y_perm=torch.empty((T * k, H), dtype=torch.float32, device=device),
+        y_perm=torch.empty((T * k, H), dtype=y_dtype, device=device),
         out=torch.empty((T, H), dtype=torch.bfloat16, device=device))
 
 
 def moe_layer_forward(x: torch.Tensor, logits: torch.Tensor, k: int, gate_up: QuantizedExperts,
                       down: QuantizedExperts, pair_bits: torch.Tensor = None,
                       buf: LayerBuffers = None, stream=None, kernel: int = MOE_KERNEL_AUTO) -> LayerBuffers:
-    """Route -> group -> gate_up (+SwiGLU, bf16 h) -> down (fp32 expert outputs) -> combine, one stream.
+    """Route -> group -> gate_up (+SwiGLU, bf16 h) -> down (expert outputs in buf.y_perm's dtype: fp16
+    unless the buffers were allocated otherwise) -> combine, one stream.
     kernel: the grouped GEMMs' kernel choice (MOE_KERNEL_*; AUTO chooses from the shapes)."""
     T, H = x.shape
     E = logits.shape[1]
@@ -400,7 +409,7 @@ def moe_layer_forward(x: torch.Tensor, logits: torch.Tensor, k: int, gate_up: Qu
     moe_route_permute(logits, k, pair_bits=pair_bits, ids=buf.ids, w=buf.w, out=buf.perm, stream=stream)
     moe_grouped_qgemm(gate_up, x, buf.perm.seg_offsets, T * k, MOE_EPI_SWIGLU, gather_pair=buf.perm.sorted_pair,
                       k=k, out=buf.h, stream=stream, kernel=kernel)
-    moe_grouped_qgemm(down, buf.h, buf.perm.seg_offsets, T * k, MOE_EPI_NONE_F32, out=buf.y_perm, stream=stream,
+    moe_grouped_qgemm(down, buf.h, buf.perm.seg_offsets, T * k, _DTYPE_EPI[buf.y_perm.dtype], out=buf.y_perm, stream=stream,
                       kernel=kernel)
     moe_unpermute_combine(buf.y_perm, buf.perm.pair_pos, buf.w, T, k, out=buf.out, stream=stream,
                           n_valid=buf.perm.seg_offsets[-1:])

@@ -311,7 +311,8 @@ moe_status check_qgemm(const moe_wdesc* w, const uint16_t* A, int32_t A_rows, co
   moe_status st = check_desc(w, MOE_LAYOUT_TILED, true);
   if (st != MOE_OK) return st;
   if (M_total < 0 || A_rows < 0) return fail(MOE_ERR_BAD_SHAPE, "M_total=%d A_rows=%d", M_total, A_rows);
-  if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SWIGLU && epilogue != MOE_EPI_NONE_F32)
+  if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SWIGLU && epilogue != MOE_EPI_NONE_F32 &&
+      epilogue != MOE_EPI_NONE_F16)
     return fail(MOE_ERR_BAD_FORMAT, "unknown epilogue %d", epilogue);
   if (kernel < MOE_KERNEL_AUTO || kernel > MOE_KERNEL_LDS_DMA_PER_WIDTH)
     return fail(MOE_ERR_BAD_FORMAT, "unknown kernel choice %d", kernel);
@@ -388,7 +389,8 @@ size_t moe_grouped_qgemm_noalloc_scratch_bytes(void) { return moe::kStaticScratc
 moe_status moe_unpermute_combine(const void* y_perm, int32_t y_dtype, const int32_t* pair_pos,
                                  const int32_t* n_valid, const float* topk_w, int32_t T, int32_t k, int32_t H,
                                  uint16_t* out, void* stream) {
-  if (y_dtype != MOE_DTYPE_BF16 && y_dtype != MOE_DTYPE_F32) return fail(MOE_ERR_BAD_FORMAT, "y_dtype %d", y_dtype);
+  if (y_dtype != MOE_DTYPE_BF16 && y_dtype != MOE_DTYPE_F32 && y_dtype != MOE_DTYPE_F16)
+    return fail(MOE_ERR_BAD_FORMAT, "y_dtype %d", y_dtype);
   if (T < 0 || k < 1 || H < 8 || H % 8 != 0)
     return fail(MOE_ERR_BAD_SHAPE, "T=%d k=%d H=%d (H must be a positive multiple of 8)", T, k, H);
   if ((int64_t)T * k >= ((int64_t)1 << 31)) return fail(MOE_ERR_BAD_SHAPE, "T*k too large");
@@ -398,7 +400,7 @@ moe_status moe_unpermute_combine(const void* y_perm, int32_t y_dtype, const int3
   if (n_valid && !aligned(n_valid, 4)) return fail(MOE_ERR_MISALIGNED, "n_valid must be 4-byte aligned");
   moe_status st = check_device();
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_combine(y_perm, y_dtype == MOE_DTYPE_F32, pair_pos, n_valid, topk_w, T, k, H, out,
+  return hip_status(moe::launch_combine(y_perm, y_dtype, pair_pos, n_valid, topk_w, T, k, H, out,
                                         stream),
                     "combine launch");
 }

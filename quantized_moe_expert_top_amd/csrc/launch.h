@@ -52,7 +52,8 @@ int launch_route_permute(const float* logits, int T, int E, int k, const uint8_t
                          void* stream);
 
 // ---------------------------------------------------------------- combine
-int launch_combine(const void* y, bool y_f32, const int32_t* pos, const int32_t* n_valid, const float* w, int T,
+// y_dtype: MOE_DTYPE_BF16, MOE_DTYPE_F32 or MOE_DTYPE_F16 (validated by the caller)
+int launch_combine(const void* y, int y_dtype, const int32_t* pos, const int32_t* n_valid, const float* w, int T,
                    int k, int H, uint16_t* out, void* stream);
 
 // ---------------------------------------------------------- grouped GEMM

@@ -121,7 +121,7 @@ size_t ws_need(const QWeights& w, int path, int epi, int A_rows, int M_total) {
 size_t qgemm_workspace_bytes(const QWeights& w, int A_rows, int M_total, int kernel) {
   const int nseg = w.E * (w.fmt == 2 ? 3 : 1);
   size_t need = 0;
-  for (int epi = 0; epi < 3; ++epi) {
+  for (int epi = 0; epi < 4; ++epi) {
     const size_t n = ws_need(w, pick_path(w, M_total, nseg, epi, kernel), epi, A_rows, M_total);
     need = n > need ? n : need;
   }

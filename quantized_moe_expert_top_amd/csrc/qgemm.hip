@@ -65,6 +65,24 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Plain epilogues: EPI 0 bf16, 2 fp32, 3 fp16 (EPI 1, SwiGLU, stores bf16 h).
+// A 16-bit output is the fp32 result rounded once.  For fp16 the value passes
+// an empty register barrier first (no instruction is emitted): otherwise the
+// compiler may contract the conversion into the producing fma as a
+// mixed-precision fma that rounds the exact sum straight to fp16, and the fp16
+// output would no longer be the fp32 output rounded.
+template <int EPI>
+__device__ __forceinline__ void store_plain(void* out, size_t i, float v) {
+  if (EPI == 2) {
+    static_cast<float*>(out)[i] = v;
+  } else if (EPI == 3) {
+    asm volatile("" : "+v"(v));
+    static_cast<uint16_t*>(out)[i] = f32_to_f16(v);
+  } else {
+    static_cast<uint16_t*>(out)[i] = f32_to_bf16(v);
+  }
+}
+
 // Locate the row tile `y` (in segment order; tiles of `rows_per_tile` rows)
 // -> segment and first row.
 // With `stride` > 1, segment s spans seg_offsets[s*stride] .. seg_offsets[(s+1)*stride]
@@ -188,7 +206,7 @@ __device__ __forceinline__ bool wave_tiles(const KArgs& p, int wv, int& ct0, int
   return ch < p.N;
 }
 
-// EPI: 0 = bf16 out, 1 = SwiGLU bf16 out, 2 = fp32 out.  acc[rt][tile].
+// EPI: 0 = bf16 out, 1 = SwiGLU bf16 out, 2 = fp32 out, 3 = fp16 out.  acc[rt][tile].
 template <int EPI>
 __device__ __forceinline__ void store_tiles(const KArgs& p, const Ctx& c, const f32x4 (&acc)[2][2], int ct0,
                                             int ct1, bool v1, int hch, bool two) {
@@ -202,18 +220,12 @@ __device__ __forceinline__ void store_tiles(const KArgs& p, const Ctx& c, const 
       const int row = rt * 16 + 4 * (lane >> 4) + r;
       if (row >= c.rows) continue;
       const float v0 = acc[rt][0][r], vv1 = acc[rt][1][r];
-      if (EPI == 2) {
-        float* orow = static_cast<float*>(p.out) + (size_t)(c.row0 + row) * p.n_out;
-        orow[ct0 * 16 + col] = v0;
-        if (v1) orow[ct1 * 16 + col] = vv1;
+      const size_t o = (size_t)(c.row0 + row) * p.n_out;
+      if (EPI == 1) {
+        static_cast<uint16_t*>(p.out)[o + hch + col] = f32_to_bf16(v0 * __builtin_amdgcn_rcpf(1.0f + __expf(-v0)) * vv1);
       } else {
-        uint16_t* orow = static_cast<uint16_t*>(p.out) + (size_t)(c.row0 + row) * p.n_out;
-        if (EPI == 1) {
-          orow[hch + col] = f32_to_bf16(v0 * __builtin_amdgcn_rcpf(1.0f + __expf(-v0)) * vv1);
-        } else {
-          orow[ct0 * 16 + col] = f32_to_bf16(v0);
-          if (v1) orow[ct1 * 16 + col] = f32_to_bf16(vv1);
-        }
+        store_plain<EPI>(p.out, o + ct0 * 16 + col, v0);
+        if (v1) store_plain<EPI>(p.out, o + ct1 * 16 + col, vv1);
       }
     }
   }
@@ -504,19 +516,13 @@ __global__ __launch_bounds__(kThreads) void qgemm_d_kernel(KArgs p, int n_cg, in
   for (int r = 0; r < 4; ++r) {
     const int row = 4 * (lane >> 4) + r;
     if (row >= c.rows) continue;
-    if (EPI == 2) {
-      float* orow = static_cast<float*>(p.out) + (size_t)(c.row0 + row) * p.n_out;
-      orow[ct0 * 16 + col] = acc[0][r];
-      if (v1) orow[ct1 * 16 + col] = acc[1][r];
+    const size_t o = (size_t)(c.row0 + row) * p.n_out;
+    if (EPI == 1) {
+      const float g = acc[0][r];
+      static_cast<uint16_t*>(p.out)[o + hch + col] = f32_to_bf16(g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * acc[1][r]);
     } else {
-      uint16_t* orow = static_cast<uint16_t*>(p.out) + (size_t)(c.row0 + row) * p.n_out;
-      if (EPI == 1) {
-        const float g = acc[0][r];
-        orow[hch + col] = f32_to_bf16(g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * acc[1][r]);
-      } else {
-        orow[ct0 * 16 + col] = f32_to_bf16(acc[0][r]);
-        if (v1) orow[ct1 * 16 + col] = f32_to_bf16(acc[1][r]);
-      }
+      store_plain<EPI>(p.out, o + ct0 * 16 + col, acc[0][r]);
+      if (v1) store_plain<EPI>(p.out, o + ct1 * 16 + col, acc[1][r]);
     }
   }
 }
@@ -887,8 +893,7 @@ __global__ __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) void qgemm_p_kernel(KA
         for (int u = 0; u < UT; ++u) {
           if (!(u ? cv1 : cv)) continue;
           const size_t o = (size_t)(row0 + row) * p.n_out + ct[u] * 16 + col;
-          if (EPI == 2) static_cast<float*>(p.out)[o] = acc[rt][u][r];
-          else static_cast<uint16_t*>(p.out)[o] = f32_to_bf16(acc[rt][u][r]);
+          store_plain<EPI>(p.out, o, acc[rt][u][r]);
         }
       }
     }
@@ -1397,8 +1402,7 @@ __device__ __forceinline__ void qgemm_p2_body(const KArgs& p, const float* __res
         for (int u = 0; u < UT; ++u) {
           if (!cval[u]) continue;
           const size_t oi = (size_t)(row0 + row) * p.n_out + ct[u] * 16 + col;
-          if (EPI == 2) static_cast<float*>(p.out)[oi] = acc[rt][u][r];
-          else static_cast<uint16_t*>(p.out)[oi] = f32_to_bf16(acc[rt][u][r]);
+          store_plain<EPI>(p.out, oi, acc[rt][u][r]);
         }
       }
     }
@@ -1644,8 +1648,7 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2d_kernel(KArgs p, const fl
         if (!cval[u]) continue;
         const float y = __builtin_fmaf(step[u], accd[rt][u][r], accb[rt][u][r]);
         const size_t o = (size_t)(c.row0 + row) * p.n_out + ct[u] * 16 + col;
-        if (EPI == 2) static_cast<float*>(p.out)[o] = y;
-        else static_cast<uint16_t*>(p.out)[o] = f32_to_bf16(y);
+        store_plain<EPI>(p.out, o, y);
       }
     }
   }
@@ -1653,8 +1656,8 @@ __global__ __launch_bounds__(kP2Threads) void qgemm_p2d_kernel(KArgs p, const fl
 
 // out[row] = sum over ks = 0..n_ks-1 of part[ks][row], in that order, for the
 // rows the segments hold, [seg_offsets[0], seg_offsets[nseg]) (a caller may
-// pass a slice of a longer offset table whose first entry is not zero); fp32
-// or bf16 out.  One thread per 4 outputs; the grid covers M_total rows.
+// pass a slice of a longer offset table whose first entry is not zero); fp32,
+// bf16 or fp16 out.  One thread per 4 outputs; the grid covers M_total rows.
 template <int EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int n_ks, int M_total,
                                                             int N, const int32_t* __restrict__ seg_offsets, int nseg,
@@ -1668,11 +1671,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   if (EPI == 2) {
     reinterpret_cast<f32x4*>(out)[i4] = v;
   } else {
-    uint16_t* o = static_cast<uint16_t*>(out) + i4 * 4;
-    o[0] = f32_to_bf16(v[0]);
-    o[1] = f32_to_bf16(v[1]);
-    o[2] = f32_to_bf16(v[2]);
-    o[3] = f32_to_bf16(v[3]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) store_plain<EPI>(out, i4 * 4 + q, v[q]);
   }
 }
 
@@ -1914,6 +1914,7 @@ int launch_qgemm(const QGemmArgs& a, void* stream) {
   const XTab& t = w.fmt == 4 ? tab : kNoTab;
   if (a.epilogue == 1) launch_epi<1>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, t, s);
   else if (a.epilogue == 2) launch_epi<2>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, t, s);
+  else if (a.epilogue == 3) launch_epi<3>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, t, s);
   else launch_epi<0>(ka, w.fmt, path, a.M_total, a.A_rows, a.ws, t, s);
   return (int)hipGetLastError();
 }

@@ -31,7 +31,7 @@ import torch
 
 import numpy as np
 
-from . import (MOE_EPI_NONE_F32, MOE_EPI_SWIGLU, MOE_LAYOUT_TILED, MOE_W_INT4_GROUP, MOE_W_MWQ_2_3_4,
+from . import (MOE_EPI_NONE_F16, MOE_EPI_SWIGLU, MOE_LAYOUT_TILED, MOE_W_INT4_GROUP, MOE_W_MWQ_2_3_4,
                QuantizedExperts, make_desc, moe_copy_rows_async, moe_grouped_qgemm, moe_permute, moe_route_topk,
                moe_unpermute_combine)
 
@@ -164,7 +164,7 @@ class OffloadedMoeLayer(_SlotCache):
                 compute.wait_event(ev)
         self._current = set(hot)
         h = torch.empty((P, self.I), dtype=torch.bfloat16, device=x.device)
-        y = torch.empty((P, self.H), dtype=torch.float32, device=x.device)
+        y = torch.empty((P, self.H), dtype=torch.float16, device=x.device)
         for phase in (0, 1):
             if phase == 1:
                 if not misses:
@@ -172,7 +172,7 @@ class OffloadedMoeLayer(_SlotCache):
                 compute.wait_event(done)
             seg = perm.seg_offsets[phase * S:phase * S + S + 1]  # rows of this phase's slots
             moe_grouped_qgemm(self.gu.view, x, seg, P, MOE_EPI_SWIGLU, gather_pair=perm.sorted_pair, k=k, out=h)
-            moe_grouped_qgemm(self.dn.view, h, seg, P, MOE_EPI_NONE_F32, out=y)
+            moe_grouped_qgemm(self.dn.view, h, seg, P, MOE_EPI_NONE_F16, out=y)
         out = moe_unpermute_combine(y, perm.pair_pos, w, T, k)
         return out, stats
 
@@ -326,7 +326,7 @@ class OffloadedMwqLayer(_SlotCache):
             self.planes_in[s] = max(self.planes_in[s], int(need[e]))
         rows = np.bincount(key // (3 * S), minlength=n_phase)
         h = torch.empty((P, self.I), dtype=torch.bfloat16, device=x.device)
-        y = torch.empty((P, self.H), dtype=torch.float32, device=x.device)
+        y = torch.empty((P, self.H), dtype=torch.float16, device=x.device)
         for ph in range(n_phase):
             if rows[ph] == 0:
                 continue
@@ -334,6 +334,6 @@ class OffloadedMwqLayer(_SlotCache):
                 compute.wait_event(landed[ph - 1])
             seg = perm.seg_offsets[3 * S * ph:3 * S * (ph + 1) + 1]
             moe_grouped_qgemm(self.gu.view, x, seg, P, MOE_EPI_SWIGLU, gather_pair=perm.sorted_pair, k=k, out=h)
-            moe_grouped_qgemm(self.dn.view, h, seg, P, MOE_EPI_NONE_F32, out=y)
+            moe_grouped_qgemm(self.dn.view, h, seg, P, MOE_EPI_NONE_F16, out=y)
         out = moe_unpermute_combine(y, perm.pair_pos, w, T, k)
         return out, stats

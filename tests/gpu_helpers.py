@@ -24,8 +24,8 @@ def t(a, dtype=None):
 
 
 def bf16_to_np(x: torch.Tensor) -> np.ndarray:
-    """bf16 (or already fp32) device tensor -> float64 numpy."""
-    if x.dtype == torch.float32:
+    """bf16 (or fp32 / fp16) device tensor -> float64 numpy."""
+    if x.dtype in (torch.float32, torch.float16):
         return x.cpu().numpy().astype(np.float64)
     return x.view(torch.bfloat16).float().cpu().numpy().astype(np.float64)
 

@@ -52,7 +52,7 @@ int launch_route_permute(const float*, int, int, int, const uint8_t*, int32_t*, 
                          int32_t*, void*, void*) {
   return launched();
 }
-int launch_combine(const void*, bool, const int32_t*, const int32_t*, const float*, int, int, int, uint16_t*, void*) {
+int launch_combine(const void*, int, const int32_t*, const int32_t*, const float*, int, int, int, uint16_t*, void*) {
   return launched();
 }
 int launch_qgemm(const QGemmArgs& a, void*) {

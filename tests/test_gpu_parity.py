@@ -323,19 +323,64 @@ def test_layer_mwq_decode_widths(G, bits):
 ])
 def test_decode_split_k(G, name, over):
     """A decode batch's down projection with long K and few work items runs as
-    K splits whose fp32 partial sums are added in order; the plain bf16
-    epilogue through the same split is the fp32 result rounded once."""
+    K splits whose fp32 partial sums are added in order; the 16-bit plain
+    epilogues through the same split are the fp32 result rounded once."""
     cfg = gen.config(name, **over)
     d = gen.generate(cfg)
     gu, dn = G.tiled_layer(d, cfg)
     buf = G.run_layer(d, cfg, gu, dn)
     ref = REF.moe_forward(d, cfg)
     assert np.array_equal(buf.perm.seg_offsets.cpu().numpy(), ref["seg_offsets"])
-    assert oracle.compare(buf.y_perm.cpu().numpy(), ref["y_perm_h16"])["rel_l2"] < 1e-2
+    assert oracle.compare(G.bf16_to_np(buf.y_perm), ref["y_perm_h16"])["rel_l2"] < 1e-2
     G.check_close(G.bf16_to_np(buf.out), ref["out"], name)
-    y16 = G.q.moe_grouped_qgemm(dn, buf.h, buf.perm.seg_offsets, cfg.T * cfg.k, G.q.MOE_EPI_NONE)
+    M = cfg.T * cfg.k
+    y32 = G.q.moe_grouped_qgemm(dn, buf.h, buf.perm.seg_offsets, M, G.q.MOE_EPI_NONE_F32)
+    y16 = G.q.moe_grouped_qgemm(dn, buf.h, buf.perm.seg_offsets, M, G.q.MOE_EPI_NONE)
     torch.cuda.synchronize()
-    assert torch.equal(y16, buf.y_perm.to(torch.bfloat16))
+    assert torch.equal(y16, y32.to(torch.bfloat16))
+    assert torch.equal(buf.y_perm, y32.to(torch.float16))
+
+
+def _plain_epilogues(G, w, A, seg, M, kernel, **kw):
+    """The same GEMM with fp32, fp16 and bf16 plain epilogues: each 16-bit
+    output is the fp32 one rounded once (to nearest even)."""
+    y32 = G.q.moe_grouped_qgemm(w, A, seg, M, G.q.MOE_EPI_NONE_F32, kernel=kernel, **kw)
+    yh = G.q.moe_grouped_qgemm(w, A, seg, M, G.q.MOE_EPI_NONE_F16, kernel=kernel, **kw)
+    yb = G.q.moe_grouped_qgemm(w, A, seg, M, G.q.MOE_EPI_NONE, kernel=kernel, **kw)
+    torch.cuda.synchronize()
+    assert yh.dtype == torch.float16 and torch.equal(yh, y32.to(torch.float16)), kernel
+    assert torch.equal(yb.view(torch.bfloat16), y32.to(torch.bfloat16)), kernel
+
+
+@pytest.mark.parametrize("fmt,kernels", [
+    ("int4", ["SMALL", "TILE64_WIDE", "TILE64", "TILE128", "LDS_DMA"]),
+    ("mwq", ["SMALL", "SMALL_PER_WIDTH", "TILE64", "LDS_DMA", "LDS_DMA_PER_WIDTH"]),
+    ("mixed", ["SMALL"]),
+    ("edge", ["SMALL"]),  # 8-bit experts: a decode launch of their own
+])
+def test_plain_epilogue_dtypes(G, fmt, kernels):
+    """fp16 expert outputs (the layer's default) on every kernel of every
+    format: bit for bit the fp32 outputs rounded once, like bf16."""
+    name = {"int4": "tiny", "mwq": "mixtral_mwq", "mixed": "olmoe_mixed_decode", "edge": "olmoe_edge_decode"}[fmt]
+    cfg = gen.config(name, T=150, E=4, k=2, H=256, I=512, seed=91)
+    d = gen.generate(cfg)
+    gu, dn = G.tiled_layer(d, cfg)
+    buf = G.run_layer(d, cfg, gu, dn)
+    M = cfg.T * cfg.k
+    for kn in kernels:
+        _plain_epilogues(G, dn, buf.h, buf.perm.seg_offsets, M, getattr(G.q, "MOE_KERNEL_" + kn))
+        _plain_epilogues(G, gu, G.t(d["x"]), buf.perm.seg_offsets, M, getattr(G.q, "MOE_KERNEL_" + kn),
+                         gather_pair=buf.perm.sorted_pair, k=cfg.k)
+
+
+@pytest.mark.parametrize("kernel", ["SMALL", "LDS_DMA"])
+def test_plain_epilogue_dtypes_delta(G, kernel):
+    cfg = gen.config("meswitch_delta", requests=20, tokens_per_request=16, K=512, N=256, E=3, n_salient=5, seed=92)
+    d = gen.generate(cfg)
+    w = G.delta_layer(d, cfg)
+    perm = G.q.moe_permute(G.t(d["ids"]).view(cfg.T, 1), cfg.E)
+    _plain_epilogues(G, w, G.t(d["x"]), perm.seg_offsets, cfg.T, getattr(G.q, "MOE_KERNEL_" + kernel),
+                     gather_pair=perm.sorted_pair, k=1)
 
 
 # ------------------------------------------- static bit-width per expert
