@@ -230,20 +230,31 @@ __global__ __launch_bounds__(kThreads) void permute_count_kernel(Keyer kr, int P
   if (tid == 0) chunk_flag[blockIdx.x] = sbad;
 }
 
+// Per key, the exclusive scan over chunks, then over keys; chunk_hist[b][key]
+// becomes the output position of chunk b's first pair with that key.  When
+// the chunk histograms fit (kScanLds ints) they are read once, coalesced, into
+// LDS, scanned there and written back once; otherwise each key walks its
+// chunks in global memory (a chain of dependent round trips).
+constexpr int kScanLds = 8192;
 __global__ __launch_bounds__(kThreads) void permute_scan_kernel(Keyer kr, int nb, int* chunk_hist,
                                                                 const uint32_t* chunk_flag, int32_t* counts,
                                                                 int32_t* seg_offsets, uint32_t* flag) {
   __shared__ int total[kMaxKeys];
+  __shared__ int sh[kScanLds];
   __shared__ int scratch[8];
   __shared__ uint32_t sbad;
   const int tid = threadIdx.x;
   const int nk1 = kr.NK + 1;
+  const int n = nb * nk1;
+  const bool in_lds = n <= kScanLds;
   if (tid == 0) sbad = 0;
+  if (in_lds)
+    for (int i = tid; i < n; i += kThreads) sh[i] = chunk_hist[i];
   __syncthreads();
   for (int key = tid; key < nk1; key += kThreads) {
     int run = 0;
     for (int b = 0; b < nb; ++b) {
-      int* h = chunk_hist + (size_t)b * nk1 + key;
+      int* h = in_lds ? sh + b * nk1 + key : chunk_hist + (size_t)b * nk1 + key;
       const int t = *h;
       *h = run;
       run += t;
@@ -262,9 +273,13 @@ __global__ __launch_bounds__(kThreads) void permute_scan_kernel(Keyer kr, int nb
   __syncthreads();
   block_exclusive_scan<kThreads>(total, nk1, scratch);
   for (int i = tid; i < nk1; i += kThreads) seg_offsets[i] = total[i];
-  for (int key = tid; key < nk1; key += kThreads) {
-    const int base = total[key];
-    for (int b = 0; b < nb; ++b) chunk_hist[(size_t)b * nk1 + key] += base;
+  if (in_lds) {
+    for (int i = tid; i < n; i += kThreads) chunk_hist[i] = sh[i] + total[i % nk1];
+  } else {
+    for (int key = tid; key < nk1; key += kThreads) {
+      const int base = total[key];
+      for (int b = 0; b < nb; ++b) chunk_hist[(size_t)b * nk1 + key] += base;
+    }
   }
   if (tid == 0) flag[0] = sbad;
 }
