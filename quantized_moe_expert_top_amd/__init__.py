@@ -252,6 +252,15 @@ def moe_repack_weights(src: QuantizedExperts, stream=None) -> QuantizedExperts:
     return dst
 
 
+def _check_segments(w: QuantizedExperts, seg_offsets: torch.Tensor) -> None:
+    """The GEMM reads E*S + 1 offsets (S = 3 for nested planes, else 1): a shorter
+    table would send its kernels to rows past the buffers."""
+    need = w.desc.E * (3 if w.desc.format == MOE_W_MWQ_2_3_4 else 1) + 1
+    if seg_offsets.dtype != torch.int32 or seg_offsets.dim() != 1 or seg_offsets.numel() < need:
+        raise ValueError(f"seg_offsets must be int32 with at least {need} entries for this weight set "
+                         f"(got {seg_offsets.dtype}, {tuple(seg_offsets.shape)})")
+
+
 def moe_grouped_qgemm_workspace_size(w: QuantizedExperts, A_rows: int, M_total: int,
                                      kernel: int = MOE_KERNEL_AUTO) -> int:
     return lib().moe_grouped_qgemm_workspace_size(ctypes.byref(w.desc), A_rows, M_total, kernel)
@@ -262,6 +271,7 @@ def moe_grouped_qgemm(w: QuantizedExperts, A: torch.Tensor, seg_offsets: torch.T
                       out: torch.Tensor = None, workspace: torch.Tensor = None, stream=None,
                       kernel: int = MOE_KERNEL_AUTO) -> torch.Tensor:
     _bf16(A)
+    _check_segments(w, seg_offsets)
     A_rows = A.shape[0]
     n_out = w.N // 2 if epilogue == MOE_EPI_SWIGLU else w.N
     if out is None:
@@ -285,6 +295,7 @@ def moe_grouped_qgemm_noalloc(w: QuantizedExperts, A: torch.Tensor, seg_offsets:
     (moe_grouped_qgemm_noalloc_scratch_bytes()) serves instead.  Pass `out` to
     allocate nothing at all."""
     _bf16(A)
+    _check_segments(w, seg_offsets)
     n_out = w.N // 2 if epilogue == MOE_EPI_SWIGLU else w.N
     if out is None:
         dt = _EPI_DTYPE.get(epilogue, torch.bfloat16)
@@ -404,6 +415,8 @@ def moe_layer_forward(x: torch.Tensor, logits: torch.Tensor, k: int, gate_up: Qu
     T, H = x.shape
     E = logits.shape[1]
     I = gate_up.N // 2
+    if (gate_up.desc.format == MOE_W_MWQ_2_3_4) != (pair_bits is not None):
+        raise ValueError("nested-plane weights need pair_bits (a width per pair); other formats take none")
     if buf is None:
         buf = alloc_layer(T, E, k, H, I, pair_bits is not None, x.device)
     moe_route_permute(logits, k, pair_bits=pair_bits, ids=buf.ids, w=buf.w, out=buf.perm, stream=stream)

@@ -253,3 +253,32 @@ def test_per_expert_width_validation_and_sizes(lib):
     src = desc(fmt=P, layout=q.MOE_LAYOUT_CANONICAL, E=4, bits=bits, zero=zero)
     dst = desc(fmt=P, E=4, codes=0x70000, bits=bits, zero=[8, 1, 3, 1])
     assert lib.moe_repack_weights(ctypes.byref(src), ctypes.byref(dst), None) == BAD_SHAPE   # tables disagree
+
+
+def test_binding_checks_segment_table_and_widths():
+    """The binding refuses a segment table shorter than the weight set's E*S + 1
+    offsets (the kernels would read offsets past it) and a layer call whose
+    nested-plane weights come without per-pair widths (or widths without them),
+    before any library call that launches."""
+    import torch
+    E, N, K = 4, 64, 128
+
+    def weights(fmt):  # a descriptor only: nothing is launched
+        d = q.WDesc()
+        d.abi_version, d.format, d.layout, d.E, d.N, d.K, d.group_size = q.MOE_ABI_VERSION, fmt, q.MOE_LAYOUT_TILED, E, N, K, 128
+        return q.QuantizedExperts(desc=d)
+    mwq, int4 = weights(q.MOE_W_MWQ_2_3_4), weights(q.MOE_W_INT4_GROUP)
+    A = torch.zeros((8, K), dtype=torch.int16)
+    for w, short in ((mwq, E + 1), (int4, E)):
+        with pytest.raises(ValueError, match="seg_offsets"):
+            q.moe_grouped_qgemm(w, A, torch.zeros(short, dtype=torch.int32), 8)
+        with pytest.raises(ValueError, match="seg_offsets"):
+            q.moe_grouped_qgemm_noalloc(w, A, torch.zeros(short, dtype=torch.int32), 8)
+    with pytest.raises(ValueError, match="seg_offsets"):
+        q.moe_grouped_qgemm(int4, A, torch.zeros(E + 1, dtype=torch.int64), 8)
+    x = torch.zeros((8, K), dtype=torch.int16)
+    logits = torch.zeros((8, E), dtype=torch.float32)
+    with pytest.raises(ValueError, match="pair_bits"):
+        q.moe_layer_forward(x, logits, 2, mwq, mwq)
+    with pytest.raises(ValueError, match="pair_bits"):
+        q.moe_layer_forward(x, logits, 2, int4, int4, pair_bits=torch.full((8, 2), 4, dtype=torch.uint8))
