@@ -80,6 +80,17 @@ class _SlotCache:
         self.step = 0
         self.copy_stream = torch.cuda.Stream(device=device)  # default priority
 
+    def _intermediates(self, P: int, device):
+        """The step's h (bf16 [P][I]) and expert outputs y (fp16 [P][H]), kept from
+        one step to the next of the same size (every use is ordered on the compute
+        stream)."""
+        hy = getattr(self, "_hy", None)
+        if hy is None or hy[0].shape[0] != P or hy[0].device != device:
+            hy = (torch.empty((P, self.I), dtype=torch.bfloat16, device=device),
+                  torch.empty((P, self.H), dtype=torch.float16, device=device))
+            self._hy = hy
+        return hy
+
     def _assign(self, hot, keep=()):
         """Slots for this step's experts (hottest first): hits keep theirs; misses take
         a free slot, else the least recently used one holding none of `hot` or `keep`."""
@@ -163,8 +174,7 @@ class OffloadedMoeLayer(_SlotCache):
             if ev is not None and e not in misses:
                 compute.wait_event(ev)
         self._current = set(hot)
-        h = torch.empty((P, self.I), dtype=torch.bfloat16, device=x.device)
-        y = torch.empty((P, self.H), dtype=torch.float16, device=x.device)
+        h, y = self._intermediates(P, x.device)
         for phase in (0, 1):
             if phase == 1:
                 if not misses:
@@ -325,8 +335,7 @@ class OffloadedMwqLayer(_SlotCache):
             s = self.slot_of[e]
             self.planes_in[s] = max(self.planes_in[s], int(need[e]))
         rows = np.bincount(key // (3 * S), minlength=n_phase)
-        h = torch.empty((P, self.I), dtype=torch.bfloat16, device=x.device)
-        y = torch.empty((P, self.H), dtype=torch.float16, device=x.device)
+        h, y = self._intermediates(P, x.device)
         for ph in range(n_phase):
             if rows[ph] == 0:
                 continue

@@ -88,10 +88,12 @@ def test_permute_flags_invalid_ids(G):
     assert p.counts.cpu().numpy().sum() == 5
 
 
-def test_combine_skips_invalid_pairs(G):
+@pytest.mark.parametrize("ydt", [torch.float32, torch.float16, torch.bfloat16])
+def test_combine_skips_invalid_pairs(G, ydt):
     """A pair whose id the grouping flagged (placed after every valid segment,
     where no GEMM writes) adds nothing to its token's output when the combine
-    gets the number of valid rows; its row is never read (NaN there stays out)."""
+    gets the number of valid rows; its row is never read (NaN there stays out).
+    Expert outputs in fp32, fp16 or bf16."""
     ids = np.array([[0, 1], [2, 7], [1, 3]], np.int32)   # E = 4: pair 3 is invalid
     p = G.q.moe_permute(G.t(ids), 4)
     torch.cuda.synchronize()
@@ -101,11 +103,13 @@ def test_combine_skips_invalid_pairs(G):
     y = rng.standard_normal((6, 16)).astype(np.float32)
     y[nv:] = np.nan
     w = np.array([[0.5, 0.5], [0.25, 0.75], [0.6, 0.4]], np.float32)
-    out = G.q.moe_unpermute_combine(G.t(y), p.pair_pos, G.t(w), 3, 2, n_valid=p.seg_offsets[-1:])
+    yd = G.t(y).to(ydt)  # the values the combine sees: y rounded to the storage type
+    out = G.q.moe_unpermute_combine(yd, p.pair_pos, G.t(w), 3, 2, n_valid=p.seg_offsets[-1:])
     torch.cuda.synchronize()
     got = G.bf16_to_np(out)
     pos = p.pair_pos.cpu().numpy()
-    y0 = np.where(np.arange(6)[:, None] < nv, y, 0.0).astype(np.float64)
+    ys = yd.float().cpu().numpy().astype(np.float64)
+    y0 = np.where(np.arange(6)[:, None] < nv, ys, 0.0)
     ref = oracle.unpermute_combine(y0, pos, w.astype(np.float64), 3, 2)
     assert np.isfinite(got).all()
     assert np.all(np.abs(got - ref) <= G.bf16_ulp(ref))   # fp32 sums, one bf16 rounding
