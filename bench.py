@@ -458,8 +458,8 @@ def main():
         hbm_probe()
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(nothing here uses a second GPU)"}), flush=True)
+        print(json.dumps({"error": "the library and this benchmark run on one GPU; --gpus must be 1 "
+                                   "(no collective or multi-GPU path exists)"}), flush=True)
         sys.exit(2)
     if args.offload_slots:
         offload_bench(args)
