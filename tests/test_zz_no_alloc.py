@@ -39,8 +39,9 @@ def _layer_calls(G, cfg, kernel):
     h_ref, h = _both(G, gu, x, perm.seg_offsets, M, G.q.MOE_EPI_SWIGLU, gather_pair=perm.sorted_pair, k=cfg.k,
                      kernel=kernel)
     assert torch.equal(h_ref.view(torch.int16), h.view(torch.int16))
-    y_ref, y = _both(G, dn, h_ref, perm.seg_offsets, M, G.q.MOE_EPI_NONE_F32, kernel=kernel)
-    assert torch.equal(y_ref, y)
+    for epi in (G.q.MOE_EPI_NONE_F32, G.q.MOE_EPI_NONE_F16):  # fp32 and fp16 expert outputs
+        y_ref, y = _both(G, dn, h_ref, perm.seg_offsets, M, epi, kernel=kernel)
+        assert torch.equal(y_ref, y)
 
 
 @pytest.mark.parametrize("kernel_name,big,small", [
